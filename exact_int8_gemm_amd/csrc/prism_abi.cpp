@@ -1,0 +1,134 @@
+// C ABI of libprism: argument validation, device check and shape dispatch.
+//
+// Every call validates its arguments before touching HIP, so an invalid
+// call enqueues nothing and writes nothing (the pages' servers refuse
+// oversized requests instead of truncating them; this library does the same
+// with unsupported shapes).  The kernel choice depends on (M, N, K) only and
+// never changes a result bit: sums are exact in int32 and each epilogue is a
+// fixed per-element sequence of fp32 operations.
+#include <atomic>
+#include <climits>
+#include <cstring>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/prism.h"
+#include "prism_internal.h"
+
+namespace prism {
+
+int launch_status() { return hipGetLastError() == hipSuccess ? PRISM_OK : PRISM_ERR_LAUNCH; }
+
+}  // namespace prism
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return PRISM_ERR_UNSUPPORTED;
+  if (dev < kMaxDevices) {
+    const int c = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (c == 1) return PRISM_OK;
+    if (c == 2) return PRISM_ERR_UNSUPPORTED;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return PRISM_ERR_UNSUPPORTED;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
+                  (prop.gcnArchName[6] == '\0' || prop.gcnArchName[6] == ':');
+  if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? PRISM_OK : PRISM_ERR_UNSUPPORTED;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shared checks of the three GEMM calls.  Returns PRISM_OK to go on, or a
+// status; *noop is set when M == 0.
+int check_gemm(const void* q, const void* s_a, const void* w, const void* scale_w, const void* y,
+               const void* acc_or_partials, int64_t M, int64_t N, int64_t K, int k_multiple, bool* noop) {
+  *noop = false;
+  if (M < 0 || N < 0 || K < 0) return PRISM_ERR_INVALID_ARG;
+  if (M == 0) {
+    *noop = true;
+    return PRISM_OK;
+  }
+  if (N == 0 || K == 0 || K > PRISM_K_MAX || M > INT_MAX || N > INT_MAX) return PRISM_ERR_INVALID_ARG;
+  if (!q || !s_a || !w || !scale_w || !y) return PRISM_ERR_INVALID_ARG;
+  if (K % k_multiple != 0) return PRISM_ERR_ALIGNMENT;
+  if (!aligned(q, 16) || !aligned(w, 16) || !aligned(s_a, 4) || !aligned(y, 4) || !aligned(acc_or_partials, 4))
+    return PRISM_ERR_ALIGNMENT;
+  return PRISM_OK;
+}
+
+// Grid limits of the tiled kernels (128 x 128 tiles at the smallest).
+bool grid_fits(int64_t M, int64_t N) { return ((M + 127) / 128) * ((N + 127) / 128) <= INT_MAX; }
+
+}  // namespace
+
+extern "C" {
+
+int prism_abi_version(void) { return PRISM_ABI_VERSION; }
+
+const char* prism_status_string(int status) {
+  switch (status) {
+    case PRISM_OK: return "ok";
+    case PRISM_ERR_INVALID_ARG: return "invalid argument (null pointer, negative or zero size, or K above PRISM_K_MAX)";
+    case PRISM_ERR_ALIGNMENT: return "misaligned pointer or K not a multiple of the required block";
+    case PRISM_ERR_UNSUPPORTED: return "no usable gfx950 (MI355X) device is current";
+    case PRISM_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int prism_quantize_rows(const float* x, int8_t* q, float* scale, int64_t M, int64_t K, void* stream) {
+  if (M < 0 || K < 0) return PRISM_ERR_INVALID_ARG;
+  if (M == 0) return PRISM_OK;
+  if (K == 0 || M > INT_MAX || K > INT_MAX / 4) return PRISM_ERR_INVALID_ARG;
+  if (!x || !q || !scale) return PRISM_ERR_INVALID_ARG;
+  if (K % 16 != 0 || !aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4)) return PRISM_ERR_ALIGNMENT;
+  const int dev = check_device();
+  if (dev != PRISM_OK) return dev;
+  return prism::launch_quantize_rows(x, q, scale, M, K, static_cast<hipStream_t>(stream));
+}
+
+int prism_gemm_w8a8(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc,
+                    int64_t M, int64_t N, int64_t K, void* stream) {
+  bool noop;
+  int st = check_gemm(q, s_a, w, s_w, y, acc, M, N, K, 16, &noop);
+  if (st != PRISM_OK || noop) return st;
+  if (!aligned(s_w, 4)) return PRISM_ERR_ALIGNMENT;
+  if (!grid_fits(M, N)) return PRISM_ERR_INVALID_ARG;
+  if ((st = check_device()) != PRISM_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M <= prism::kSmallMMax) return prism::launch_gemm_small(q, s_a, w, false, s_w, y, acc, (int)M, (int)N, (int)K, s);
+  return prism::launch_gemm_tiled(q, s_a, w, false, s_w, y, acc, (int)M, (int)N, (int)K, s);
+}
+
+int prism_gemm_w4a8(const int8_t* q, const float* s_a, const uint8_t* w4, const float* s_w, float* y, int32_t* acc,
+                    int64_t M, int64_t N, int64_t K, void* stream) {
+  bool noop;
+  int st = check_gemm(q, s_a, w4, s_w, y, acc, M, N, K, 32, &noop);
+  if (st != PRISM_OK || noop) return st;
+  if (!aligned(s_w, 4)) return PRISM_ERR_ALIGNMENT;
+  if (!grid_fits(M, N)) return PRISM_ERR_INVALID_ARG;
+  if ((st = check_device()) != PRISM_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M <= prism::kSmallMMax) return prism::launch_gemm_small(q, s_a, w4, true, s_w, y, acc, (int)M, (int)N, (int)K, s);
+  return prism::launch_gemm_tiled(q, s_a, w4, true, s_w, y, acc, (int)M, (int)N, (int)K, s);
+}
+
+int prism_gemm_w8a8_blockscale(const int8_t* q, const float* s_a, const int8_t* w, const uint16_t* d, float* y,
+                               int32_t* partials, int64_t M, int64_t N, int64_t K, void* stream) {
+  bool noop;
+  int st = check_gemm(q, s_a, w, d, y, partials, M, N, K, 32, &noop);
+  if (st != PRISM_OK || noop) return st;
+  if (!aligned(d, 2)) return PRISM_ERR_ALIGNMENT;
+  if (!grid_fits(M, N)) return PRISM_ERR_INVALID_ARG;
+  if ((st = check_device()) != PRISM_OK) return st;
+  return prism::launch_gemm_blockscale(q, s_a, w, d, y, partials, (int)M, (int)N, (int)K,
+                                       static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,34 @@
+// Internal declarations shared by the HIP sources of libprism.  Not part of
+// the C ABI (that is include/prism.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace prism {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+// Rows up to this count take the split-K small-M kernels; more rows take the
+// LDS-tiled kernels.  Either choice gives the same bits (exact int32 sums and
+// a fixed per-element epilogue).
+constexpr int kSmallMMax = 64;
+
+// Each launcher assumes its arguments were validated by the C ABI layer and
+// returns a PRISM_* status.
+int launch_quantize_rows(const float* x, int8_t* q, float* s, int64_t M, int64_t K, hipStream_t st);
+
+int launch_gemm_small(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
+                      float* y, int32_t* acc, int M, int N, int K, hipStream_t st);
+
+int launch_gemm_tiled(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
+                      float* y, int32_t* acc, int M, int N, int K, hipStream_t st);
+
+int launch_gemm_blockscale(const int8_t* q, const float* s_a, const int8_t* w, const uint16_t* d, float* y,
+                           int32_t* partials, int M, int N, int K, hipStream_t st);
+
+// Status of the most recent launch on this thread.
+int launch_status();
+
+}  // namespace prism

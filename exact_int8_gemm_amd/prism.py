@@ -1,0 +1,169 @@
+"""Python binding of libprism (the C ABI in ``include/prism.h``).
+
+Argument marshalling only: tensors are checked for dtype, device, shape,
+contiguity and alignment, their device pointers and the current HIP stream
+are passed to the C entry points, and a non-zero status raises
+:class:`PrismError`.  Every step of the computation runs in the HIP kernels
+of ``libprism.so``; there is no fallback of any kind, and a missing library
+raises instead of computing elsewhere.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libprism.so")
+
+PRISM_OK = 0
+ABI_VERSION = 1
+K_MAX = 131040
+
+
+class PrismError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__("prism status %d: %s" % (status, text))
+        self.status = status
+
+
+_lib = None
+
+
+def _declare(lib):
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.prism_abi_version.restype = i32
+    lib.prism_abi_version.argtypes = []
+    lib.prism_status_string.restype = ctypes.c_char_p
+    lib.prism_status_string.argtypes = [i32]
+    lib.prism_quantize_rows.restype = i32
+    lib.prism_quantize_rows.argtypes = [p, p, p, i64, i64, p]
+    for name in ("prism_gemm_w8a8", "prism_gemm_w8a8_blockscale", "prism_gemm_w4a8"):
+        fn = getattr(lib, name)
+        fn.restype = i32
+        fn.argtypes = [p, p, p, p, p, p, i64, i64, i64, p]
+    return lib
+
+
+def lib():
+    """The loaded ``libprism.so`` (built with hipcc first if it does not exist yet)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build
+            build.build_library()
+        _lib = _declare(ctypes.CDLL(LIB_PATH))
+        v = _lib.prism_abi_version()
+        if v != ABI_VERSION:
+            raise RuntimeError("libprism ABI version %d, binding expects %d: rebuild" % (v, ABI_VERSION))
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().prism_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != PRISM_OK:
+        raise PrismError(status, status_string(status))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.device != device:
+        raise ValueError("%s must be on %s, got %s" % (name, device, t.device))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _gpu(t, name):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError("%s must be a tensor on a HIP device" % name)
+    return t.device
+
+
+def quantize_rows(x, q=None, scale=None):
+    """x float32 [M, K] on the GPU -> (q int8 [M, K], scale float32 [M])."""
+    dev = _gpu(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    M, K = x.shape
+    _need(x, "x", torch.float32, (M, K), dev)
+    q = torch.empty((M, K), dtype=torch.int8, device=dev) if q is None else _need(q, "q", torch.int8, (M, K), dev)
+    scale = torch.empty((M,), dtype=torch.float32, device=dev) if scale is None else \
+        _need(scale, "scale", torch.float32, (M,), dev)
+    with torch.cuda.device(dev):
+        _check(lib().prism_quantize_rows(_ptr(x), _ptr(q), _ptr(scale), M, K, _stream(dev)))
+    return q, scale
+
+
+def _gemm_args(q, s_a, w, w_cols, wdtype, s_w_name, s_w, s_w_dtype, s_w_shape_fn):
+    dev = _gpu(q, "q")
+    if q.dim() != 2 or w.dim() != 2:
+        raise ValueError("q and w must be 2-D")
+    M, K = q.shape
+    N = w.shape[0]
+    _need(q, "q", torch.int8, (M, K), dev)
+    _need(s_a, "s_a", torch.float32, (M,), dev)
+    _need(w, "w", wdtype, (N, w_cols(K)), dev)
+    _need(s_w, s_w_name, s_w_dtype, s_w_shape_fn(N, K), dev)
+    return dev, M, N, K
+
+
+def gemm_w8a8(q, s_a, w, s_w, y=None, acc=None):
+    """Per-channel W8A8: q int8 [M,K], s_a f32 [M], w int8 [N,K], s_w f32 [N] -> y f32 [M,N].
+
+    If ``acc`` (int32 [M,N]) is given, the exact int32 sums are written there too."""
+    dev, M, N, K = _gemm_args(q, s_a, w, lambda k: k, torch.int8, "s_w", s_w, torch.float32, lambda n, k: (n,))
+    y = torch.empty((M, N), dtype=torch.float32, device=dev) if y is None else _need(y, "y", torch.float32, (M, N), dev)
+    if acc is not None:
+        _need(acc, "acc", torch.int32, (M, N), dev)
+    with torch.cuda.device(dev):
+        _check(lib().prism_gemm_w8a8(_ptr(q), _ptr(s_a), _ptr(w), _ptr(s_w), _ptr(y), _ptr(acc), M, N, K,
+                                     _stream(dev)))
+    return y
+
+
+def gemm_w4a8(q, s_a, w4, s_w, y=None, acc=None):
+    """W4A8: q int8 [M,K], s_a f32 [M], w4 uint8 [N,K/2] (low nibble = even k), s_w f32 [N] -> y f32 [M,N]."""
+    dev, M, N, K = _gemm_args(q, s_a, w4, lambda k: k // 2, torch.uint8, "s_w", s_w, torch.float32,
+                              lambda n, k: (n,))
+    y = torch.empty((M, N), dtype=torch.float32, device=dev) if y is None else _need(y, "y", torch.float32, (M, N), dev)
+    if acc is not None:
+        _need(acc, "acc", torch.int32, (M, N), dev)
+    with torch.cuda.device(dev):
+        _check(lib().prism_gemm_w4a8(_ptr(q), _ptr(s_a), _ptr(w4), _ptr(s_w), _ptr(y), _ptr(acc), M, N, K,
+                                     _stream(dev)))
+    return y
+
+
+def gemm_w8a8_blockscale(q, s_a, w, d, y=None, partials=None):
+    """Block-scale W8A8: q int8 [M,K], s_a f32 [M], w int8 [N,K], d [N,K/32] fp16 scales
+    (torch.float16, or their bit patterns as int16/uint16) -> y f32 [M,N].
+
+    If ``partials`` (int32 [M,N,K/32]) is given, every exact 32-k block sum is written there."""
+    if not isinstance(d, torch.Tensor) or d.dtype not in (torch.float16, torch.int16, torch.uint16):
+        raise TypeError("d must be a float16 (or 16-bit integer bit-pattern) tensor")
+    dev, M, N, K = _gemm_args(q, s_a, w, lambda k: k, torch.int8, "d", d, d.dtype, lambda n, k: (n, k // 32))
+    y = torch.empty((M, N), dtype=torch.float32, device=dev) if y is None else _need(y, "y", torch.float32, (M, N), dev)
+    if partials is not None:
+        _need(partials, "partials", torch.int32, (M, N, K // 32), dev)
+    with torch.cuda.device(dev):
+        _check(lib().prism_gemm_w8a8_blockscale(_ptr(q), _ptr(s_a), _ptr(w), _ptr(d), _ptr(y), _ptr(partials),
+                                                M, N, K, _stream(dev)))
+    return y

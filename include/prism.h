@@ -1,0 +1,126 @@
+/*
+ * prism.h -- C ABI of the exact, batch-invariant int8 linear layer for
+ * MI355X (gfx950).
+ *
+ * The operation (StartLux-Prism README): "Why StartLux-Prism" says that the
+ * int8 GEMMs sum exactly in int32, so that a request gets the same result
+ * whatever it is batched with, and that Q8_0 weights run as int8 (W8A8)
+ * while Q4_K_M weights run on their own 4-bit values (W4A8); "How it works"
+ * repeats that the int8 tensor-core path sums exactly in int32; "Quick
+ * start" says the activations are quantized to int8 with measured ranges.
+ * The pages fix neither the activation scale nor the epilogue; the readings
+ * taken here are stated at each call below.
+ *
+ * Conventions shared by every call:
+ *   - Every pointer argument is a DEVICE pointer (HBM of the current HIP
+ *     device).  The caller allocates and owns all buffers; the library keeps
+ *     no pointer after the call returns and allocates nothing.
+ *   - Matrices are dense and row-major with no padding: x, q are [M][K],
+ *     w is [N][K], w4 is [N][K/2], d is [N][K/32], y and acc are [M][N],
+ *     partials is [M][N][K/32].
+ *   - x, q, w and w4 must be 16-byte aligned; every other pointer must be
+ *     aligned to its element size.
+ *   - Work is enqueued on `stream` (a hipStream_t; 0 = the null stream) and
+ *     the call returns without synchronizing.  Results are ready when the
+ *     stream reaches that point.
+ *   - M = 0 is a successful no-op that touches no memory.
+ *   - Arguments are validated before any HIP call; an invalid call returns a
+ *     negative status, enqueues nothing and writes nothing.
+ *   - Results are a pure function of the inputs: they do not depend on M,
+ *     on a row's position in the batch, on the stream or on concurrency.
+ *     Calls hold no global state except a per-device cache of the device's
+ *     architecture, and may be made from several threads at once.
+ */
+#ifndef PRISM_H
+#define PRISM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Bumped on any change of a signature or of the semantics below. */
+#define PRISM_ABI_VERSION 1
+
+/* Largest accepted K.  For K <= 131040 every exact sum of K products of two
+ * int8 values (|q|, |w| <= 128) lies strictly inside the int32 range. */
+#define PRISM_K_MAX 131040
+
+/* Status codes. */
+#define PRISM_OK 0
+#define PRISM_ERR_INVALID_ARG (-1) /* null required pointer, negative size, N or K = 0 with M > 0, K > PRISM_K_MAX */
+#define PRISM_ERR_ALIGNMENT (-2)   /* misaligned pointer, or K not a multiple of 16 (32 for block-scale and W4A8) */
+#define PRISM_ERR_UNSUPPORTED (-3) /* the current device is not gfx950, or no device is usable */
+#define PRISM_ERR_LAUNCH (-4)      /* the kernel launch reported an error */
+
+/* Returns PRISM_ABI_VERSION of the built library. */
+int prism_abi_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* prism_status_string(int status);
+
+/*
+ * Per-row int8 activation quantizer (README "Quick start": int8 activation
+ * ranges; the per-row absmax form is the reading taken here).
+ *   x      [M][K] fp32, input.
+ *   q      [M][K] int8, output.
+ *   scale  [M] fp32, output.
+ * For each row m: a = max_k |x[m][k]|; scale[m] = a / 127 (IEEE division,
+ * round to nearest even); q[m][k] = clamp(rint(x[m][k] / scale[m]), -127, 127)
+ * with rint rounding half to even.  A row holding a NaN or an infinity gets
+ * scale NaN and q = 0; a row whose scale is 0 (all zeros, or a subnormal
+ * amax that underflows) gets q = 0.  Rows never influence each other.
+ * K must be a multiple of 16.
+ */
+int prism_quantize_rows(const float* x, int8_t* q, float* scale,
+                        int64_t M, int64_t K, void* stream);
+
+/*
+ * W8A8 GEMM with per-output-channel weight scales (README "Why
+ * StartLux-Prism": Q8_0 weights as int8 W8A8, summed exactly in int32).
+ *   q    [M][K] int8 activations, s_a [M] fp32 row scales.
+ *   w    [N][K] int8 weights (one row per output channel), s_w [N] fp32.
+ *   y    [M][N] fp32 output.
+ *   acc  [M][N] int32 output, or NULL.
+ * acc[m][n] = sum_k q[m][k] * w[n][k], exact in int32;
+ * y[m][n]   = ((float)acc[m][n] * s_a[m]) * s_w[n], each product rounded
+ * to nearest even on its own, in that order.  K must be a multiple of 16.
+ */
+int prism_gemm_w8a8(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w,
+                    float* y, int32_t* acc, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * W8A8 GEMM with one fp16 weight scale per 32 consecutive k of each weight
+ * row (Q8_0-style blocks; README "Why StartLux-Prism", released Q8_0 files).
+ *   q [M][K] int8, s_a [M] fp32, w [N][K] int8.
+ *   d [N][K/32] binary16 bit patterns: the scale of block b of row n.
+ *   y [M][N] fp32 output.
+ *   partials [M][N][K/32] int32 output, or NULL (meant for small debug sizes).
+ * P_b = sum_{32b <= k < 32b+32} q[m][k] * w[n][k] (exact int32);
+ * f = +0; for b = 0, 1, ..., K/32-1 in that order: f = fmaf((float)P_b,
+ * (float)d[n][b], f); y[m][n] = f * s_a[m].  K must be a multiple of 32.
+ */
+int prism_gemm_w8a8_blockscale(const int8_t* q, const float* s_a, const int8_t* w,
+                               const uint16_t* d, float* y, int32_t* partials,
+                               int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * W4A8 GEMM on packed signed 4-bit weights (README "Why StartLux-Prism":
+ * Q4_K_M files run on their own 4-bit weights with int8 activations; the
+ * symmetric per-channel form is the reading taken here).
+ *   q [M][K] int8, s_a [M] fp32.
+ *   w4 [N][K/2] bytes: byte j of row n holds w[n][2j] in its low nibble and
+ *      w[n][2j+1] in its high nibble, each a two's-complement value in [-8, 7].
+ *   s_w [N] fp32, y [M][N] fp32, acc [M][N] int32 or NULL.
+ * acc and y as for prism_gemm_w8a8 with w decoded from the nibbles.
+ * K must be a multiple of 32.
+ */
+int prism_gemm_w4a8(const int8_t* q, const float* s_a, const uint8_t* w4, const float* s_w,
+                    float* y, int32_t* acc, int64_t M, int64_t N, int64_t K, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PRISM_H */

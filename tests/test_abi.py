@@ -1,0 +1,189 @@
+"""The C ABI library loads, exports what include/prism.h declares, and rejects
+invalid calls before any HIP call (runs without a GPU).
+
+The validation calls pass fake pointers, so they run in a child process in
+which no HIP device is visible: even a validation bug could then never reach
+a kernel launch.
+"""
+import json
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "prism.h")
+LIB = os.path.join(ROOT, "exact_int8_gemm_amd", "libprism.so")
+
+
+def _header():
+    return open(HEADER).read()
+
+
+def _declared_functions():
+    return re.findall(r"^\s*(?:int|const char\*)\s+(prism_\w+)\s*\(", _header(), flags=re.M)
+
+
+def _defines():
+    return {k: int(v) for k, v in re.findall(r"#define\s+(PRISM_\w+)\s+\(?(-?\d+)\)?", _header())}
+
+
+@pytest.fixture(scope="module")
+def built():
+    if not os.path.exists(LIB):
+        sys.path.insert(0, ROOT)
+        from exact_int8_gemm_amd import build
+        build.build_library()
+    return LIB
+
+
+def test_header_declares_the_four_calls():
+    names = set(_declared_functions())
+    assert {"prism_quantize_rows", "prism_gemm_w8a8", "prism_gemm_w8a8_blockscale", "prism_gemm_w4a8",
+            "prism_abi_version", "prism_status_string"} <= names
+
+
+def test_library_exports_every_declared_symbol(built):
+    out = subprocess.run(["nm", "-D", "--defined-only", built], capture_output=True, text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for name in _declared_functions():
+        assert name in exported, name
+
+
+def test_binding_constants_match_header():
+    sys.path.insert(0, ROOT)
+    from exact_int8_gemm_amd import prism
+    d = _defines()
+    assert d["PRISM_ABI_VERSION"] == prism.ABI_VERSION
+    assert d["PRISM_K_MAX"] == prism.K_MAX
+    # the K bound keeps every exact sum inside int32 even for -128 * -128 products
+    assert d["PRISM_K_MAX"] * 128 * 128 < 2 ** 31
+    assert d["PRISM_K_MAX"] % 32 == 0
+
+
+_CHILD = r"""
+import ctypes, json, sys
+lib = ctypes.CDLL(sys.argv[1])
+p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+lib.prism_abi_version.restype = i32
+lib.prism_status_string.restype = ctypes.c_char_p
+lib.prism_status_string.argtypes = [i32]
+lib.prism_quantize_rows.restype = i32
+lib.prism_quantize_rows.argtypes = [p, p, p, i64, i64, p]
+for n in ("prism_gemm_w8a8", "prism_gemm_w8a8_blockscale", "prism_gemm_w4a8"):
+    getattr(lib, n).restype = i32
+    getattr(lib, n).argtypes = [p, p, p, p, p, p, i64, i64, i64, p]
+A = 0x7f0000000000          # 256-byte aligned fake address, never dereferenced
+res = {"version": lib.prism_abi_version(),
+       "strings": {str(s): lib.prism_status_string(s).decode() for s in (0, -1, -2, -3, -4, 7)}}
+cases = json.loads(sys.argv[2])
+out = []
+for fn, args in cases:
+    out.append(getattr(lib, fn)(*[None if a is None else a for a in args]))
+res["status"] = out
+print(json.dumps(res))
+"""
+
+OK, INVALID, ALIGN, UNSUP = 0, -1, -2, -3
+A = 0x7F0000000000
+
+
+def _g(q=A, sa=A, w=A, sw=A, y=A, acc=None, M=4, N=16, K=64):
+    return [q, sa, w, sw, y, acc, M, N, K, None]
+
+
+# (function, args, expected status); every non-OK case is invalid before any HIP call
+CASES = [
+    ("prism_quantize_rows", [A, A, A, 0, 64, None], OK),            # M = 0: no-op
+    ("prism_quantize_rows", [None, None, None, 0, 0, None], OK),    # M = 0 with nothing at all
+    ("prism_quantize_rows", [A, A, A, -1, 64, None], INVALID),
+    ("prism_quantize_rows", [A, A, A, 4, -16, None], INVALID),
+    ("prism_quantize_rows", [A, A, A, 4, 0, None], INVALID),
+    ("prism_quantize_rows", [None, A, A, 4, 64, None], INVALID),
+    ("prism_quantize_rows", [A, None, A, 4, 64, None], INVALID),
+    ("prism_quantize_rows", [A, A, None, 4, 64, None], INVALID),
+    ("prism_quantize_rows", [A, A, A, 4, 40, None], ALIGN),          # K % 16
+    ("prism_quantize_rows", [A + 4, A, A, 4, 64, None], ALIGN),
+    ("prism_quantize_rows", [A, A + 8, A, 4, 64, None], ALIGN),
+    ("prism_quantize_rows", [A, A, A + 2, 4, 64, None], ALIGN),
+]
+for fn, kmul in (("prism_gemm_w8a8", 16), ("prism_gemm_w4a8", 32), ("prism_gemm_w8a8_blockscale", 32)):
+    CASES += [
+        (fn, _g(M=0), OK),
+        (fn, _g(None, None, None, None, None, None, 0, 16, 64), OK),
+        (fn, _g(M=-1), INVALID),
+        (fn, _g(N=-1), INVALID),
+        (fn, _g(K=-32), INVALID),
+        (fn, _g(M=-1, N=0, K=0), INVALID),
+        (fn, _g(N=0), INVALID),
+        (fn, _g(K=0), INVALID),
+        (fn, _g(K=131040 + 32), INVALID),
+        (fn, _g(K=1 << 40), INVALID),
+        (fn, _g(M=1 << 31), INVALID),
+        (fn, _g(N=1 << 31), INVALID),
+        (fn, _g(q=None), INVALID),
+        (fn, _g(sa=None), INVALID),
+        (fn, _g(w=None), INVALID),
+        (fn, _g(sw=None), INVALID),
+        (fn, _g(y=None), INVALID),
+        (fn, _g(K=kmul + 8), ALIGN),
+        (fn, _g(q=A + 8), ALIGN),
+        (fn, _g(w=A + 4), ALIGN),
+        (fn, _g(sa=A + 2), ALIGN),
+        (fn, _g(y=A + 1), ALIGN),
+        (fn, _g(acc=A + 2), ALIGN),
+    ]
+    if kmul == 32:
+        CASES.append((fn, _g(K=48), ALIGN))
+CASES.append(("prism_gemm_w8a8", _g(sw=A + 2), ALIGN))
+CASES.append(("prism_gemm_w4a8", _g(sw=A + 1), ALIGN))
+CASES.append(("prism_gemm_w8a8_blockscale", _g(sw=A + 1), ALIGN))   # d is 2-byte data
+
+
+@pytest.fixture(scope="module")
+def child_results(built):
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", CUDA_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1")
+    payload = json.dumps([[fn, args] for fn, args, _ in CASES])
+    out = subprocess.run([sys.executable, "-c", _CHILD, built, payload], env=env, capture_output=True, text=True,
+                         timeout=120)
+    assert out.returncode == 0, out.stderr
+    return json.loads(out.stdout.strip().splitlines()[-1])
+
+
+def test_abi_version(child_results):
+    assert child_results["version"] == _defines()["PRISM_ABI_VERSION"]
+
+
+def test_status_strings(child_results):
+    s = child_results["strings"]
+    assert s["0"] == "ok"
+    texts = [s[k] for k in ("-1", "-2", "-3", "-4")]
+    assert all(texts) and len(set(texts)) == 4
+    assert s["7"] == "unknown status"
+
+
+@pytest.mark.parametrize("i", range(len(CASES)))
+def test_validation(child_results, i):
+    fn, args, expect = CASES[i]
+    assert child_results["status"][i] == expect, (fn, args)
+
+
+def test_valid_call_without_a_device_is_unsupported(built):
+    """Valid arguments with no visible device: the device check answers, nothing launches."""
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", CUDA_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1")
+    payload = json.dumps([["prism_gemm_w8a8", _g()], ["prism_quantize_rows", [A, A, A, 4, 64, None]]])
+    out = subprocess.run([sys.executable, "-c", _CHILD, built, payload], env=env, capture_output=True, text=True,
+                         timeout=120)
+    assert out.returncode == 0, out.stderr
+    assert json.loads(out.stdout.strip().splitlines()[-1])["status"] == [UNSUP, UNSUP]
+
+
+def test_build_uses_result_defining_flags():
+    sys.path.insert(0, ROOT)
+    from exact_int8_gemm_amd import build
+    cmd = " ".join(build._compile_cmd("x.hip", "x.o"))
+    for flag in ("--offload-arch=gfx950", "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
+                 "-fno-gpu-flush-denormals-to-zero", "-packed-fp32-ops"):
+        assert flag in cmd, flag

@@ -1,0 +1,212 @@
+"""GPU parity: every entry point of the C ABI against the CPU oracle, bit for bit.
+
+Shapes sweep the row count across both kernel families (split-K small-M
+kernel up to 64 rows, LDS-tiled kernels above) and across tile edges, with
+ragged N and K tails.  Tolerance is zero: int32 accumulators and block
+partials must be equal, fp32 outputs must have equal bit patterns.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_int8_gemm_amd import prism
+from exact_int8_gemm_amd import workloads as wl
+from gpu_util import DEV, assert_same_floats, assert_same_ints, dev, host
+
+pytestmark = pytest.mark.gpu
+
+M_SWEEP = [1, 2, 3, 7, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+
+
+# ------------------------------------------------------------------ quantizer
+
+@pytest.mark.parametrize("M,K", [(1, 16), (5, 48), (64, 256), (3, 512), (33, 2560), (8, 9728), (4, 10240),
+                                 (4, 10256), (2, 20480), (300, 512)])
+def test_quantize_rows(M, K):
+    rng = np.random.default_rng(M * 100003 + K)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    x[:, rng.choice(K, max(1, K // 100), replace=False)] *= np.float32(20.0)
+    q_ref, s_ref = oracle.quantize_rows(x)
+    q, s = prism.quantize_rows(dev(x))
+    torch.cuda.synchronize()
+    assert_same_floats(host(s), s_ref, "scale")
+    assert_same_ints(host(q), q_ref, "codes")
+
+
+def test_quantize_special_rows():
+    K = 64
+    rows = []
+    rows.append(np.zeros(K))                                   # all zeros
+    r = np.zeros(K); r[3] = -0.0; rows.append(r)               # negative zeros
+    r = np.ones(K); r[5] = np.nan; rows.append(r)              # NaN
+    r = np.ones(K); r[0] = np.inf; rows.append(r)              # +inf
+    r = np.ones(K); r[63] = -np.inf; rows.append(r)            # -inf
+    rows.append(np.full(K, 1e-44))                             # subnormal amax: scale 0
+    rows.append((np.arange(K) - 60) * 3 * 2.0 ** -149)         # subnormal scale, clamp binds
+    rows.append(np.linspace(-3e38, 3e38, K))                   # huge values
+    r = np.arange(K) - 32 + 0.5; r[0] = 127.0; rows.append(r)  # exact halves with scale 1
+    r = np.full(K, 2.5); r[1] = -127.0; rows.append(r)         # ties to even, negative max
+    rows.append(np.full(K, 7.0))                               # constant row -> all 127
+    x = np.array(rows, dtype=np.float32)
+    q_ref, s_ref = oracle.quantize_rows(x)
+    q, s = prism.quantize_rows(dev(x))
+    torch.cuda.synchronize()
+    assert_same_floats(host(s), s_ref, "scale")
+    assert_same_ints(host(q), q_ref, "codes")
+
+
+# ------------------------------------------------------------------ GEMMs
+
+def _case(seed, M, N, K, kind):
+    c = wl.random_case(seed, M, N, K, kind)
+    q, s_a = oracle.quantize_rows(c["x"])
+    return c, q, s_a
+
+
+@pytest.mark.parametrize("M", M_SWEEP)
+@pytest.mark.parametrize("N,K", [(16, 16), (100, 144), (300, 1040)])
+def test_w8a8(M, N, K):
+    c, q, s_a = _case(1, M, N, K, "w8a8")
+    y_ref, acc_ref = oracle.gemm_w8a8(q, s_a, c["w"], c["s_w"])
+    acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    y = prism.gemm_w8a8(dev(q), dev(s_a), dev(c["w"]), dev(c["s_w"]), acc=acc)
+    torch.cuda.synchronize()
+    assert_same_ints(host(acc), acc_ref, "acc")
+    assert_same_floats(host(y), y_ref, "y")
+
+
+@pytest.mark.parametrize("M", M_SWEEP)
+@pytest.mark.parametrize("N,K", [(16, 32), (100, 160), (300, 1056)])
+def test_w4a8(M, N, K):
+    c, q, s_a = _case(2, M, N, K, "w4a8")
+    y_ref, acc_ref = oracle.gemm_w4a8(q, s_a, c["w4"], c["s_w"])
+    acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    y = prism.gemm_w4a8(dev(q), dev(s_a), dev(c["w4"]), dev(c["s_w"]), acc=acc)
+    torch.cuda.synchronize()
+    assert_same_ints(host(acc), acc_ref, "acc")
+    assert_same_floats(host(y), y_ref, "y")
+
+
+@pytest.mark.parametrize("M", [1, 7, 64, 65, 129, 257])
+@pytest.mark.parametrize("N,K", [(16, 32), (100, 160), (300, 1056)])
+def test_w8a8_blockscale(M, N, K):
+    c, q, s_a = _case(3, M, N, K, "block")
+    y_ref, p_ref = oracle.gemm_w8a8_blockscale(q, s_a, c["w"], c["d"], want_partials=True)
+    part = torch.empty((M, N, K // 32), dtype=torch.int32, device=DEV)
+    y = prism.gemm_w8a8_blockscale(dev(q), dev(s_a), dev(c["w"]), dev(c["d"]), partials=part)
+    y2 = prism.gemm_w8a8_blockscale(dev(q), dev(s_a), dev(c["w"]), dev(c["d"]))   # without partials
+    torch.cuda.synchronize()
+    assert_same_ints(host(part), p_ref, "partials")
+    assert_same_floats(host(y), y_ref, "y")
+    assert_same_floats(host(y2), y_ref, "y without partials")
+
+
+def test_full_int8_range_and_largest_k():
+    """-128 codes and weights (valid inputs, though the quantizer never makes -128)
+    and the largest accepted K: the exact sums reach K * 16384 < 2^31."""
+    K = prism.K_MAX
+    M, N = 4, 3
+    q = np.full((M, K), -128, np.int8)
+    q[1] = 127
+    q[2] = np.tile(np.array([-128, 127], np.int8), K // 2)
+    q[3] = 1
+    w = np.full((N, K), -128, np.int8)
+    w[1] = 127
+    w[2, ::2] = 0
+    s_a = np.array([1.0, 0.5, 2.0 ** -20, 3.0], np.float32)
+    s_w = np.array([1.0, 2.0 ** -30, 0.25], np.float32)
+    y_ref, acc_ref = oracle.gemm_w8a8(q, s_a, w, s_w)
+    acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    y = prism.gemm_w8a8(dev(q), dev(s_a), dev(w), dev(s_w), acc=acc)
+    torch.cuda.synchronize()
+    assert int(acc_ref[0, 0]) == K * 16384
+    assert_same_ints(host(acc), acc_ref, "acc")
+    assert_same_floats(host(y), y_ref, "y")
+    # same rows through the tiled kernels (row count above the small-M limit)
+    rep = 40
+    qb, sab = np.tile(q, (rep, 1)), np.tile(s_a, rep)
+    yb_ref = np.tile(y_ref, (rep, 1))
+    yb = prism.gemm_w8a8(dev(qb), dev(sab), dev(w), dev(s_w))
+    torch.cuda.synchronize()
+    assert_same_floats(host(yb), yb_ref, "y tiled")
+
+
+def test_w4a8_extremes():
+    K = 4096
+    M, N = 3, 4
+    q = np.full((M, K), -128, np.int8)
+    q[1] = 127
+    q[2] = -127
+    wv = np.full((N, K), -8, np.int8)
+    wv[1] = 7
+    wv[2, 1::2] = 7
+    wv[3] = 0
+    w4 = wl.pack_int4(wv)
+    s_a = np.ones(M, np.float32)
+    s_w = np.ones(N, np.float32)
+    y_ref, acc_ref = oracle.gemm_w4a8(q, s_a, w4, s_w)
+    for rows in (M, 100):  # small-M kernel and tiled kernel
+        qq = np.tile(q, (rows // M + 1, 1))[:rows]
+        acc = torch.empty((rows, N), dtype=torch.int32, device=DEV)
+        prism.gemm_w4a8(dev(qq), dev(np.ones(rows, np.float32)), dev(w4), dev(s_w), acc=acc)
+        torch.cuda.synchronize()
+        assert_same_ints(host(acc)[:M], acc_ref, "acc rows=%d" % rows)
+
+
+def test_blockscale_every_fp16_pattern():
+    """One output per binary16 bit pattern: y = fmaf(1, d, +0) * 1 = d (NaN stays NaN)."""
+    N, K = 65536, 32
+    x = np.zeros((1, K), np.float32)
+    x[0, 0], x[0, 1] = 1.0, 127.0            # scale 1, codes [1, 127, 0, ...]
+    q, s_a = oracle.quantize_rows(x)
+    assert s_a[0] == 1.0
+    w = np.zeros((N, K), np.int8)
+    w[:, 0] = 1                              # P = 1 for every row
+    d = np.arange(N, dtype=np.uint32).astype(np.uint16).reshape(N, 1)
+    y_ref, _ = oracle.gemm_w8a8_blockscale(q, s_a, w, d)
+    y = prism.gemm_w8a8_blockscale(dev(q), dev(s_a), dev(w), dev(d))
+    torch.cuda.synchronize()
+    assert_same_floats(host(y), y_ref, "y")
+    # and the same through a 65-row batch (different tile position of the row)
+    qb = np.zeros((65, K), np.int8)
+    qb[64] = q[0]
+    sab = np.ones(65, np.float32)
+    yb = prism.gemm_w8a8_blockscale(dev(qb), dev(sab), dev(w), dev(d))
+    torch.cuda.synchronize()
+    assert_same_floats(host(yb)[64:65], y_ref, "y row 64")
+
+
+def test_epilogue_subnormal_outputs():
+    """Products that land in the fp32 subnormal range must not be flushed."""
+    rng = np.random.default_rng(9)
+    M, N, K = 70, 40, 64
+    q = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    w = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    s_a = np.full(M, 2.0 ** -85, np.float32)
+    s_w = rng.uniform(1e-3, 1e-2, N).astype(np.float32) * np.float32(2.0 ** -60)
+    y_ref, _ = oracle.gemm_w8a8(q, s_a, w, s_w)
+    assert (np.abs(y_ref[y_ref != 0]) < 1.2e-38).all()
+    for rows in (5, M):
+        y = prism.gemm_w8a8(dev(q[:rows]), dev(s_a[:rows]), dev(w), dev(s_w))
+        torch.cuda.synchronize()
+        assert_same_floats(host(y), y_ref[:rows], "y rows=%d" % rows)
+
+
+def test_m_zero_is_a_no_op():
+    y = torch.full((0, 16), 1.0, device=DEV)
+    out = prism.gemm_w8a8(torch.empty((0, 64), dtype=torch.int8, device=DEV),
+                          torch.empty((0,), dtype=torch.float32, device=DEV),
+                          torch.zeros((16, 64), dtype=torch.int8, device=DEV),
+                          torch.ones((16,), dtype=torch.float32, device=DEV), y=y)
+    assert out.shape == (0, 16)
+    q, s = prism.quantize_rows(torch.empty((0, 32), dtype=torch.float32, device=DEV))
+    assert q.shape == (0, 32) and s.shape == (0,)
+
+
+def test_invalid_shapes_raise_before_launch():
+    q = torch.zeros((4, 40), dtype=torch.int8, device=DEV)   # K = 40 is not a multiple of 16
+    with pytest.raises(prism.PrismError) as e:
+        prism.gemm_w8a8(q, torch.ones(4, device=DEV), torch.zeros((8, 40), dtype=torch.int8, device=DEV),
+                        torch.ones(8, device=DEV))
+    assert e.value.status == -2

@@ -1,0 +1,348 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact int8 linear layer on one MI355X.
+
+A step is one pass of the hot path over one batch of the 4B-class projection
+prefill workload (M = 512 tokens, W8A8 with per-channel scales):
+    quantize rows of X_up [512 x 2560]  -> GEMM with W_up   [9728 x 2560]
+    quantize rows of X_dn [512 x 9728]  -> GEMM with W_down [2560 x 9728]
+Inputs are synthetic and seeded (exact_int8_gemm_amd.workloads) and resident
+in HBM before timing starts.  R copies of every input set are rotated so that
+the working set exceeds the 256 MB MALL plus L2, so operands come from HBM.
+
+Printed: one JSON line with the whole-step int8 throughput (TOPS), the
+roofline of the dominant kernel (measured with HIP events around its
+launches inside the timed region), the CPU oracle's throughput on a bounded
+sample, and per-kernel measurements of the other workloads (W4A8 decode,
+block-scale, batch-invariance stress) under "kernels".
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+METRIC = "int8 TOPS (and GB/s at small M) as % of MI355X roofline, bit-exact"
+ROTATE_BYTES = 640 << 20     # rotate input copies until the working set exceeds this
+
+
+def _args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel measurements of other workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", default=None, help="run only one kernel measurement (for profiling): "
+                    "step | w4a8 | block | stress")
+    return ap.parse_args()
+
+
+class Launcher:
+    """Direct ctypes calls of the C ABI with pointers resolved once (no per-call checks)."""
+
+    def __init__(self, prism, stream):
+        self.lib = prism.lib()
+        self.stream = ctypes.c_void_p(stream)
+
+    @staticmethod
+    def p(t):
+        return ctypes.c_void_p(t.data_ptr())
+
+    def quantize(self, x, q, s):
+        M, K = x.shape
+        f, a = self.lib.prism_quantize_rows, (self.p(x), self.p(q), self.p(s), M, K, self.stream)
+        return lambda: f(*a)
+
+    def w8a8(self, q, sa, w, sw, y):
+        M, K = q.shape
+        N = w.shape[0]
+        f, a = self.lib.prism_gemm_w8a8, (self.p(q), self.p(sa), self.p(w), self.p(sw), self.p(y), None, M, N, K,
+                                          self.stream)
+        return lambda: f(*a)
+
+    def w4a8(self, q, sa, w4, sw, y):
+        M, K = q.shape
+        N = w4.shape[0]
+        f, a = self.lib.prism_gemm_w4a8, (self.p(q), self.p(sa), self.p(w4), self.p(sw), self.p(y), None, M, N, K,
+                                          self.stream)
+        return lambda: f(*a)
+
+    def block(self, q, sa, w, d, y):
+        M, K = q.shape
+        N = w.shape[0]
+        f, a = self.lib.prism_gemm_w8a8_blockscale, (self.p(q), self.p(sa), self.p(w), self.p(d), self.p(y), None,
+                                                     M, N, K, self.stream)
+        return lambda: f(*a)
+
+
+def _check(status):
+    if status != 0:
+        raise RuntimeError("prism call failed with status %d" % status)
+
+
+def _copies(bytes_per_set):
+    return max(2, -(-ROTATE_BYTES // max(1, bytes_per_set)))
+
+
+def _src_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "exact_int8_gemm_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key, src_hash):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_" + kernel_key + ".md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("{") and '"traffic_bytes"' in line:
+            rec = json.loads(line)
+            if rec.get("src_hash") == src_hash:
+                return rec["traffic_bytes"]
+    return None
+
+
+# --------------------------------------------------------------------- headline
+
+def headline(torch, prism, wl, args):
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    L = Launcher(prism, stream.cuda_stream)
+    up, dn = wl.proj_up(), wl.proj_down()
+    M = up["x"].shape[0]
+
+    def T(a):
+        return torch.from_numpy(a).to(dev)
+
+    per_set = sum(c["x"].nbytes + c["w"].nbytes + c["x"].shape[0] * (c["x"].shape[1] + 4 * c["w"].shape[0])
+                  for c in (up, dn))
+    R = _copies(per_set)
+    sets = []
+    for _ in range(R):
+        s = []
+        for c in (up, dn):
+            Mx, K = c["x"].shape
+            N = c["w"].shape[0]
+            x, w, sw = T(c["x"]), T(c["w"]), T(c["s_w"])
+            q = torch.empty((Mx, K), dtype=torch.int8, device=dev)
+            sa = torch.empty((Mx,), dtype=torch.float32, device=dev)
+            y = torch.empty((Mx, N), dtype=torch.float32, device=dev)
+            # the launchers hold raw pointers only: keep every tensor referenced here
+            s.append(dict(quant=L.quantize(x, q, sa), gemm=L.w8a8(q, sa, w, sw, y), x=x, w=w, sw=sw, y=y, q=q,
+                          sa=sa))
+        sets.append(s)
+    torch.cuda.synchronize()
+
+    E = torch.cuda.Event
+    ev = [[(E(enable_timing=True), E(enable_timing=True)) for _ in range(2)] for _ in range(args.steps)]
+
+    def step(i, record):
+        for j, p in enumerate(sets[i % R]):
+            _check(p["quant"]())
+            if record is not None:
+                record[j][0].record(stream)
+            _check(p["gemm"]())
+            if record is not None:
+                record[j][1].record(stream)
+
+    for i in range(args.warmup):
+        step(i, None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    gemm_ms = [[ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(args.steps)] for j in range(2)]
+    ops_per_gemm = 2 * M * 2560 * 9728
+    ops_step = 2 * ops_per_gemm
+    ms_step = wall * 1e3 / args.steps
+    avg_gemm_s = sum(gemm_ms[0] + gemm_ms[1]) / (2 * args.steps) / 1e3
+    bytes_up = 9728 * 2560 + 9728 * 4 + M * 2560 + M * 4 + M * 9728 * 4
+    bytes_dn = 2560 * 9728 + 2560 * 4 + M * 9728 + M * 4 + M * 2560 * 4
+    achieved = ops_per_gemm / avg_gemm_s / 1e12
+    src = _src_hash(["gemm_tiled.hip", "gemm_small.hip", "prism_abi.cpp"])
+    last = sets[(args.steps - 1) % R]
+    return dict(
+        value=ops_step / (ms_step / 1e3) / 1e12, ms_per_step=ms_step, R=R, M=M,
+        roofline=dict(bound="mfma", achieved=achieved, peak=PEAK_INT8_TOPS, unit="TFLOP/s",
+                      frac=achieved / PEAK_INT8_TOPS, traffic=_traffic("gemm_w8a8_proj_prefill", src),
+                      kernel="prism gemm_tiled_kernel (W8A8, per-channel)",
+                      ops_per_launch=ops_per_gemm, avg_launch_us=avg_gemm_s * 1e6,
+                      up_us=sum(gemm_ms[0]) / args.steps * 1e3, down_us=sum(gemm_ms[1]) / args.steps * 1e3,
+                      hbm_frac_up=bytes_up / (sum(gemm_ms[0]) / args.steps / 1e3) / 1e9 / PEAK_HBM_GBS,
+                      hbm_frac_down=bytes_dn / (sum(gemm_ms[1]) / args.steps / 1e3) / 1e9 / PEAK_HBM_GBS),
+        outputs=[(p["q"], p["sa"], p["y"]) for p in last], inputs=(up, dn))
+
+
+# --------------------------------------------------------------- other kernels
+
+def _time_launches(torch, fns, reps):
+    """Average duration (s) of launches cycled from fns, each bracketed by events."""
+    E = torch.cuda.Event
+    pairs = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(reps)]
+    s = torch.cuda.current_stream()
+    for i in range(min(len(fns), 4)):
+        _check(fns[i % len(fns)]())
+    torch.cuda.synchronize()
+    for i in range(reps):
+        pairs[i][0].record(s)
+        _check(fns[i % len(fns)]())
+        pairs[i][1].record(s)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in pairs) / reps / 1e3
+
+
+def kernels(torch, prism, wl, only=None):
+    dev = torch.device("cuda:0")
+    L = Launcher(prism, torch.cuda.current_stream(dev).cuda_stream)
+
+    def T(a):
+        a = a.view("int16") if a.dtype.name == "uint16" else a
+        return torch.from_numpy(a).to(dev)
+
+    out = {}
+    if only in (None, "w4a8"):
+        c = wl.w4()
+        K, N = 4096, 12288
+        R = _copies(c["w4"].nbytes)
+        ws = [T(c["w4"]) for _ in range(R)]
+        sw = T(c["s_w"])
+        for M in (1, 4, 16, 64):
+            x = T(c["x"][:M].copy())
+            q = torch.empty((M, K), dtype=torch.int8, device=dev)
+            sa = torch.empty((M,), dtype=torch.float32, device=dev)
+            _check(L.quantize(x, q, sa)())
+            y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            t = _time_launches(torch, [L.w4a8(q, sa, w, sw, y) for w in ws], 100)
+            nbytes = N * K // 2 + 4 * N + M * K + 4 * M + 4 * M * N
+            out["w4a8_m%d" % M] = dict(us=t * 1e6, gbs=nbytes / t / 1e9, hbm_frac=nbytes / t / 1e9 / PEAK_HBM_GBS,
+                                       tops=2 * M * N * K / t / 1e12, algorithmic_bytes=nbytes, copies=R)
+        del ws
+    if only in (None, "block"):
+        c = wl.block()
+        M, K = c["x"].shape
+        N = c["w"].shape[0]
+        R = _copies(c["w"].nbytes + c["d"].nbytes)
+        ws = [(T(c["w"]), T(c["d"])) for _ in range(R)]
+        x = T(c["x"])
+        q = torch.empty((M, K), dtype=torch.int8, device=dev)
+        sa = torch.empty((M,), dtype=torch.float32, device=dev)
+        _check(L.quantize(x, q, sa)())
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        t = _time_launches(torch, [L.block(q, sa, w, d, y) for w, d in ws], 10)
+        ops = 2 * M * N * K
+        # fp32 VALU bound of the block epilogue: one convert and one fma per 32-k partial,
+        # 256 CUs x 64 lanes x 2.4 GHz lane-operations per second
+        valu_s = M * N * (K // 32) * 2 / (256 * 64 * 2.4e9)
+        out["block_scale_m2048"] = dict(us=t * 1e6, tops=ops / t / 1e12, mfma_frac=ops / t / 1e12 / PEAK_INT8_TOPS,
+                                        valu_bound_us=valu_s * 1e6, valu_frac=valu_s / t, copies=R)
+        del ws
+    if only in (None, "stress"):
+        st = wl.stress()
+        w, sw = T(st["w"]), T(st["s_w"])
+        K = N = 5120
+        x_over, _ = wl.stress_overwrite(st)
+        for M, xa in ((8192, x_over), (1, st["x_probe"][:1].copy())):
+            x = T(xa)
+            q = torch.empty((M, K), dtype=torch.int8, device=dev)
+            sa = torch.empty((M,), dtype=torch.float32, device=dev)
+            tq = _time_launches(torch, [L.quantize(x, q, sa)], 20)
+            y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            t = _time_launches(torch, [L.w8a8(q, sa, w, sw, y)], 20 if M > 1 else 100)
+            nbytes = N * K + 4 * N + M * K + 4 * M + 4 * M * N
+            out["stress_m%d" % M] = dict(us=t * 1e6, tops=2 * M * N * K / t / 1e12,
+                                         mfma_frac=2 * M * N * K / t / 1e12 / PEAK_INT8_TOPS,
+                                         gbs=nbytes / t / 1e9, hbm_frac=nbytes / t / 1e9 / PEAK_HBM_GBS,
+                                         quantize_us=tq * 1e6,
+                                         quantize_gbs=(5 * M * K + 4 * M) / tq / 1e9)
+    return out
+
+
+# ------------------------------------------------------------------ CPU oracle
+
+def cpu_baseline(np, oracle, up, dn, gpu_outputs, budget_s=10.0):
+    """The oracle, as it stands, on the host cores: the same step (quantize + GEMM,
+    up and down); full steps repeated until the budget is spent, or a row subset
+    if one full step would take far longer than the budget."""
+    M = up["x"].shape[0]
+    t0 = time.perf_counter()
+    oracle.gemm_w8a8(*oracle.quantize_rows(up["x"][:8]), up["w"], up["s_w"])
+    oracle.gemm_w8a8(*oracle.quantize_rows(dn["x"][:8]), dn["w"], dn["s_w"])
+    est_full = (time.perf_counter() - t0) * M / 8
+    rows = M if est_full <= 3 * budget_s else max(8, int(M * budget_s / est_full) // 8 * 8)
+    done, reps, outs = 0.0, 0, None
+    t0 = time.perf_counter()
+    while reps == 0 or (time.perf_counter() - t0 < budget_s and rows == M):
+        outs = []
+        for c in (up, dn):
+            q, s = oracle.quantize_rows(c["x"][:rows])
+            y, _ = oracle.gemm_w8a8(q, s, c["w"], c["s_w"])
+            outs.append((q, s, y))
+        reps += 1
+    dt = time.perf_counter() - t0
+    ops = reps * 2 * (2 * rows * 2560 * 9728)
+    exact = True
+    for (q, s, y), (gq, gs, gy) in zip(outs, gpu_outputs):
+        exact &= bool(np.array_equal(gq[:rows], q) and np.array_equal(gs[:rows].view(np.uint32), s.view(np.uint32))
+                      and np.array_equal(gy[:rows].view(np.uint32), y.view(np.uint32)))
+    sample = ("%d full step(s) (quantize + GEMM, up and down, M=%d)" % (reps, M) if rows == M else
+              "rows 0..%d of one step (quantize + GEMM, up and down)" % (rows - 1))
+    return dict(value=ops / dt / 1e12, unit="TOPS", cores=oracle.max_threads(), kind="oracle", sample=sample,
+                seconds=dt, cpu=platform.processor() or platform.machine(), nproc=os.cpu_count()), exact
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from exact_int8_gemm_amd import prism
+    from exact_int8_gemm_amd import workloads as wl
+
+    if args.only is not None and args.only != "step":
+        print(json.dumps(kernels(torch, prism, wl, only=args.only)))
+        return
+    h = headline(torch, prism, wl, args)
+    rec = {
+        "metric": METRIC, "value": h["value"], "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": h["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": "4B-class projection prefill, W8A8 per-channel: quantize rows + GEMM for "
+                               "up (M=512, K=2560, N=9728) and down (M=512, K=9728, N=2560)",
+                   "M": h["M"], "rotated_input_copies": h["R"], "parallelism": "single GPU"},
+        "roofline": h["roofline"],
+    }
+    if args.only is None and not args.no_cpu:
+        import oracle
+        outs = [(o[0].cpu().numpy(), o[1].cpu().numpy(), o[2].cpu().numpy()) for o in h["outputs"]]
+        cb, exact = cpu_baseline(np, oracle, h["inputs"][0], h["inputs"][1], outs)
+        rec["cpu_baseline"] = cb
+        rec["bit_exact_vs_oracle"] = exact
+    if args.only is None and not args.no_kernels:
+        rec["kernels"] = kernels(torch, prism, wl)
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

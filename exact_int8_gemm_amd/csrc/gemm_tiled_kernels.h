@@ -1,0 +1,663 @@
+// LDS-tiled GEMM kernels for gfx950: W8A8 and W4A8 with per-channel scales,
+// and W8A8 with fp16 scales per 32-k block.
+//
+// The exact int32 sums of the StartLux-Prism README ("Why StartLux-Prism",
+// "How it works") are computed with v_mfma_i32_32x32x32_i8.  One workgroup
+// owns a BM x BN output tile and walks K in stages of BK bytes:
+//
+//  * software pipeline: the 16-byte global loads of stage k+2 are issued
+//    into one of two register sets while stage k is multiplied out of LDS
+//    and stage k+1 waits in the other register set; stage k+1 is written to
+//    the second LDS buffer at the end of the iteration, then one barrier.
+//    A load therefore has about two stages of MFMA work to arrive;
+//  * LDS rows are BK + 16 bytes apart, which puts the 16-byte operand reads
+//    of 8 (or 16) consecutive lanes into distinct bank groups;
+//  * 4-bit weights are unpacked once per tile on their way into LDS (nibble
+//    moved to the top of a byte, i.e. 16 * w as int8), so the inner loop is
+//    the same as for int8 weights and the accumulator is shifted right by 4;
+//  * MFMA lane layout (32x32x32): lane l supplies row (l % 32) of the A tile
+//    and column (l % 32) of the B tile, with k-group l / 32; both operands use
+//    the same lane -> k assignment, so the integer sum is the plain dot
+//    product.  The int32 result of lane l, register r sits at row
+//    8 * (r / 4) + 4 * (l / 32) + (r % 4), column l % 32;
+//  * workgroups are renumbered so that each of the 8 XCDs (which receive
+//    workgroups round-robin) runs a contiguous range of tiles, walked in
+//    groups of 8 tile rows so that neighbouring tiles share operand panels
+//    in that XCD's L2.
+//
+// Epilogues, per element and in a fixed order:
+//   per channel: y = ((float)acc * s_a[m]) * s_w[n]
+//   per block:   f = +0; for b ascending f = fmaf((float)P_b, (float)d[n][b], f);
+//                y = f * s_a[m]
+#pragma once
+
+#include "prism_internal.h"
+
+namespace prism {
+namespace tiled {
+
+__device__ inline void unpack_w4(const v4i p, v4i& lo, v4i& hi) {
+  int o[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t u = (uint32_t)p[j];
+    const uint32_t L = (u << 4) & 0xF0F0F0F0u;  // even k: low nibbles, moved up
+    const uint32_t H = u & 0xF0F0F0F0u;         // odd k: high nibbles, in place
+    // byte order of the output: L0 H0 L1 H1 | L2 H2 L3 H3
+    o[2 * j] = (int)__builtin_amdgcn_perm(H, L, 0x05010400u);
+    o[2 * j + 1] = (int)__builtin_amdgcn_perm(H, L, 0x07030602u);
+  }
+  lo = v4i{o[0], o[1], o[2], o[3]};
+  hi = v4i{o[4], o[5], o[6], o[7]};
+}
+
+// Tile index of this workgroup: XCD-contiguous renumbering, then grouped
+// row-major order over the tile grid.
+__device__ inline void tile_of(int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int G = (int)gridDim.x;
+  const int b = (int)blockIdx.x;
+  const int xcd = b % 8, r = b / 8;
+  const int base = G / 8, rem = G % 8;
+  const int id = xcd * base + min(xcd, rem) + r;
+  constexpr int kGroup = 8;
+  const int per_group = kGroup * tiles_n;
+  const int grp = id / per_group;
+  const int first = grp * kGroup;
+  const int gm = min(tiles_m - first, kGroup);
+  const int in = id - grp * per_group;
+  tm = first + in % gm;
+  tn = in / gm;
+}
+
+// Byte offset that a buffer access treats as out of range: loads return 0.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// Buffer resource over `bytes` bytes from `base` (raw, stride 0); accesses at
+// offsets past the end return zero.  Clamped below kOutOfRange.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < (int64_t)kOutOfRange - 1 ? bytes : (int64_t)kOutOfRange - 1;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+
+// One BK slice of the A (activation) and B (weight) tiles, held in registers
+// between its global loads and its LDS stores.  Loads are branch-free buffer
+// loads: a row outside the matrix has an out-of-range base offset and a
+// chunk past K is sent out of range, so both read zeros.
+template <int BM, int BN, int BK, int NT, bool W4>
+struct Stage {
+  static constexpr int kSA = BK + 16;                 // LDS row stride (bytes)
+  static constexpr int kCA = BK / 16;                 // 16-byte chunks per A row
+  static constexpr int kCB = W4 ? BK / 32 : BK / 16;  // 16-byte global chunks per B row
+  static constexpr int kNA = BM * kCA / NT;
+  static constexpr int kNB = BN * kCB / NT;
+  static_assert(BM * kCA % NT == 0 && BN * kCB % NT == 0, "tile chunks must divide among threads");
+
+  v4i a[kNA];
+  v4i b[kNB];
+};
+
+// Per-thread addressing of the stage loads and LDS stores, fixed for the
+// whole tile.
+template <int BM, int BN, int BK, int NT, bool W4>
+struct StageAddr {
+  using S = Stage<BM, BN, BK, NT, W4>;
+  __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t oa[S::kNA], ob[S::kNB];  // byte offset of the chunk at k0 = 0 (or out of range)
+  int ka[S::kNA], kb[S::kNB];       // k of the chunk at k0 = 0
+
+  __device__ inline void init(const int8_t* q, const int8_t* w, int m0, int n0, int M, int N, int K) {
+    const int tid = threadIdx.x;
+    const int64_t wrow = W4 ? K / 2 : K;
+    ra = make_rsrc(q + (size_t)m0 * (size_t)K, (int64_t)(M - m0) * K);
+    rb = make_rsrc(w + (size_t)n0 * (size_t)wrow, (int64_t)(N - n0) * wrow);
+#pragma unroll
+    for (int i = 0; i < S::kNA; ++i) {
+      const int idx = tid + i * NT;
+      const int r = idx / S::kCA, c = idx % S::kCA;
+      ka[i] = c * 16;
+      oa[i] = (m0 + r < M) ? (uint32_t)(r * K + c * 16) : kOutOfRange;
+    }
+#pragma unroll
+    for (int i = 0; i < S::kNB; ++i) {
+      const int idx = tid + i * NT;
+      const int r = idx / S::kCB, c = idx % S::kCB;
+      kb[i] = W4 ? c * 32 : c * 16;
+      ob[i] = (n0 + r < N) ? (uint32_t)(r * wrow + c * 16) : kOutOfRange;  // W4: 16 packed bytes = 32 k
+    }
+  }
+
+  __device__ inline void load(S& s, int k0, int K) const {
+#pragma unroll
+    for (int i = 0; i < S::kNA; ++i) {
+      const uint32_t off = (k0 + ka[i] < K) ? oa[i] + (uint32_t)k0 : kOutOfRange;
+      s.a[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < S::kNB; ++i) {
+      const uint32_t kb0 = W4 ? (uint32_t)(k0 / 2) : (uint32_t)k0;
+      const uint32_t off = (k0 + kb[i] < K) ? ob[i] + kb0 : kOutOfRange;
+      s.b[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+    }
+  }
+
+  __device__ inline void store(const S& s, int8_t* lds) const {
+    const int tid = threadIdx.x;
+    int8_t* sa = lds;
+    int8_t* sb = lds + BM * S::kSA;
+#pragma unroll
+    for (int i = 0; i < S::kNA; ++i) {
+      const int idx = tid + i * NT;
+      const int r = idx / S::kCA, c = idx % S::kCA;
+      *reinterpret_cast<v4i*>(sa + r * S::kSA + c * 16) = s.a[i];
+    }
+#pragma unroll
+    for (int i = 0; i < S::kNB; ++i) {
+      const int idx = tid + i * NT;
+      const int r = idx / S::kCB, c = idx % S::kCB;
+      if (W4) {
+        v4i lo, hi;
+        unpack_w4(s.b[i], lo, hi);
+        *reinterpret_cast<v4i*>(sb + r * S::kSA + c * 32) = lo;
+        *reinterpret_cast<v4i*>(sb + r * S::kSA + c * 32 + 16) = hi;
+      } else {
+        *reinterpret_cast<v4i*>(sb + r * S::kSA + c * 16) = s.b[i];
+      }
+    }
+  }
+};
+
+template <int BM, int BN, int BK, int WM, int WN>
+struct Geometry {
+  static constexpr int kNT = 64 * WM * WN;
+  static constexpr int kSA = BK + 16;
+  static constexpr int kWTM = BM / WM, kWTN = BN / WN;
+  static constexpr int kTM = kWTM / 32, kTN = kWTN / 32;
+  static constexpr int kLds = (BM + BN) * kSA;  // bytes per LDS buffer
+  static_assert(kTM * 32 == kWTM && kTN * 32 == kWTN, "wave tile must be a multiple of 32x32");
+  static_assert(BK % 32 == 0, "stage depth must be a multiple of 32");
+};
+
+// Scheduling masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+// Multiply-accumulate one LDS stage into acc.  The operand fragments of k-step
+// ks+1 are read from LDS while the MFMAs of k-step ks run (one fragment read
+// after each of the first MFMAs), so LDS latency hides behind matrix work.
+template <int BM, int BN, int BK, int WM, int WN>
+__device__ inline void mma_stage(const int8_t* lds, int wm, int wn, int lane,
+                                 v16i (&acc)[Geometry<BM, BN, BK, WM, WN>::kTM][Geometry<BM, BN, BK, WM, WN>::kTN]) {
+  using G = Geometry<BM, BN, BK, WM, WN>;
+  constexpr int KS = BK / 32;
+  constexpr int NF = G::kTM + G::kTN;  // fragments per k-step
+  const int rl = lane & 31, kg = (lane >> 5) * 16;
+  const int8_t* sa = lds + (wm * G::kWTM + rl) * G::kSA + kg;
+  const int8_t* sb = lds + (BM + wn * G::kWTN + rl) * G::kSA + kg;
+  v4i af[2][G::kTM], bf[2][G::kTN];
+#pragma unroll
+  for (int i = 0; i < G::kTM; ++i) af[0][i] = *reinterpret_cast<const v4i*>(sa + i * 32 * G::kSA);
+#pragma unroll
+  for (int j = 0; j < G::kTN; ++j) bf[0][j] = *reinterpret_cast<const v4i*>(sb + j * 32 * G::kSA);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int cur = ks & 1, nxt = cur ^ 1;
+    if (ks + 1 < KS) {
+#pragma unroll
+      for (int i = 0; i < G::kTM; ++i)
+        af[nxt][i] = *reinterpret_cast<const v4i*>(sa + i * 32 * G::kSA + (ks + 1) * 32);
+#pragma unroll
+      for (int j = 0; j < G::kTN; ++j)
+        bf[nxt][j] = *reinterpret_cast<const v4i*>(sb + j * 32 * G::kSA + (ks + 1) * 32);
+    }
+#pragma unroll
+    for (int i = 0; i < G::kTM; ++i)
+#pragma unroll
+      for (int j = 0; j < G::kTN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[cur][i], bf[cur][j], acc[i][j], 0, 0, 0);
+    if (ks + 1 < KS) {
+      // interleave: MFMA, fragment read, MFMA, fragment read, ..., then the rest of the MFMAs
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, G::kTM * G::kTN - NF, 0);
+    }
+  }
+}
+
+template <int BM, int BN, int BK, int WM, int WN, bool W4, int OCC>
+__global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_tiled_kernel(const int8_t* __restrict__ q,
+                                                                       const float* __restrict__ s_a,
+                                                                       const int8_t* __restrict__ w,
+                                                                       const float* __restrict__ s_w,
+                                                                       float* __restrict__ y,
+                                                                       int32_t* __restrict__ acc_out, int M, int N,
+                                                                       int K, int tiles_m, int tiles_n) {
+  using G = Geometry<BM, BN, BK, WM, WN>;
+  __shared__ __attribute__((aligned(16))) int8_t lds[2][G::kLds];
+
+  int tm, tn;
+  tile_of(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  v16i acc[G::kTM][G::kTN];
+#pragma unroll
+  for (int i = 0; i < G::kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < G::kTN; ++j) acc[i][j] = v16i{};
+
+  StageAddr<BM, BN, BK, G::kNT, W4> ad;
+  ad.init(q, w, m0, n0, M, N, K);
+  Stage<BM, BN, BK, G::kNT, W4> s0, s1;
+  const int nk = (K + BK - 1) / BK;
+  auto mma = [&](int buf) { mma_stage<BM, BN, BK, WM, WN>(lds[buf], wm, wn, lane, acc); };
+
+  // Pipeline: stage k is in LDS buffer k % 2, stage k+1 waits in a register
+  // set, stage k+2 is being loaded into the other set.  The stage count is
+  // rounded up to even: stages at or past K load as zeros (every chunk is out
+  // of range), so the loop needs no tail and no conditions.
+  ad.load(s0, 0, K);
+  ad.load(s1, BK, K);
+  ad.store(s0, lds[0]);
+  __syncthreads();
+  // The scheduling barriers keep the global loads of a stage ahead of the
+  // MFMAs (so they have two stages of work to arrive) and the LDS writes of
+  // the waiting stage behind them.
+  for (int k = 0; k < nk; k += 2) {
+    ad.load(s0, (k + 2) * BK, K);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(0);
+    __builtin_amdgcn_sched_barrier(0);
+    ad.store(s1, lds[1]);
+    __syncthreads();
+    ad.load(s1, (k + 3) * BK, K);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(1);
+    __builtin_amdgcn_sched_barrier(0);
+    ad.store(s0, lds[0]);
+    __syncthreads();
+  }
+
+  const int rl = lane & 31;
+#pragma unroll
+  for (int j = 0; j < G::kTN; ++j) {
+    const int n = n0 + wn * G::kWTN + j * 32 + rl;
+    if (n >= N) continue;
+    const float sw = s_w[n];
+#pragma unroll
+    for (int i = 0; i < G::kTM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * G::kWTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (m < M) {
+          int a = acc[i][j][r];
+          if (W4) a >>= 4;  // exact: the sum is a multiple of 16
+          const size_t o = (size_t)m * (size_t)N + (size_t)n;
+          if (acc_out) acc_out[o] = a;
+          const float t = (float)a * s_a[m];
+          y[o] = t * sw;
+        }
+      }
+    }
+  }
+}
+
+__device__ inline float half_bits_to_float(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+// Block-scale W8A8: each 32-k block of a stage is one MFMA started from zero;
+// its exact int32 result is folded into fp32 accumulators in ascending block
+// order with one fused multiply-add per element.
+template <int BM, int BN, int BK, int WM, int WN, int OCC>
+__global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_blockscale_kernel(
+    const int8_t* __restrict__ q, const float* __restrict__ s_a, const int8_t* __restrict__ w,
+    const uint16_t* __restrict__ d, float* __restrict__ y, int32_t* __restrict__ partials, int M, int N, int K,
+    int tiles_m, int tiles_n) {
+  using G = Geometry<BM, BN, BK, WM, WN>;
+  constexpr int KS = BK / 32;  // 32-k blocks per stage
+  __shared__ __attribute__((aligned(16))) int8_t lds[2][G::kLds];
+
+  int tm, tn;
+  tile_of(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int rl = lane & 31, kg = (lane >> 5) * 16;
+  const int NB = K / 32;
+
+  float f[G::kTM][G::kTN][16];
+#pragma unroll
+  for (int i = 0; i < G::kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < G::kTN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) f[i][j][r] = 0.0f;
+
+  int ncol[G::kTN];
+#pragma unroll
+  for (int j = 0; j < G::kTN; ++j) ncol[j] = n0 + wn * G::kWTN + j * 32 + rl;
+
+  auto stage = [&](const int8_t* buf, int kt) {
+    float dv[G::kTN][KS];
+#pragma unroll
+    for (int j = 0; j < G::kTN; ++j)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int b = kt * KS + ks;
+        dv[j][ks] = (ncol[j] < N && b < NB) ? half_bits_to_float(d[(size_t)ncol[j] * (size_t)NB + b]) : 0.0f;
+      }
+    const int8_t* sa = buf + (wm * G::kWTM + rl) * G::kSA + kg;
+    const int8_t* sb = buf + (BM + wn * G::kWTN + rl) * G::kSA + kg;
+    const v16i zero = v16i{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int b = kt * KS + ks;
+      if (b >= NB) break;  // uniform over the workgroup
+      v4i af[G::kTM], bf[G::kTN];
+#pragma unroll
+      for (int i = 0; i < G::kTM; ++i) af[i] = *reinterpret_cast<const v4i*>(sa + i * 32 * G::kSA + ks * 32);
+#pragma unroll
+      for (int j = 0; j < G::kTN; ++j) bf[j] = *reinterpret_cast<const v4i*>(sb + j * 32 * G::kSA + ks * 32);
+#pragma unroll
+      for (int i = 0; i < G::kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < G::kTN; ++j) {
+          const v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], zero, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) f[i][j][r] = __builtin_fmaf((float)p[r], dv[j][ks], f[i][j][r]);
+          if (partials) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int m = m0 + wm * G::kWTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+              if (m < M && ncol[j] < N)
+                partials[((size_t)m * (size_t)N + (size_t)ncol[j]) * (size_t)NB + b] = p[r];
+            }
+          }
+        }
+    }
+  };
+
+  StageAddr<BM, BN, BK, G::kNT, false> ad;
+  ad.init(q, w, m0, n0, M, N, K);
+  Stage<BM, BN, BK, G::kNT, false> s0, s1;
+  const int nk = (K + BK - 1) / BK;
+  ad.load(s0, 0, K);
+  ad.load(s1, BK, K);
+  ad.store(s0, lds[0]);
+  __syncthreads();
+  for (int k = 0; k < nk; k += 2) {  // stages past K are skipped inside stage()
+    ad.load(s0, (k + 2) * BK, K);
+    stage(lds[0], k);
+    ad.store(s1, lds[1]);
+    __syncthreads();
+    ad.load(s1, (k + 3) * BK, K);
+    stage(lds[1], k + 1);
+    ad.store(s0, lds[0]);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int j = 0; j < G::kTN; ++j) {
+    if (ncol[j] >= N) continue;
+#pragma unroll
+    for (int i = 0; i < G::kTM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * G::kWTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (m < M) y[(size_t)m * (size_t)N + (size_t)ncol[j]] = f[i][j][r] * s_a[m];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS pipeline (int8 weights).
+//
+// Stages of BK bytes of k are copied from HBM straight into an LDS ring of
+// RING buffers by buffer_load_dwordx4 ... lds (no register staging): lane i
+// of a wave-wide copy writes 16 bytes at LDS base + 16 i, so one copy moves
+// 1024 / BK rows of BK bytes.  With BK = 128 every row of a copy is one full
+// 128-byte line, which halves the number of L2 requests compared with
+// 64-byte row pieces (the L2 request rate is what bounds this kernel).
+// Rows are BK bytes apart in LDS and the 16-byte chunks of row r are stored
+// in the order c ^ swz(r), chosen so that the fragment reads of 16
+// consecutive lanes (16 consecutive rows, same chunk) fall in 16 distinct
+// 16-byte groups of the 64 LDS banks.  Out-of-range copies (rows past M or N,
+// k past K) write zeros.
+//
+// Iteration k: wait until this wave's copies of stage k have landed (the
+// copies of the RING - 2 later stages may still be in flight), barrier (all
+// waves' copies of stage k landed, all waves done with stage k - 1), start
+// the copies of stage k + RING - 1 into the buffer of stage k - 1, then run
+// the MFMAs of stage k.  Copies are always issued, also for stages past K
+// (they write zeros and are never read), so the number of copies in flight
+// at each wait is a constant.
+namespace dma {
+
+// Raw buffer resource as four dwords (raw, stride 0): base address, bounds
+// `bytes` (clamped below kOutOfRange), data format word of gfx9.
+__device__ inline v4i rsrc_words(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const int64_t n = bytes < (int64_t)kOutOfRange - 1 ? bytes : (int64_t)kOutOfRange - 1;
+  return v4i{(int)(uint32_t)a, (int)(uint32_t)((a >> 32) & 0xFFFFu), (int)n, 0x00020000};
+}
+
+// One wave-wide 16-byte-per-lane copy from a buffer into LDS at lds_addr +
+// 16 * lane.  Written as inline assembly so that the compiler does not add
+// its own (conservative) waits for it: every copy is awaited explicitly with
+// wait_vmcnt before its data is read, and all are drained before the kernel
+// leaves the main loop.  No compiler-generated code in these kernels uses M0.
+__device__ inline void copy_to_lds(const v4i rsrc, uint32_t lds_addr, uint32_t voff) {
+  // lds_addr and rsrc are wave-uniform; readfirstlane puts them in SGPRs.
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+  const v4i r = v4i{__builtin_amdgcn_readfirstlane(rsrc[0]), __builtin_amdgcn_readfirstlane(rsrc[1]),
+                    __builtin_amdgcn_readfirstlane(rsrc[2]), __builtin_amdgcn_readfirstlane(rsrc[3])};
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(r)
+               : "memory");
+}
+
+// s_waitcnt with vmcnt <= n and no wait on the other counters (gfx9 encoding).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+__device__ inline uint32_t lds_addr(const int8_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int8_t*)p;
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int RING>
+struct Cfg {
+  static constexpr int kNW = WM * WN;
+  static constexpr int kNT = 64 * kNW;
+  static constexpr int kChunks = BK / 16;          // 16-byte chunks per row
+  static constexpr int kRowsPerCopy = 1024 / BK;   // rows per wave-wide copy
+  static constexpr int kRowsPerWindow = 256 / BK;  // rows per 256-byte bank window
+  static constexpr int kCopiesA = BM * BK / 1024;  // copies per stage
+  static constexpr int kCopiesB = BN * BK / 1024;
+  static constexpr int kPerWaveA = kCopiesA / kNW;
+  static constexpr int kPerWaveB = kCopiesB / kNW;
+  static constexpr int kPerWave = kPerWaveA + kPerWaveB;
+  static constexpr int kStage = (BM + BN) * BK;
+  static constexpr int kWTM = BM / WM, kWTN = BN / WN;
+  static constexpr int kTM = kWTM / 32, kTN = kWTN / 32;
+  static_assert(BK == 64 || BK == 128, "stage depth");
+  static_assert(kCopiesA % kNW == 0 && kCopiesB % kNW == 0, "copies must divide among waves");
+  static_assert(kTM * 32 == kWTM && kTN * 32 == kWTN, "wave tile must be a multiple of 32x32");
+  static_assert(RING >= 2 && RING <= 4, "ring depth");
+  static_assert(RING * kStage <= 160 * 1024, "LDS ring exceeds 160 KiB");
+  static_assert((RING - 2) * kPerWave < 64, "vmcnt range");
+  __device__ static int swz(int row) { return (row / kRowsPerWindow) % kChunks; }
+};
+
+template <int BM, int BN, int BK, int WM, int WN, int RING, int OCC>
+__global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(const int8_t* __restrict__ q,
+                                                                     const float* __restrict__ s_a,
+                                                                     const int8_t* __restrict__ w,
+                                                                     const float* __restrict__ s_w,
+                                                                     float* __restrict__ y,
+                                                                     int32_t* __restrict__ acc_out, int M, int N,
+                                                                     int K, int tiles_m, int tiles_n) {
+  using C = Cfg<BM, BN, BK, WM, WN, RING>;
+  // Separate buffers (not one indexed array), so that every copy and every
+  // read names its buffer statically.
+  __shared__ __attribute__((aligned(1024))) int8_t lds0[C::kStage];
+  __shared__ __attribute__((aligned(1024))) int8_t lds1[C::kStage];
+  __shared__ __attribute__((aligned(1024))) int8_t lds2[RING > 2 ? C::kStage : 16];
+  __shared__ __attribute__((aligned(1024))) int8_t lds3[RING > 3 ? C::kStage : 16];
+
+  int tm, tn;
+  tile_of(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  // Copy sources: this lane's row and chunk in each of the wave's copies.
+  const v4i ra = rsrc_words(q + (size_t)m0 * (size_t)K, (int64_t)(M - m0) * K);
+  const v4i rb = rsrc_words(w + (size_t)n0 * (size_t)K, (int64_t)(N - n0) * K);
+  uint32_t off[C::kPerWave];
+  int kc[C::kPerWave];
+#pragma unroll
+  for (int s = 0; s < C::kPerWave; ++s) {
+    const bool isA = s < C::kPerWaveA;
+    const int copy = isA ? wave * C::kPerWaveA + s : wave * C::kPerWaveB + (s - C::kPerWaveA);
+    const int row = copy * C::kRowsPerCopy + lane / C::kChunks;
+    const int chunk = (lane % C::kChunks) ^ C::swz(row);
+    kc[s] = chunk * 16;
+    const bool valid = isA ? (m0 + row < M) : (n0 + row < N);
+    off[s] = valid ? (uint32_t)(row * K + chunk * 16) : kOutOfRange;
+  }
+  auto issue = [&](int8_t* base, int stage) {
+    const int k0 = stage * BK;
+#pragma unroll
+    for (int s = 0; s < C::kPerWave; ++s) {
+      const bool isA = s < C::kPerWaveA;
+      const int copy = isA ? wave * C::kPerWaveA + s : wave * C::kPerWaveB + (s - C::kPerWaveA);
+      const uint32_t o = (k0 + kc[s] < K) ? off[s] + (uint32_t)k0 : kOutOfRange;
+      const int8_t* dst = base + (isA ? 0 : BM * BK) + copy * 1024;
+      copy_to_lds(isA ? ra : rb, lds_addr(dst), o);
+    }
+  };
+
+  v16i acc[C::kTM][C::kTN];
+#pragma unroll
+  for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::kTN; ++j) acc[i][j] = v16i{};
+
+  // Fragment reads: row (l % 32) of each 32-row tile, logical chunk
+  // 2 ks + l / 32, stored at chunk ^ swz(row) (tile bases are multiples of
+  // 32 rows, so swz depends on the lane only).
+  const int rl = lane & 31;
+  const int sw = C::swz(rl);
+  const int arow = (wm * C::kWTM + rl) * BK;
+  const int brow = (BM + wn * C::kWTN + rl) * BK;
+  constexpr int KS = BK / 32;
+
+  auto compute = [&](const int8_t* buf) {
+    v4i af[2][C::kTM], bf[2][C::kTN];
+    auto read = [&](int ks, int slot) {
+      const int c = ((2 * ks + (lane >> 5)) ^ sw) * 16;
+#pragma unroll
+      for (int i = 0; i < C::kTM; ++i) af[slot][i] = *reinterpret_cast<const v4i*>(buf + arow + i * 32 * BK + c);
+#pragma unroll
+      for (int j = 0; j < C::kTN; ++j) bf[slot][j] = *reinterpret_cast<const v4i*>(buf + brow + j * 32 * BK + c);
+    };
+    read(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) read(ks + 1, (ks + 1) & 1);
+#pragma unroll
+      for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kTN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks & 1][i], bf[ks & 1][j], acc[i][j], 0, 0, 0);
+    }
+  };
+  // One pipeline step: stage `stage` sits in `cur`; the copies of stage
+  // stage + RING - 1 go into `nxt` (the buffer of stage - 1).
+  auto step = [&](const int8_t* cur, int8_t* nxt, int stage) {
+    wait_vmcnt<(RING - 2) * C::kPerWave>();
+    __syncthreads();
+    issue(nxt, stage + RING - 1);
+    compute(cur);
+  };
+
+  // Stage count padded to a multiple of the ring: padded stages are all zero.
+  const int nk = (K + BK - 1) / BK;
+  const int nkr = (nk + RING - 1) / RING * RING;
+  issue(lds0, 0);
+  if constexpr (RING > 2) issue(lds1, 1);
+  if constexpr (RING > 3) issue(lds2, 2);
+  for (int k = 0; k < nkr; k += RING) {
+    if constexpr (RING == 2) {
+      step(lds0, lds1, k);
+      step(lds1, lds0, k + 1);
+    } else if constexpr (RING == 3) {
+      step(lds0, lds2, k);
+      step(lds1, lds0, k + 1);
+      step(lds2, lds1, k + 2);
+    } else {
+      step(lds0, lds3, k);
+      step(lds1, lds0, k + 1);
+      step(lds2, lds1, k + 2);
+      step(lds3, lds2, k + 3);
+    }
+  }
+  wait_vmcnt<0>();  // no copy may land in LDS after the workgroup ends
+
+#pragma unroll
+  for (int j = 0; j < C::kTN; ++j) {
+    const int n = n0 + wn * C::kWTN + j * 32 + rl;
+    if (n >= N) continue;
+    const float swn = s_w[n];
+#pragma unroll
+    for (int i = 0; i < C::kTM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * C::kWTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (m < M) {
+          const int a = acc[i][j][r];
+          const size_t o = (size_t)m * (size_t)N + (size_t)n;
+          if (acc_out) acc_out[o] = a;
+          const float t = (float)a * s_a[m];
+          y[o] = t * swn;
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int RING, int OCC>
+void launch(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc, int M,
+            int N, int K, hipStream_t st) {
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  gemm_dma_kernel<BM, BN, BK, WM, WN, RING, OCC>
+      <<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, 0, st>>>(q, s_a, w, s_w, y, acc, M, N, K, tiles_m, tiles_n);
+}
+
+}  // namespace dma
+
+template <int BM, int BN, int BK, int WM, int WN, bool W4, int OCC>
+void launch_tiled(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc,
+                  int M, int N, int K, hipStream_t st) {
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  gemm_tiled_kernel<BM, BN, BK, WM, WN, W4, OCC>
+      <<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, 0, st>>>(q, s_a, w, s_w, y, acc, M, N, K, tiles_m, tiles_n);
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int OCC>
+void launch_blockscale(const int8_t* q, const float* s_a, const int8_t* w, const uint16_t* d, float* y,
+                       int32_t* partials, int M, int N, int K, hipStream_t st) {
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  gemm_blockscale_kernel<BM, BN, BK, WM, WN, OCC><<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, 0, st>>>(
+      q, s_a, w, d, y, partials, M, N, K, tiles_m, tiles_n);
+}
+
+}  // namespace tiled
+}  // namespace prism

@@ -1,12 +1,13 @@
 // Per-row int8 activation quantizer (StartLux-Prism README, "Quick start":
 // int8 activation ranges; the per-row absmax form is the reading used here).
 //
-// One 64-lane wave owns one row, four rows per 256-thread workgroup.  The
-// row is streamed from HBM once with 16-byte loads and kept in registers
-// (CPT float4 per lane), the absmax is reduced across the wave (max is exact
-// and order-free), then the codes are written with one 4-byte store per
-// float4.  Rows longer than 256*kMaxCpt floats take a two-pass variant that
-// reads the row twice.
+// One workgroup owns one row and spreads it over up to 16 waves, so that a
+// few hundred rows already give every SIMD several waves to hide HBM latency
+// with.  Each thread loads CPT float4 of the row with 16-byte loads and keeps
+// them in registers, the absmax is reduced within each wave (shuffles) and
+// across waves (LDS, one barrier; max is exact and order-free), then the
+// codes are written with one 4-byte store per float4.  Rows longer than
+// 1024 * 4 * kMaxCpt floats take a two-pass variant that reads the row twice.
 //
 // Arithmetic per row (IEEE fp32, round to nearest even, no flushing):
 //   s = amax / 127;  q = clamp(rint(x / s), -127, 127)
@@ -19,8 +20,8 @@
 namespace prism {
 namespace {
 
-constexpr int kRowsPerBlock = 4;
-constexpr int kMaxCpt = 40;  // float4 per lane kept in registers: K <= 10240
+constexpr int kMaxThreads = 1024;
+constexpr int kMaxCpt = 16;  // float4 per thread kept in registers: K <= 65536
 
 __device__ inline float wave_max(float v) {
 #pragma unroll
@@ -50,16 +51,37 @@ __device__ inline float absmax4(const float4 v) {
   return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 }
 
-// Register-resident variant: the row's nchunk = K/4 float4 are spread over the
-// wave, chunk c on lane c % 64, slot c / 64 < CPT.
+// Row absmax and finiteness over the whole workgroup; every thread gets the
+// same answer.
+__device__ inline void row_reduce(float& amax, bool& finite) {
+  __shared__ float red_max[kMaxThreads / 64];
+  __shared__ int red_fin[kMaxThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  amax = wave_max(amax);
+  finite = __all(finite);
+  if (lane == 0) {
+    red_max[wave] = amax;
+    red_fin[wave] = finite ? 1 : 0;
+  }
+  __syncthreads();
+  const int nw = (int)(blockDim.x >> 6);
+  amax = red_max[0];
+  int fin = red_fin[0];
+  for (int i = 1; i < nw; ++i) {
+    amax = fmaxf(amax, red_max[i]);
+    fin &= red_fin[i];
+  }
+  finite = fin != 0;
+}
+
+// Register-resident variant: the row's K/4 float4 are spread over the
+// workgroup, chunk c on thread c % blockDim.x, slot c / blockDim.x < CPT.
 template <int CPT>
-__global__ __launch_bounds__(64 * kRowsPerBlock) void quantize_rows_reg(const float* __restrict__ x,
-                                                                        int8_t* __restrict__ q,
-                                                                        float* __restrict__ s, int64_t M,
-                                                                        int64_t K) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= M) return;  // whole wave leaves together
+__global__ __launch_bounds__(kMaxThreads) void quantize_rows_reg(const float* __restrict__ x,
+                                                                  int8_t* __restrict__ q, float* __restrict__ s,
+                                                                  int64_t K) {
+  const int64_t row = blockIdx.x;
+  const int T = (int)blockDim.x;
   const float4* xr = reinterpret_cast<const float4*>(x + row * K);
   uint32_t* qr = reinterpret_cast<uint32_t*>(q + row * K);
   const int64_t nchunk = K / 4;
@@ -69,77 +91,70 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void quantize_rows_reg(const fl
   bool finite = true;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int64_t c = lane + 64 * i;
+    const int64_t c = threadIdx.x + (int64_t)T * i;
     if (c < nchunk) {
       v[i] = xr[c];
       amax = fmaxf(amax, absmax4(v[i]));
       finite = finite && finite4(v[i]);
     }
   }
-  amax = wave_max(amax);
-  finite = __all(finite);
+  row_reduce(amax, finite);
 
   const float sc = finite ? amax / 127.0f : __builtin_nanf("");
-  if (lane == 0) s[row] = sc;
+  if (threadIdx.x == 0) s[row] = sc;
   const bool zero = !finite || sc == 0.0f;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int64_t c = lane + 64 * i;
+    const int64_t c = threadIdx.x + (int64_t)T * i;
     if (c < nchunk) qr[c] = zero ? 0u : pack4(v[i], sc);
   }
 }
 
 // Long rows: first pass reduces, second pass re-reads and quantizes.
-__global__ __launch_bounds__(64 * kRowsPerBlock) void quantize_rows_2pass(const float* __restrict__ x,
-                                                                          int8_t* __restrict__ q,
-                                                                          float* __restrict__ s, int64_t M,
-                                                                          int64_t K) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= M) return;
+__global__ __launch_bounds__(kMaxThreads) void quantize_rows_2pass(const float* __restrict__ x,
+                                                                    int8_t* __restrict__ q, float* __restrict__ s,
+                                                                    int64_t K) {
+  const int64_t row = blockIdx.x;
   const float4* xr = reinterpret_cast<const float4*>(x + row * K);
   uint32_t* qr = reinterpret_cast<uint32_t*>(q + row * K);
   const int64_t nchunk = K / 4;
 
   float amax = 0.0f;
   bool finite = true;
-  for (int64_t c = lane; c < nchunk; c += 64) {
+  for (int64_t c = threadIdx.x; c < nchunk; c += blockDim.x) {
     const float4 v = xr[c];
     amax = fmaxf(amax, absmax4(v));
     finite = finite && finite4(v);
   }
-  amax = wave_max(amax);
-  finite = __all(finite);
+  row_reduce(amax, finite);
 
   const float sc = finite ? amax / 127.0f : __builtin_nanf("");
-  if (lane == 0) s[row] = sc;
+  if (threadIdx.x == 0) s[row] = sc;
   const bool zero = !finite || sc == 0.0f;
-  for (int64_t c = lane; c < nchunk; c += 64) qr[c] = zero ? 0u : pack4(xr[c], sc);
+  for (int64_t c = threadIdx.x; c < nchunk; c += blockDim.x) qr[c] = zero ? 0u : pack4(xr[c], sc);
 }
 
 template <int CPT>
 void launch_reg(const float* x, int8_t* q, float* s, int64_t M, int64_t K, hipStream_t st) {
-  const unsigned grid = (unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock);
-  quantize_rows_reg<CPT><<<grid, 64 * kRowsPerBlock, 0, st>>>(x, q, s, M, K);
+  const int64_t nchunk = K / 4;
+  const int64_t per_cpt = (nchunk + CPT - 1) / CPT;
+  const int threads = (int)((per_cpt + 63) / 64 * 64);
+  quantize_rows_reg<CPT><<<(unsigned)M, threads, 0, st>>>(x, q, s, K);
 }
 
 }  // namespace
 
 int launch_quantize_rows(const float* x, int8_t* q, float* s, int64_t M, int64_t K, hipStream_t st) {
-  const int64_t cpt = (K / 4 + 63) / 64;
+  const int64_t cpt = (K / 4 + kMaxThreads - 1) / kMaxThreads;
   if (cpt <= 1) launch_reg<1>(x, q, s, M, K, st);
   else if (cpt <= 2) launch_reg<2>(x, q, s, M, K, st);
+  else if (cpt <= 3) launch_reg<3>(x, q, s, M, K, st);
   else if (cpt <= 4) launch_reg<4>(x, q, s, M, K, st);
+  else if (cpt <= 6) launch_reg<6>(x, q, s, M, K, st);
   else if (cpt <= 8) launch_reg<8>(x, q, s, M, K, st);
   else if (cpt <= 12) launch_reg<12>(x, q, s, M, K, st);
-  else if (cpt <= 16) launch_reg<16>(x, q, s, M, K, st);
-  else if (cpt <= 24) launch_reg<24>(x, q, s, M, K, st);
-  else if (cpt <= 32) launch_reg<32>(x, q, s, M, K, st);
   else if (cpt <= kMaxCpt) launch_reg<kMaxCpt>(x, q, s, M, K, st);
-  else {
-    const unsigned grid = (unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock);
-    quantize_rows_2pass<<<grid, 64 * kRowsPerBlock, 0, st>>>(x, q, s, M, K);
-  }
+  else quantize_rows_2pass<<<(unsigned)M, kMaxThreads, 0, st>>>(x, q, s, K);
   return launch_status();
 }
 

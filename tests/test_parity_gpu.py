@@ -22,7 +22,7 @@ M_SWEEP = [1, 2, 3, 7, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255
 # ------------------------------------------------------------------ quantizer
 
 @pytest.mark.parametrize("M,K", [(1, 16), (5, 48), (64, 256), (3, 512), (33, 2560), (8, 9728), (4, 10240),
-                                 (4, 10256), (2, 20480), (300, 512)])
+                                 (4, 10256), (2, 20480), (300, 512), (2, 65536), (2, 65552), (3, 131072)])
 def test_quantize_rows(M, K):
     rng = np.random.default_rng(M * 100003 + K)
     x = rng.standard_normal((M, K), dtype=np.float32)

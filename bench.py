@@ -42,6 +42,8 @@ def _args():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel measurements of other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy three times (scale for HBM byte counters)")
     ap.add_argument("--only", default=None, help="run only one kernel measurement (for profiling): "
                     "step | w4a8 | block | stress")
     return ap.parse_args()
@@ -92,6 +94,11 @@ def _check(status):
 
 def _copies(bytes_per_set):
     return max(2, -(-ROTATE_BYTES // max(1, bytes_per_set)))
+
+
+# Sources of the GEMM kernels: a traffic figure is used only if it was
+# measured on exactly these sources.
+KERNEL_SOURCES = ["gemm_tiled_kernels.h", "gemm_tiled.hip", "gemm_small.hip", "prism_abi.cpp", "prism_internal.h"]
 
 
 def _src_hash(names):
@@ -169,25 +176,35 @@ def headline(torch, prism, wl, args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    gemm_ms = [[ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(args.steps)] for j in range(2)]
-    ops_per_gemm = 2 * M * 2560 * 9728
-    ops_step = 2 * ops_per_gemm
+    gemm_us = [sum(ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(args.steps)) / args.steps * 1e3
+               for j in range(2)]
     ms_step = wall * 1e3 / args.steps
-    avg_gemm_s = sum(gemm_ms[0] + gemm_ms[1]) / (2 * args.steps) / 1e3
-    bytes_up = 9728 * 2560 + 9728 * 4 + M * 2560 + M * 4 + M * 9728 * 4
-    bytes_dn = 2560 * 9728 + 2560 * 4 + M * 9728 + M * 4 + M * 2560 * 4
-    achieved = ops_per_gemm / avg_gemm_s / 1e12
-    src = _src_hash(["gemm_tiled.hip", "gemm_small.hip", "prism_abi.cpp"])
+    ops_per_gemm = 2 * M * 2560 * 9728
+    src = _src_hash(KERNEL_SOURCES)
+    gemms = []
+    for j, (c, name, key) in enumerate(((up, "up-projection", "proj_up"), (dn, "down-projection", "proj_down"))):
+        K = c["x"].shape[1]
+        N = c["w"].shape[0]
+        nbytes = N * K + 4 * N + M * K + 4 * M + 4 * M * N  # W, s_w, q, s_a, y
+        t = gemm_us[j] / 1e6
+        t_mfma = ops_per_gemm / (PEAK_INT8_TOPS * 1e12)
+        t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+        if t_mfma >= t_hbm:
+            rec = dict(bound="mfma", achieved=ops_per_gemm / t / 1e12, peak=PEAK_INT8_TOPS, unit="TOPS")
+        else:
+            rec = dict(bound="hbm", achieved=nbytes / t / 1e9, peak=PEAK_HBM_GBS, unit="GB/s")
+        rec["frac"] = rec["achieved"] / rec["peak"]
+        rec["traffic"] = _traffic("gemm_w8a8_" + key, src)
+        rec.update(launch="%s GEMM, prism_gemm_w8a8 (M=%d, K=%d, N=%d)" % (name, M, K, N),
+                   avg_launch_us=gemm_us[j], ops_per_launch=ops_per_gemm, algorithmic_bytes_per_launch=nbytes,
+                   mfma_frac=ops_per_gemm / t / 1e12 / PEAK_INT8_TOPS, hbm_frac=nbytes / t / 1e9 / PEAK_HBM_GBS)
+        gemms.append(rec)
+    dominant = max(range(2), key=lambda j: gemm_us[j])
+    roof = dict(gemms[dominant])
+    roof["other_gemm"] = gemms[1 - dominant]
     last = sets[(args.steps - 1) % R]
     return dict(
-        value=ops_step / (ms_step / 1e3) / 1e12, ms_per_step=ms_step, R=R, M=M,
-        roofline=dict(bound="mfma", achieved=achieved, peak=PEAK_INT8_TOPS, unit="TFLOP/s",
-                      frac=achieved / PEAK_INT8_TOPS, traffic=_traffic("gemm_w8a8_proj_prefill", src),
-                      kernel="prism gemm_tiled_kernel (W8A8, per-channel)",
-                      ops_per_launch=ops_per_gemm, avg_launch_us=avg_gemm_s * 1e6,
-                      up_us=sum(gemm_ms[0]) / args.steps * 1e3, down_us=sum(gemm_ms[1]) / args.steps * 1e3,
-                      hbm_frac_up=bytes_up / (sum(gemm_ms[0]) / args.steps / 1e3) / 1e9 / PEAK_HBM_GBS,
-                      hbm_frac_down=bytes_dn / (sum(gemm_ms[1]) / args.steps / 1e3) / 1e9 / PEAK_HBM_GBS),
+        value=2 * ops_per_gemm / (ms_step / 1e3) / 1e12, ms_per_step=ms_step, R=R, M=M, roofline=roof,
         outputs=[(p["q"], p["sa"], p["y"]) for p in last], inputs=(up, dn))
 
 
@@ -323,6 +340,13 @@ def main():
     if args.only is not None and args.only != "step":
         print(json.dumps(kernels(torch, prism, wl, only=args.only)))
         return
+    if args.calib_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     h = headline(torch, prism, wl, args)
     rec = {
         "metric": METRIC, "value": h["value"], "unit": "TOPS", "n_gpus": 1, "steps": args.steps,

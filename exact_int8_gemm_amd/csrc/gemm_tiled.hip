@@ -20,12 +20,24 @@ inline int64_t tiles(int64_t M, int64_t N, int bm, int bn) { return ((M + bm - 1
 //    once they give every CU a tile;
 //  * 256 x 128 tiles (8 waves of 64 x 64, 3-deep ring) when those still give
 //    at least half of the CUs a tile;
-//  * 128 x 128 tiles (4 waves of 64 x 64, 4-deep ring) otherwise.
+//  * 128 x 128 tiles (4 waves of 64 x 64, 4-deep ring) otherwise, with K
+//    split over floor(256 / tiles) workgroups per tile (at most 4, at least 8
+//    stages each) whose exact int32 partial tiles are added atomically.
 void pick_int8(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc, int M,
                int N, int K, hipStream_t st) {
-  if (tiles(M, N, 256, 256) >= 256) tiled::dma::launch<256, 256, 128, 4, 2, 2, 1>(q, s_a, w, s_w, y, acc, M, N, K, st);
-  else if (tiles(M, N, 256, 128) >= 128) tiled::dma::launch<256, 128, 128, 4, 2, 3, 1>(q, s_a, w, s_w, y, acc, M, N, K, st);
-  else tiled::dma::launch<128, 128, 128, 2, 2, 4, 1>(q, s_a, w, s_w, y, acc, M, N, K, st);
+  if (tiles(M, N, 256, 256) >= 256) {
+    tiled::dma::launch<256, 256, 128, 4, 2, 2, 1>(q, s_a, w, s_w, y, acc, M, N, K, st);
+  } else if (tiles(M, N, 256, 128) >= 128) {
+    tiled::dma::launch<256, 128, 128, 4, 2, 3, 1>(q, s_a, w, s_w, y, acc, M, N, K, st);
+  } else {
+    const int64_t t = tiles(M, N, 128, 128);
+    const int64_t stages = (K + 127) / 128;
+    int64_t splits = 256 / t;
+    if (splits > 4) splits = 4;
+    if (splits > stages / 8) splits = stages / 8;
+    if (splits < 1) splits = 1;
+    tiled::dma::launch<128, 128, 128, 2, 2, 4, 1>(q, s_a, w, s_w, y, acc, M, N, K, st, (int)splits);
+  }
 }
 
 // 4-bit weights: register-staged pipeline that unpacks the nibbles on their

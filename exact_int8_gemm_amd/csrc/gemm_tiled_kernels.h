@@ -69,6 +69,26 @@ __device__ inline void tile_of(int tiles_m, int tiles_n, int& tm, int& tn) {
   tn = in / gm;
 }
 
+// Tile and k-split of this workgroup: workgroup ids are split-major inside
+// each XCD's range, so the splits of one tile run on the same XCD.
+__device__ inline void tile_of_split(int tiles_m, int tiles_n, int splits, int& tm, int& tn, int& split) {
+  const int G = (int)gridDim.x;
+  const int b = (int)blockIdx.x;
+  const int xcd = b % 8, r = b / 8;
+  const int base = G / 8, rem = G % 8;
+  const int id = xcd * base + min(xcd, rem) + r;
+  const int tile = id / splits;
+  split = id - tile * splits;
+  constexpr int kGroup = 8;
+  const int per_group = kGroup * tiles_n;
+  const int grp = tile / per_group;
+  const int first = grp * kGroup;
+  const int gm = min(tiles_m - first, kGroup);
+  const int in = tile - grp * per_group;
+  tm = first + in % gm;
+  tn = in / gm;
+}
+
 // Byte offset that a buffer access treats as out of range: loads return 0.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
@@ -495,6 +515,11 @@ struct Cfg {
   __device__ static int swz(int row) { return (row / kRowsPerWindow) % kChunks; }
 };
 
+// splits > 1: workgroup (tile, split) sums the split-th contiguous range of
+// stages and adds its int32 partial tile into y viewed as int32 (zeroed
+// before; the fp32 epilogue runs afterwards in finalize_kernel).  Integer
+// addition is exact and associative, so the result does not depend on the
+// order in which the partial tiles arrive.
 template <int BM, int BN, int BK, int WM, int WN, int RING, int OCC>
 __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(const int8_t* __restrict__ q,
                                                                      const float* __restrict__ s_a,
@@ -502,7 +527,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(const int8_
                                                                      const float* __restrict__ s_w,
                                                                      float* __restrict__ y,
                                                                      int32_t* __restrict__ acc_out, int M, int N,
-                                                                     int K, int tiles_m, int tiles_n) {
+                                                                     int K, int tiles_m, int tiles_n, int splits) {
   using C = Cfg<BM, BN, BK, WM, WN, RING>;
   // Separate buffers (not one indexed array), so that every copy and every
   // read names its buffer statically.
@@ -511,11 +536,17 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(const int8_
   __shared__ __attribute__((aligned(1024))) int8_t lds2[RING > 2 ? C::kStage : 16];
   __shared__ __attribute__((aligned(1024))) int8_t lds3[RING > 3 ? C::kStage : 16];
 
-  int tm, tn;
-  tile_of(tiles_m, tiles_n, tm, tn);
+  int tm, tn, split;
+  tile_of_split(tiles_m, tiles_n, splits, tm, tn, split);
   const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
+
+  // This split's stages [kb, ke); copies are bounded by kend, so the padded
+  // stages of the ring (past ke) read as zeros instead of other splits' k.
+  const int nk = (K + BK - 1) / BK;
+  const int kb = (int)((int64_t)split * nk / splits), ke = (int)((int64_t)(split + 1) * nk / splits);
+  const int kend = ke * BK < K ? ke * BK : K;
 
   // Copy sources: this lane's row and chunk in each of the wave's copies.
   const v4i ra = rsrc_words(q + (size_t)m0 * (size_t)K, (int64_t)(M - m0) * K);
@@ -538,7 +569,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(const int8_
     for (int s = 0; s < C::kPerWave; ++s) {
       const bool isA = s < C::kPerWaveA;
       const int copy = isA ? wave * C::kPerWaveA + s : wave * C::kPerWaveB + (s - C::kPerWaveA);
-      const uint32_t o = (k0 + kc[s] < K) ? off[s] + (uint32_t)k0 : kOutOfRange;
+      const uint32_t o = (k0 + kc[s] < kend) ? off[s] + (uint32_t)k0 : kOutOfRange;
       const int8_t* dst = base + (isA ? 0 : BM * BK) + copy * 1024;
       copy_to_lds(isA ? ra : rb, lds_addr(dst), o);
     }
@@ -588,13 +619,12 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(const int8_
     compute(cur);
   };
 
-  // Stage count padded to a multiple of the ring: padded stages are all zero.
-  const int nk = (K + BK - 1) / BK;
-  const int nkr = (nk + RING - 1) / RING * RING;
-  issue(lds0, 0);
-  if constexpr (RING > 2) issue(lds1, 1);
-  if constexpr (RING > 3) issue(lds2, 2);
-  for (int k = 0; k < nkr; k += RING) {
+  // Stage count padded to a multiple of the ring: padded stages read zeros.
+  const int nkr = (ke - kb + RING - 1) / RING * RING;
+  issue(lds0, kb);
+  if constexpr (RING > 2) issue(lds1, kb + 1);
+  if constexpr (RING > 3) issue(lds2, kb + 2);
+  for (int k = kb; k < kb + nkr; k += RING) {
     if constexpr (RING == 2) {
       step(lds0, lds1, k);
       step(lds1, lds0, k + 1);
@@ -610,6 +640,25 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(const int8_
     }
   }
   wait_vmcnt<0>();  // no copy may land in LDS after the workgroup ends
+
+  if (splits > 1) {
+    int32_t* yi = reinterpret_cast<int32_t*>(y);
+#pragma unroll
+    for (int j = 0; j < C::kTN; ++j) {
+      const int n = n0 + wn * C::kWTN + j * 32 + rl;
+      if (n >= N) continue;
+#pragma unroll
+      for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm * C::kWTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          if (m < M)
+            __hip_atomic_fetch_add(yi + (size_t)m * (size_t)N + (size_t)n, acc[i][j][r], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    return;
+  }
 
 #pragma unroll
   for (int j = 0; j < C::kTN; ++j) {
@@ -633,12 +682,38 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(const int8_
   }
 }
 
+// Split-K helpers: zero y (as int32) before the partial tiles are added, and
+// turn the exact int32 sums into the per-channel fp32 epilogue afterwards,
+// in place, one element per thread.
+__global__ __launch_bounds__(256) void zero_kernel(int32_t* __restrict__ p, int64_t n) {
+  const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+#pragma unroll
+  for (int64_t i = i0; i < i0 + 4; ++i)
+    if (i < n) p[i] = 0;
+}
+
+__global__ __launch_bounds__(256) void finalize_kernel(float* __restrict__ y, int32_t* __restrict__ acc_out,
+                                                       const float* __restrict__ s_a, const float* __restrict__ s_w,
+                                                       int M, int N) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)M * N) return;
+  const int m = (int)(i / N), n = (int)(i % N);
+  const int a = reinterpret_cast<const int32_t*>(y)[i];
+  if (acc_out) acc_out[i] = a;
+  const float t = (float)a * s_a[m];
+  y[i] = t * s_w[n];
+}
+
 template <int BM, int BN, int BK, int WM, int WN, int RING, int OCC>
 void launch(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc, int M,
-            int N, int K, hipStream_t st) {
+            int N, int K, hipStream_t st, int splits = 1) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  gemm_dma_kernel<BM, BN, BK, WM, WN, RING, OCC>
-      <<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, 0, st>>>(q, s_a, w, s_w, y, acc, M, N, K, tiles_m, tiles_n);
+  const int64_t total = (int64_t)M * N;
+  if (splits > 1)
+    zero_kernel<<<(unsigned)((total + 1023) / 1024), 256, 0, st>>>(reinterpret_cast<int32_t*>(y), total);
+  gemm_dma_kernel<BM, BN, BK, WM, WN, RING, OCC><<<(unsigned)(tiles_m * tiles_n * splits), 64 * WM * WN, 0, st>>>(
+      q, s_a, w, s_w, y, acc, M, N, K, tiles_m, tiles_n, splits);
+  if (splits > 1) finalize_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(y, acc, s_a, s_w, M, N);
 }
 
 }  // namespace dma

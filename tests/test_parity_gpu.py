@@ -210,3 +210,18 @@ def test_invalid_shapes_raise_before_launch():
         prism.gemm_w8a8(q, torch.ones(4, device=DEV), torch.zeros((8, 40), dtype=torch.int8, device=DEV),
                         torch.ones(8, device=DEV))
     assert e.value.status == -2
+
+
+@pytest.mark.parametrize("M,N,K", [(65, 130, 2064), (200, 300, 4096), (129, 257, 4112), (100, 2560, 9728)])
+def test_w8a8_split_k(M, N, K):
+    """Few output tiles and a long K: the tiled path splits K over several
+    workgroups whose exact int32 partial tiles are added atomically."""
+    c, q, s_a = _case(7, M, N, K, "w8a8")
+    y_ref, acc_ref = oracle.gemm_w8a8(q, s_a, c["w"], c["s_w"])
+    acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    y = prism.gemm_w8a8(dev(q), dev(s_a), dev(c["w"]), dev(c["s_w"]), acc=acc)
+    y2 = prism.gemm_w8a8(dev(q), dev(s_a), dev(c["w"]), dev(c["s_w"]))
+    torch.cuda.synchronize()
+    assert_same_ints(host(acc), acc_ref, "acc")
+    assert_same_floats(host(y), y_ref, "y")
+    assert_same_floats(host(y2), y_ref, "y without acc")

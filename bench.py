@@ -211,7 +211,9 @@ def headline(torch, prism, wl, args):
 # --------------------------------------------------------------- other kernels
 
 def _time_launches(torch, fns, reps):
-    """Average duration (s) of launches cycled from fns, each bracketed by events."""
+    """(single, stream): average duration (s) of launches cycled from fns when each
+    is bracketed by its own pair of events, and when `reps` launches run back to
+    back between one pair of events (a decode loop's view; no event overhead)."""
     E = torch.cuda.Event
     pairs = [(E(enable_timing=True), E(enable_timing=True)) for _ in range(reps)]
     s = torch.cuda.current_stream()
@@ -223,7 +225,14 @@ def _time_launches(torch, fns, reps):
         _check(fns[i % len(fns)]())
         pairs[i][1].record(s)
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in pairs) / reps / 1e3
+    single = sum(a.elapsed_time(b) for a, b in pairs) / reps / 1e3
+    a, b = E(enable_timing=True), E(enable_timing=True)
+    a.record(s)
+    for i in range(reps):
+        _check(fns[i % len(fns)]())
+    b.record(s)
+    torch.cuda.synchronize()
+    return single, a.elapsed_time(b) / reps / 1e3
 
 
 def kernels(torch, prism, wl, only=None):
@@ -247,10 +256,11 @@ def kernels(torch, prism, wl, only=None):
             sa = torch.empty((M,), dtype=torch.float32, device=dev)
             _check(L.quantize(x, q, sa)())
             y = torch.empty((M, N), dtype=torch.float32, device=dev)
-            t = _time_launches(torch, [L.w4a8(q, sa, w, sw, y) for w in ws], 100)
+            t1, t = _time_launches(torch, [L.w4a8(q, sa, w, sw, y) for w in ws], 100)
             nbytes = N * K // 2 + 4 * N + M * K + 4 * M + 4 * M * N
             out["w4a8_m%d" % M] = dict(us=t * 1e6, gbs=nbytes / t / 1e9, hbm_frac=nbytes / t / 1e9 / PEAK_HBM_GBS,
-                                       tops=2 * M * N * K / t / 1e12, algorithmic_bytes=nbytes, copies=R)
+                                       tops=2 * M * N * K / t / 1e12, us_single_launch=t1 * 1e6,
+                                       algorithmic_bytes=nbytes, copies=R)
         del ws
     if only in (None, "block"):
         c = wl.block()
@@ -263,13 +273,14 @@ def kernels(torch, prism, wl, only=None):
         sa = torch.empty((M,), dtype=torch.float32, device=dev)
         _check(L.quantize(x, q, sa)())
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
-        t = _time_launches(torch, [L.block(q, sa, w, d, y) for w, d in ws], 10)
+        t1, t = _time_launches(torch, [L.block(q, sa, w, d, y) for w, d in ws], 10)
         ops = 2 * M * N * K
         # fp32 VALU bound of the block epilogue: one convert and one fma per 32-k partial,
         # 256 CUs x 64 lanes x 2.4 GHz lane-operations per second
         valu_s = M * N * (K // 32) * 2 / (256 * 64 * 2.4e9)
         out["block_scale_m2048"] = dict(us=t * 1e6, tops=ops / t / 1e12, mfma_frac=ops / t / 1e12 / PEAK_INT8_TOPS,
-                                        valu_bound_us=valu_s * 1e6, valu_frac=valu_s / t, copies=R)
+                                        valu_bound_us=valu_s * 1e6, valu_frac=valu_s / t, us_single_launch=t1 * 1e6,
+                                        copies=R)
         del ws
     if only in (None, "stress"):
         st = wl.stress()
@@ -280,14 +291,14 @@ def kernels(torch, prism, wl, only=None):
             x = T(xa)
             q = torch.empty((M, K), dtype=torch.int8, device=dev)
             sa = torch.empty((M,), dtype=torch.float32, device=dev)
-            tq = _time_launches(torch, [L.quantize(x, q, sa)], 20)
+            _, tq = _time_launches(torch, [L.quantize(x, q, sa)], 20)
             y = torch.empty((M, N), dtype=torch.float32, device=dev)
-            t = _time_launches(torch, [L.w8a8(q, sa, w, sw, y)], 20 if M > 1 else 100)
+            t1, t = _time_launches(torch, [L.w8a8(q, sa, w, sw, y)], 20 if M > 1 else 100)
             nbytes = N * K + 4 * N + M * K + 4 * M + 4 * M * N
             out["stress_m%d" % M] = dict(us=t * 1e6, tops=2 * M * N * K / t / 1e12,
                                          mfma_frac=2 * M * N * K / t / 1e12 / PEAK_INT8_TOPS,
                                          gbs=nbytes / t / 1e9, hbm_frac=nbytes / t / 1e9 / PEAK_HBM_GBS,
-                                         quantize_us=tq * 1e6,
+                                         quantize_us=tq * 1e6, us_single_launch=t1 * 1e6,
                                          quantize_gbs=(5 * M * K + 4 * M) / tq / 1e9)
     return out
 

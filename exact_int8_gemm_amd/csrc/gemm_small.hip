@@ -5,16 +5,21 @@
 // grouping of the k-range gives the same accumulator.  At small M the weights
 // dominate the bytes, so this kernel is built to stream them from HBM:
 //
-//  * one workgroup owns 16 output columns and all M rows; its WAVES waves
-//    split K into contiguous ranges and reduce their int32 partials in LDS;
-//  * weights go from HBM straight into MFMA operand registers with 16-byte
-//    loads (no LDS staging: each weight byte is used by one wave only), four
-//    128-k units at a time so that many loads are in flight per wave;
+//  * one workgroup owns 16 * CB output columns and all M rows; its WAVES
+//    waves split K into contiguous ranges of 128-k units and reduce their
+//    int32 partials in LDS;
+//  * each wave issues all loads of a batch of U units at once (weights for
+//    its CB column blocks and activation fragments for its MB row blocks)
+//    before any MFMA, as branch-free buffer loads that read zeros outside the
+//    matrices, so the weight stream is in flight from the first cycles;
+//  * weights go from HBM straight into MFMA operand registers (no LDS: each
+//    weight byte is used by one wave only); an activation fragment is used by
+//    CB column blocks;
 //  * v_mfma_i32_16x16x64_i8: lane l holds column (l % 16) of the weights and
-//    row (l % 16) of the activations, k-group l / 16.  Both operands use the
-//    same lane -> k assignment, so the integer sum is the plain dot product
-//    whatever that assignment is.  Lane group g covers k = unit*128 + 32g +
-//    [0, 16) in the first MFMA of a unit and + [16, 32) in the second;
+//    row (l % 16) of the activations, k-group g = l / 16.  Both operands use
+//    the same lane -> k assignment, so the integer sum is the plain dot
+//    product whatever that assignment is.  In unit u, group g covers
+//    k = 128 u + 32 g + [0, 16) in the first MFMA and + [16, 32) in the second;
 //  * 4-bit weights are unpacked in registers: each nibble is moved to the top
 //    half of a byte, which as int8 equals 16 * w, so the MFMA sums 16 * acc
 //    exactly (|16 * acc| < 2^31 for K <= 131040) and an arithmetic shift by 4
@@ -27,9 +32,16 @@ namespace prism {
 namespace {
 
 constexpr int kUnitK = 128;
-constexpr int kUnroll = 4;
+constexpr uint32_t kOutOfRange = 0x80000000u;
 
-__device__ inline v4i load16(const int8_t* p) { return *reinterpret_cast<const v4i*>(p); }
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < (int64_t)kOutOfRange - 1 ? bytes : (int64_t)kOutOfRange - 1;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
+
+__device__ inline v4i bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
 
 // 16 packed bytes = 32 nibbles, k ascending, low nibble first ->
 // two 16-byte fragments of int8 (16 * w) in k order.
@@ -48,7 +60,7 @@ __device__ inline void unpack_w4(const v4i p, v4i& lo, v4i& hi) {
   hi = v4i{o[4], o[5], o[6], o[7]};
 }
 
-template <int MB, bool W4, int WAVES>
+template <int MB, int CB, bool W4, int WAVES, int U>
 __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(const int8_t* __restrict__ q,
                                                                 const float* __restrict__ s_a,
                                                                 const int8_t* __restrict__ w,
@@ -56,115 +68,143 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(const int8_t* __
                                                                 float* __restrict__ y,
                                                                 int32_t* __restrict__ acc_out, int M, int N,
                                                                 int K) {
-  __shared__ int red[WAVES][MB * 4][64];
+  __shared__ int red[WAVES][CB * MB * 4][64];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15;
   const int g = lane >> 4;
-  const int n0 = blockIdx.x * 16;
-  const int n = n0 + col;
-  const bool nvalid = n < N;
+  const int n0 = blockIdx.x * 16 * CB;
 
   const int nunits = (K + kUnitK - 1) / kUnitK;
   const int ub = (int)((int64_t)wave * nunits / WAVES);
   const int ue = (int)((int64_t)(wave + 1) * nunits / WAVES);
 
-  v4i acc[MB];
+  // Weight rows n0 .. N-1 and activation rows 0 .. M-1; rows outside read zeros.
+  const int64_t wrow = W4 ? K / 2 : K;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + (size_t)n0 * (size_t)wrow, (int64_t)(N - n0) * wrow);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q, (int64_t)M * K);
+  uint32_t wbase[CB], qbase[MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = v4i{0, 0, 0, 0};
-
-  const int8_t* wrow = w + (W4 ? (size_t)n * (size_t)(K / 2) : (size_t)n * (size_t)K);
-
-  for (int u0 = ub; u0 < ue; u0 += kUnroll) {
-    v4i b0[kUnroll], b1[kUnroll];
+  for (int cb = 0; cb < CB; ++cb)
+    wbase[cb] = (n0 + cb * 16 + col < N) ? (uint32_t)((cb * 16 + col) * wrow) : kOutOfRange;
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
+  for (int mb = 0; mb < MB; ++mb) qbase[mb] = (mb * 16 + col < M) ? (uint32_t)((mb * 16 + col) * K) : kOutOfRange;
+
+  v4i acc[CB][MB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[cb][mb] = v4i{0, 0, 0, 0};
+
+  for (int u0 = ub; u0 < ue; u0 += U) {
+    // All loads of the batch first.
+    v4i wl[CB][U][W4 ? 1 : 2];
+    v4i al[MB][U][2];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
       const int kk = (u0 + j) * kUnitK + g * 32;
-      b0[j] = v4i{0, 0, 0, 0};
-      b1[j] = v4i{0, 0, 0, 0};
-      if (u0 + j < ue && nvalid) {
+      const bool in = (u0 + j < ue) && kk < K;  // K % 32 == 0 (4-bit) keeps a 32-k group whole
+      const bool in2 = (u0 + j < ue) && kk + 16 < K;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
         if (W4) {
-          if (kk < K) unpack_w4(load16(wrow + kk / 2), b0[j], b1[j]);
+          wl[cb][j][0] = bload(rw, in ? wbase[cb] + (uint32_t)(kk / 2) : kOutOfRange);
         } else {
-          if (kk < K) b0[j] = load16(wrow + kk);
-          if (kk + 16 < K) b1[j] = load16(wrow + kk + 16);
+          wl[cb][j][0] = bload(rw, in ? wbase[cb] + (uint32_t)kk : kOutOfRange);
+          wl[cb][j][W4 ? 0 : 1] = bload(rw, in2 ? wbase[cb] + (uint32_t)(kk + 16) : kOutOfRange);
         }
       }
-    }
-#pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
-      if (u0 + j >= ue) break;  // uniform over the wave
-      const int kk = (u0 + j) * kUnitK + g * 32;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const int m = mb * 16 + col;
-        v4i a0 = v4i{0, 0, 0, 0}, a1 = v4i{0, 0, 0, 0};
-        if (m < M) {
-          const int8_t* qr = q + (size_t)m * (size_t)K;
-          if (kk < K) a0 = load16(qr + kk);
-          if (kk + 16 < K) a1 = load16(qr + kk + 16);
+        al[mb][j][0] = bload(rq, in ? qbase[mb] + (uint32_t)kk : kOutOfRange);
+        al[mb][j][1] = bload(rq, in2 ? qbase[mb] + (uint32_t)(kk + 16) : kOutOfRange);
+      }
+    }
+    // Keep every load of the batch ahead of the first MFMA (the scheduler
+    // would otherwise pair each load with its use and wait on it).
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        v4i b0, b1;
+        if (W4) {
+          unpack_w4(wl[cb][j][0], b0, b1);
+        } else {
+          b0 = wl[cb][j][0];
+          b1 = wl[cb][j][W4 ? 0 : 1];
         }
-        acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0[j], acc[mb], 0, 0, 0);
-        acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1[j], acc[mb], 0, 0, 0);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          acc[cb][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(al[mb][j][0], b0, acc[cb][mb], 0, 0, 0);
+          acc[cb][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(al[mb][j][1], b1, acc[cb][mb], 0, 0, 0);
+        }
       }
     }
   }
 
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[wave][mb * 4 + i][lane] = acc[mb][i];
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][(cb * MB + mb) * 4 + i][lane] = acc[cb][mb][i];
   __syncthreads();
 
   // Output layout of the 16x16 MFMA: lane l, register i -> row 4 * (l / 16) + i,
   // column l % 16.
-  for (int e = threadIdx.x; e < MB * 4 * 64; e += 64 * WAVES) {
-    const int mbi = e >> 6;
+  for (int e = threadIdx.x; e < CB * MB * 4 * 64; e += 64 * WAVES) {
+    const int idx = e >> 6;
     const int l = e & 63;
     int s = 0;
 #pragma unroll
-    for (int wv = 0; wv < WAVES; ++wv) s += red[wv][mbi][l];
+    for (int wv = 0; wv < WAVES; ++wv) s += red[wv][idx][l];
     if (W4) s >>= 4;  // exact: the sum is a multiple of 16
-    const int m = (mbi >> 2) * 16 + (l >> 4) * 4 + (mbi & 3);
-    const int nn = n0 + (l & 15);
-    if (m < M && nn < N) {
-      const size_t o = (size_t)m * (size_t)N + (size_t)nn;
+    const int cb = idx / (MB * 4), mb = (idx / 4) % MB, i = idx % 4;
+    const int m = mb * 16 + (l >> 4) * 4 + i;
+    const int n = n0 + cb * 16 + (l & 15);
+    if (m < M && n < N) {
+      const size_t o = (size_t)m * (size_t)N + (size_t)n;
       if (acc_out) acc_out[o] = s;
       const float t = (float)s * s_a[m];
-      y[o] = t * s_w[nn];
+      y[o] = t * s_w[n];
     }
   }
 }
 
-template <int MB, bool W4, int WAVES>
-void launch_small(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y,
-                  int32_t* acc, int M, int N, int K, hipStream_t st) {
-  const unsigned grid = (unsigned)((N + 15) / 16);
-  gemm_small_kernel<MB, W4, WAVES><<<grid, 64 * WAVES, 0, st>>>(q, s_a, w, s_w, y, acc, M, N, K);
+template <int MB, int CB, bool W4, int WAVES>
+void launch_small(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc,
+                  int M, int N, int K, hipStream_t st) {
+  constexpr int U = MB >= 4 ? 2 : 4;  // units per batch: keeps the batch's registers under ~100 VGPRs
+  const unsigned grid = (unsigned)((N + 16 * CB - 1) / (16 * CB));
+  gemm_small_kernel<MB, CB, W4, WAVES, U><<<grid, 64 * WAVES, 0, st>>>(q, s_a, w, s_w, y, acc, M, N, K);
+}
+
+template <int MB, int CB, bool W4>
+void pick_waves(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc,
+                int M, int N, int K, hipStream_t st) {
+  // About four 128-k units per wave, between 4 and 16 waves per workgroup.
+  const int64_t nunits = (K + kUnitK - 1) / kUnitK;
+  if (nunits >= 64) launch_small<MB, CB, W4, 16>(q, s_a, w, s_w, y, acc, M, N, K, st);
+  else if (nunits >= 24) launch_small<MB, CB, W4, 8>(q, s_a, w, s_w, y, acc, M, N, K, st);
+  else launch_small<MB, CB, W4, 4>(q, s_a, w, s_w, y, acc, M, N, K, st);
 }
 
 template <int MB, bool W4>
-void pick_waves(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc,
-                int M, int N, int K, hipStream_t st) {
-  // Aim for about 16 waves per CU over the 256 CUs, without giving a wave
-  // less than two 128-k units.
-  const int64_t nwg = (N + 15) / 16;
-  const int64_t nunits = (K + kUnitK - 1) / kUnitK;
-  int waves = 4;
-  if (nwg * 8 <= 4096 && nunits >= 16) waves = 8;
-  if (nwg * 16 <= 4096 && nunits >= 32) waves = 16;
-  if (waves == 16) launch_small<MB, W4, 16>(q, s_a, w, s_w, y, acc, M, N, K, st);
-  else if (waves == 8) launch_small<MB, W4, 8>(q, s_a, w, s_w, y, acc, M, N, K, st);
-  else launch_small<MB, W4, 4>(q, s_a, w, s_w, y, acc, M, N, K, st);
+void pick_cb(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc, int M,
+             int N, int K, hipStream_t st) {
+  // Two column blocks per workgroup when that still leaves one workgroup per CU.
+  if ((N + 31) / 32 >= 256) pick_waves<MB, 2, W4>(q, s_a, w, s_w, y, acc, M, N, K, st);
+  else pick_waves<MB, 1, W4>(q, s_a, w, s_w, y, acc, M, N, K, st);
 }
 
 template <bool W4>
-void pick_mb(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc,
-             int M, int N, int K, hipStream_t st) {
-  if (M <= 16) pick_waves<1, W4>(q, s_a, w, s_w, y, acc, M, N, K, st);
-  else if (M <= 32) pick_waves<2, W4>(q, s_a, w, s_w, y, acc, M, N, K, st);
-  else pick_waves<4, W4>(q, s_a, w, s_w, y, acc, M, N, K, st);
+void pick_mb(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc, int M,
+             int N, int K, hipStream_t st) {
+  if (M <= 16) pick_cb<1, W4>(q, s_a, w, s_w, y, acc, M, N, K, st);
+  else if (M <= 32) pick_cb<2, W4>(q, s_a, w, s_w, y, acc, M, N, K, st);
+  else pick_cb<4, W4>(q, s_a, w, s_w, y, acc, M, N, K, st);
 }
 
 }  // namespace

@@ -8,7 +8,6 @@
 namespace prism {
 namespace {
 
-using tiled::launch_blockscale;
 using tiled::launch_tiled;
 
 inline int64_t tiles(int64_t M, int64_t N, int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
@@ -57,9 +56,13 @@ int launch_gemm_tiled(const int8_t* q, const float* s_a, const void* w, bool w_i
   return launch_status();
 }
 
+// Block scales: direct-to-LDS pipeline with the scales riding along in each
+// stage; 128 x 128 tiles of 4 waves, two workgroups per CU (the fp32 block
+// combine is VALU-bound, so a second workgroup keeps the VALU busy while the
+// first one waits).
 int launch_gemm_blockscale(const int8_t* q, const float* s_a, const int8_t* w, const uint16_t* d, float* y,
                            int32_t* partials, int M, int N, int K, hipStream_t st) {
-  launch_blockscale<128, 128, 64, 2, 2, 2>(q, s_a, w, d, y, partials, M, N, K, st);
+  tiled::dma::launch_block<128, 128, 2, 2, 2, 2>(q, s_a, w, d, y, partials, M, N, K, st);
   return launch_status();
 }
 

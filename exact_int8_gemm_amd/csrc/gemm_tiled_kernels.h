@@ -89,6 +89,8 @@ __device__ inline void tile_of_split(int tiles_m, int tiles_n, int splits, int& 
   tn = in / gm;
 }
 
+__device__ inline float half_bits_to_float(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
 // Byte offset that a buffer access treats as out of range: loads return 0.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
@@ -273,7 +275,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_tiled_kernel(const int
   ad.init(q, w, m0, n0, M, N, K);
   Stage<BM, BN, BK, G::kNT, W4> s0, s1;
   const int nk = (K + BK - 1) / BK;
-  auto mma = [&](int buf) { mma_stage<BM, BN, BK, WM, WN>(lds[buf], wm, wn, lane, acc); };
+  auto mma = [&](int buf) __attribute__((always_inline)) { mma_stage<BM, BN, BK, WM, WN>(lds[buf], wm, wn, lane, acc); };
 
   // Pipeline: stage k is in LDS buffer k % 2, stage k+1 waits in a register
   // set, stage k+2 is being loaded into the other set.  The stage count is
@@ -325,113 +327,6 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_tiled_kernel(const int
   }
 }
 
-__device__ inline float half_bits_to_float(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
-
-// Block-scale W8A8: each 32-k block of a stage is one MFMA started from zero;
-// its exact int32 result is folded into fp32 accumulators in ascending block
-// order with one fused multiply-add per element.
-template <int BM, int BN, int BK, int WM, int WN, int OCC>
-__global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_blockscale_kernel(
-    const int8_t* __restrict__ q, const float* __restrict__ s_a, const int8_t* __restrict__ w,
-    const uint16_t* __restrict__ d, float* __restrict__ y, int32_t* __restrict__ partials, int M, int N, int K,
-    int tiles_m, int tiles_n) {
-  using G = Geometry<BM, BN, BK, WM, WN>;
-  constexpr int KS = BK / 32;  // 32-k blocks per stage
-  __shared__ __attribute__((aligned(16))) int8_t lds[2][G::kLds];
-
-  int tm, tn;
-  tile_of(tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  const int rl = lane & 31, kg = (lane >> 5) * 16;
-  const int NB = K / 32;
-
-  float f[G::kTM][G::kTN][16];
-#pragma unroll
-  for (int i = 0; i < G::kTM; ++i)
-#pragma unroll
-    for (int j = 0; j < G::kTN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) f[i][j][r] = 0.0f;
-
-  int ncol[G::kTN];
-#pragma unroll
-  for (int j = 0; j < G::kTN; ++j) ncol[j] = n0 + wn * G::kWTN + j * 32 + rl;
-
-  auto stage = [&](const int8_t* buf, int kt) {
-    float dv[G::kTN][KS];
-#pragma unroll
-    for (int j = 0; j < G::kTN; ++j)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int b = kt * KS + ks;
-        dv[j][ks] = (ncol[j] < N && b < NB) ? half_bits_to_float(d[(size_t)ncol[j] * (size_t)NB + b]) : 0.0f;
-      }
-    const int8_t* sa = buf + (wm * G::kWTM + rl) * G::kSA + kg;
-    const int8_t* sb = buf + (BM + wn * G::kWTN + rl) * G::kSA + kg;
-    const v16i zero = v16i{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int b = kt * KS + ks;
-      if (b >= NB) break;  // uniform over the workgroup
-      v4i af[G::kTM], bf[G::kTN];
-#pragma unroll
-      for (int i = 0; i < G::kTM; ++i) af[i] = *reinterpret_cast<const v4i*>(sa + i * 32 * G::kSA + ks * 32);
-#pragma unroll
-      for (int j = 0; j < G::kTN; ++j) bf[j] = *reinterpret_cast<const v4i*>(sb + j * 32 * G::kSA + ks * 32);
-#pragma unroll
-      for (int i = 0; i < G::kTM; ++i)
-#pragma unroll
-        for (int j = 0; j < G::kTN; ++j) {
-          const v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], zero, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) f[i][j][r] = __builtin_fmaf((float)p[r], dv[j][ks], f[i][j][r]);
-          if (partials) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int m = m0 + wm * G::kWTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-              if (m < M && ncol[j] < N)
-                partials[((size_t)m * (size_t)N + (size_t)ncol[j]) * (size_t)NB + b] = p[r];
-            }
-          }
-        }
-    }
-  };
-
-  StageAddr<BM, BN, BK, G::kNT, false> ad;
-  ad.init(q, w, m0, n0, M, N, K);
-  Stage<BM, BN, BK, G::kNT, false> s0, s1;
-  const int nk = (K + BK - 1) / BK;
-  ad.load(s0, 0, K);
-  ad.load(s1, BK, K);
-  ad.store(s0, lds[0]);
-  __syncthreads();
-  for (int k = 0; k < nk; k += 2) {  // stages past K are skipped inside stage()
-    ad.load(s0, (k + 2) * BK, K);
-    stage(lds[0], k);
-    ad.store(s1, lds[1]);
-    __syncthreads();
-    ad.load(s1, (k + 3) * BK, K);
-    stage(lds[1], k + 1);
-    ad.store(s0, lds[0]);
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int j = 0; j < G::kTN; ++j) {
-    if (ncol[j] >= N) continue;
-#pragma unroll
-    for (int i = 0; i < G::kTM; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * G::kWTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (m < M) y[(size_t)m * (size_t)N + (size_t)ncol[j]] = f[i][j][r] * s_a[m];
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Direct-to-LDS pipeline (int8 weights).
 //
@@ -475,6 +370,18 @@ __device__ inline void copy_to_lds(const v4i rsrc, uint32_t lds_addr, uint32_t v
   const v4i r = v4i{__builtin_amdgcn_readfirstlane(rsrc[0]), __builtin_amdgcn_readfirstlane(rsrc[1]),
                     __builtin_amdgcn_readfirstlane(rsrc[2]), __builtin_amdgcn_readfirstlane(rsrc[3])};
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(r)
+               : "memory");
+}
+
+// The same for 2-byte elements: lane i's value lands zero-extended in the
+// dword at lds_addr + 4 * lane.
+__device__ inline void copy2_to_lds(const v4i rsrc, uint32_t lds_addr, uint32_t voff) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+  const v4i r = v4i{__builtin_amdgcn_readfirstlane(rsrc[0]), __builtin_amdgcn_readfirstlane(rsrc[1]),
+                    __builtin_amdgcn_readfirstlane(rsrc[2]), __builtin_amdgcn_readfirstlane(rsrc[3])};
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ushort %1, %2, 0 offen lds"
                :
                : "s"(m0v), "v"(voff), "s"(r)
                : "memory");
@@ -563,7 +470,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(const int8_
     const bool valid = isA ? (m0 + row < M) : (n0 + row < N);
     off[s] = valid ? (uint32_t)(row * K + chunk * 16) : kOutOfRange;
   }
-  auto issue = [&](int8_t* base, int stage) {
+  auto issue = [&](int8_t* base, int stage) __attribute__((always_inline)) {
     const int k0 = stage * BK;
 #pragma unroll
     for (int s = 0; s < C::kPerWave; ++s) {
@@ -590,9 +497,9 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(const int8_
   const int brow = (BM + wn * C::kWTN + rl) * BK;
   constexpr int KS = BK / 32;
 
-  auto compute = [&](const int8_t* buf) {
+  auto compute = [&](const int8_t* buf) __attribute__((always_inline)) {
     v4i af[2][C::kTM], bf[2][C::kTN];
-    auto read = [&](int ks, int slot) {
+    auto read = [&](int ks, int slot) __attribute__((always_inline)) {
       const int c = ((2 * ks + (lane >> 5)) ^ sw) * 16;
 #pragma unroll
       for (int i = 0; i < C::kTM; ++i) af[slot][i] = *reinterpret_cast<const v4i*>(buf + arow + i * 32 * BK + c);
@@ -612,7 +519,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(const int8_
   };
   // One pipeline step: stage `stage` sits in `cur`; the copies of stage
   // stage + RING - 1 go into `nxt` (the buffer of stage - 1).
-  auto step = [&](const int8_t* cur, int8_t* nxt, int stage) {
+  auto step = [&](const int8_t* cur, int8_t* nxt, int stage) __attribute__((always_inline)) {
     wait_vmcnt<(RING - 2) * C::kPerWave>();
     __syncthreads();
     issue(nxt, stage + RING - 1);
@@ -716,6 +623,201 @@ void launch(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w
   if (splits > 1) finalize_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(y, acc, s_a, s_w, M, N);
 }
 
+// Block-scale W8A8 on the direct-to-LDS pipeline.  Each stage also carries
+// the fp16 block scales of its BK / 32 blocks for the tile's BN columns: a
+// 2-byte copy writes lane i's value zero-extended into the dword at LDS base
+// + 4 i, so one wave-wide copy moves one block's scales for 64 columns, and
+// block ks of column c sits at dword ks * BN + c of the stage's scale area.
+// Per 32-k block, each 32x32 tile is one MFMA started from zero; its exact
+// int32 result is folded into fp32 accumulators in ascending block order:
+// f = fmaf((float)P_b, (float)d[n][b], f); at the end y = f * s_a[m].
+template <int BM, int BN, int WM, int WN, int RING, int OCC, bool PARTIALS>
+__global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_block_kernel(const int8_t* __restrict__ q,
+                                                                       const float* __restrict__ s_a,
+                                                                       const int8_t* __restrict__ w,
+                                                                       const uint16_t* __restrict__ d,
+                                                                       float* __restrict__ y,
+                                                                       int32_t* __restrict__ partials, int M, int N,
+                                                                       int K, int tiles_m, int tiles_n) {
+  constexpr int BK = 128;
+  constexpr int KS = BK / 32;  // blocks per stage
+  using C = Cfg<BM, BN, BK, WM, WN, RING>;
+  constexpr int kDCopies = KS * BN / 64;
+  constexpr int kPerWaveD = kDCopies / C::kNW;
+  static_assert(kDCopies % C::kNW == 0, "scale copies must divide among waves");
+  constexpr int kPerWave = C::kPerWave + kPerWaveD;
+  constexpr int kDOff = (BM + BN) * BK;          // scale area within a stage
+  constexpr int kStage = kDOff + KS * BN * 4;
+  static_assert(RING * kStage <= 160 * 1024, "LDS ring exceeds 160 KiB");
+  static_assert((RING - 2) * kPerWave < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) int8_t lds0[kStage];
+  __shared__ __attribute__((aligned(1024))) int8_t lds1[kStage];
+  __shared__ __attribute__((aligned(1024))) int8_t lds2[RING > 2 ? kStage : 16];
+  __shared__ __attribute__((aligned(1024))) int8_t lds3[RING > 3 ? kStage : 16];
+
+  int tm, tn;
+  tile_of(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int NB = K / 32;
+
+  const v4i ra = rsrc_words(q + (size_t)m0 * (size_t)K, (int64_t)(M - m0) * K);
+  const v4i rb = rsrc_words(w + (size_t)n0 * (size_t)K, (int64_t)(N - n0) * K);
+  const v4i rd = rsrc_words(d + (size_t)n0 * (size_t)NB, (int64_t)(N - n0) * NB * 2);
+  uint32_t off[C::kPerWave];
+  int kc[C::kPerWave];
+#pragma unroll
+  for (int s = 0; s < C::kPerWave; ++s) {
+    const bool isA = s < C::kPerWaveA;
+    const int copy = isA ? wave * C::kPerWaveA + s : wave * C::kPerWaveB + (s - C::kPerWaveA);
+    const int row = copy * C::kRowsPerCopy + lane / C::kChunks;
+    const int chunk = (lane % C::kChunks) ^ C::swz(row);
+    kc[s] = chunk * 16;
+    const bool valid = isA ? (m0 + row < M) : (n0 + row < N);
+    off[s] = valid ? (uint32_t)(row * K + chunk * 16) : kOutOfRange;
+  }
+  // Scale copies of this wave: copy c holds block c / (BN / 64) of columns
+  // (c % (BN / 64)) * 64 + lane.
+  uint32_t doff[kPerWaveD > 0 ? kPerWaveD : 1];
+  int dks[kPerWaveD > 0 ? kPerWaveD : 1];
+#pragma unroll
+  for (int s = 0; s < kPerWaveD; ++s) {
+    const int c = wave * kPerWaveD + s;
+    const int col = (c % (BN / 64)) * 64 + lane;
+    dks[s] = c / (BN / 64);
+    doff[s] = (n0 + col < N) ? (uint32_t)(col * NB * 2) : kOutOfRange;
+  }
+  auto issue = [&](int8_t* base, int stage) __attribute__((always_inline)) {
+    const int k0 = stage * BK;
+#pragma unroll
+    for (int s = 0; s < C::kPerWave; ++s) {
+      const bool isA = s < C::kPerWaveA;
+      const int copy = isA ? wave * C::kPerWaveA + s : wave * C::kPerWaveB + (s - C::kPerWaveA);
+      const uint32_t o = (k0 + kc[s] < K) ? off[s] + (uint32_t)k0 : kOutOfRange;
+      const int8_t* dst = base + (isA ? 0 : BM * BK) + copy * 1024;
+      copy_to_lds(isA ? ra : rb, lds_addr(dst), o);
+    }
+#pragma unroll
+    for (int s = 0; s < kPerWaveD; ++s) {
+      const int b = stage * KS + dks[s];
+      const uint32_t o = (b < NB) ? doff[s] + (uint32_t)(b * 2) : kOutOfRange;
+      const int8_t* dst = base + kDOff + (wave * kPerWaveD + s) * 256;
+      copy2_to_lds(rd, lds_addr(dst), o);
+    }
+  };
+
+  float f[C::kTM][C::kTN][16];
+#pragma unroll
+  for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::kTN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) f[i][j][r] = 0.0f;
+
+  const int rl = lane & 31;
+  const int sw = C::swz(rl);
+  const int arow = (wm * C::kWTM + rl) * BK;
+  const int brow = (BM + wn * C::kWTN + rl) * BK;
+  int ncol[C::kTN];
+#pragma unroll
+  for (int j = 0; j < C::kTN; ++j) ncol[j] = wn * C::kWTN + j * 32 + rl;
+
+  auto compute = [&](const int8_t* buf, int stage) __attribute__((always_inline)) {
+    const v16i zero = v16i{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      // Blocks past K (padding of the last stage and of the ring) read zero
+      // operands and zero scales: fmaf(0, 0, f) returns f unchanged (f starts
+      // at +0 and can never become -0), so they need no branch.
+      const int b = stage * KS + ks;
+      const int c = ((2 * ks + (lane >> 5)) ^ sw) * 16;
+      v4i af[C::kTM], bf[C::kTN];
+      float dv[C::kTN];
+#pragma unroll
+      for (int i = 0; i < C::kTM; ++i) af[i] = *reinterpret_cast<const v4i*>(buf + arow + i * 32 * BK + c);
+#pragma unroll
+      for (int j = 0; j < C::kTN; ++j) {
+        bf[j] = *reinterpret_cast<const v4i*>(buf + brow + j * 32 * BK + c);
+        const uint32_t hbits = *reinterpret_cast<const uint32_t*>(buf + kDOff + (ks * BN + ncol[j]) * 4);
+        dv[j] = half_bits_to_float((uint16_t)hbits);
+      }
+#pragma unroll
+      for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kTN; ++j) {
+          const v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], zero, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) f[i][j][r] = __builtin_fmaf((float)p[r], dv[j], f[i][j][r]);
+          if constexpr (PARTIALS) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int m = m0 + wm * C::kWTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+              const int n = n0 + ncol[j];
+              if (m < M && n < N && b < NB) partials[((size_t)m * (size_t)N + (size_t)n) * (size_t)NB + b] = p[r];
+            }
+          }
+        }
+    }
+  };
+  auto step = [&](const int8_t* cur, int8_t* nxt, int stage) __attribute__((always_inline)) {
+    wait_vmcnt<(RING - 2) * kPerWave>();
+    __syncthreads();
+    issue(nxt, stage + RING - 1);
+    compute(cur, stage);
+  };
+
+  const int nk = (K + BK - 1) / BK;
+  const int nkr = (nk + RING - 1) / RING * RING;
+  issue(lds0, 0);
+  if constexpr (RING > 2) issue(lds1, 1);
+  if constexpr (RING > 3) issue(lds2, 2);
+  for (int k = 0; k < nkr; k += RING) {
+    if constexpr (RING == 2) {
+      step(lds0, lds1, k);
+      step(lds1, lds0, k + 1);
+    } else if constexpr (RING == 3) {
+      step(lds0, lds2, k);
+      step(lds1, lds0, k + 1);
+      step(lds2, lds1, k + 2);
+    } else {
+      step(lds0, lds3, k);
+      step(lds1, lds0, k + 1);
+      step(lds2, lds1, k + 2);
+      step(lds3, lds2, k + 3);
+    }
+  }
+  wait_vmcnt<0>();
+
+#pragma unroll
+  for (int j = 0; j < C::kTN; ++j) {
+    const int n = n0 + ncol[j];
+    if (n >= N) continue;
+#pragma unroll
+    for (int i = 0; i < C::kTM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * C::kWTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (m < M) y[(size_t)m * (size_t)N + (size_t)n] = f[i][j][r] * s_a[m];
+      }
+    }
+  }
+}
+
+// The partial-sum output (a debugging aid) is a separate instantiation, so
+// that the hot loop of the plain call carries no per-block stores.
+template <int BM, int BN, int WM, int WN, int RING, int OCC>
+void launch_block(const int8_t* q, const float* s_a, const int8_t* w, const uint16_t* d, float* y, int32_t* partials,
+                  int M, int N, int K, hipStream_t st) {
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  if (partials)
+    gemm_block_kernel<BM, BN, WM, WN, RING, OCC, true><<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, 0, st>>>(
+        q, s_a, w, d, y, partials, M, N, K, tiles_m, tiles_n);
+  else
+    gemm_block_kernel<BM, BN, WM, WN, RING, OCC, false><<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, 0, st>>>(
+        q, s_a, w, d, y, nullptr, M, N, K, tiles_m, tiles_n);
+}
+
 }  // namespace dma
 
 template <int BM, int BN, int BK, int WM, int WN, bool W4, int OCC>
@@ -724,14 +826,6 @@ void launch_tiled(const int8_t* q, const float* s_a, const int8_t* w, const floa
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   gemm_tiled_kernel<BM, BN, BK, WM, WN, W4, OCC>
       <<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, 0, st>>>(q, s_a, w, s_w, y, acc, M, N, K, tiles_m, tiles_n);
-}
-
-template <int BM, int BN, int BK, int WM, int WN, int OCC>
-void launch_blockscale(const int8_t* q, const float* s_a, const int8_t* w, const uint16_t* d, float* y,
-                       int32_t* partials, int M, int N, int K, hipStream_t st) {
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  gemm_blockscale_kernel<BM, BN, BK, WM, WN, OCC><<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, 0, st>>>(
-      q, s_a, w, d, y, partials, M, N, K, tiles_m, tiles_n);
 }
 
 }  // namespace tiled

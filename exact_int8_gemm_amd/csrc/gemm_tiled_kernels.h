@@ -593,22 +593,48 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(const int8_
 // turn the exact int32 sums into the per-channel fp32 epilogue afterwards,
 // in place, one element per thread.
 __global__ __launch_bounds__(256) void zero_kernel(int32_t* __restrict__ p, int64_t n) {
-  const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-#pragma unroll
-  for (int64_t i = i0; i < i0 + 4; ++i)
-    if (i < n) p[i] = 0;
+  // One 16-byte chunk per thread (p is 16-byte aligned); the last chunk may be partial.
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i + 4 <= n) {
+    *reinterpret_cast<v4i*>(p + i) = v4i{0, 0, 0, 0};
+  } else {
+    for (int64_t j = i; j < n; ++j) p[j] = 0;
+  }
 }
 
 __global__ __launch_bounds__(256) void finalize_kernel(float* __restrict__ y, int32_t* __restrict__ acc_out,
                                                        const float* __restrict__ s_a, const float* __restrict__ s_w,
                                                        int M, int N) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)M * N) return;
-  const int m = (int)(i / N), n = (int)(i % N);
-  const int a = reinterpret_cast<const int32_t*>(y)[i];
-  if (acc_out) acc_out[i] = a;
-  const float t = (float)a * s_a[m];
-  y[i] = t * s_w[n];
+  // Four consecutive elements per thread (16-byte aligned), which may run
+  // across the end of a row.
+  const int64_t total = (int64_t)M * N;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= total) return;
+  int m = (int)(i / N), n = (int)(i - (int64_t)m * N);
+  const int cnt = total - i < 4 ? (int)(total - i) : 4;
+  int a[4] = {0, 0, 0, 0};
+  float o[4];
+  if (cnt == 4) {
+    const v4i v = *reinterpret_cast<const v4i*>(reinterpret_cast<const int32_t*>(y) + i);
+    a[0] = v[0]; a[1] = v[1]; a[2] = v[2]; a[3] = v[3];
+  } else {
+    for (int e = 0; e < cnt; ++e) a[e] = reinterpret_cast<const int32_t*>(y)[i + e];
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float t = (float)a[e] * s_a[m];
+    o[e] = t * s_w[n];
+    if (++n == N) { n = 0; if (m + 1 < M) ++m; }
+  }
+  if (cnt == 4) {
+    if (acc_out) *reinterpret_cast<v4i*>(acc_out + i) = v4i{a[0], a[1], a[2], a[3]};
+    *reinterpret_cast<v4f*>(y + i) = v4f{o[0], o[1], o[2], o[3]};
+  } else {
+    for (int e = 0; e < cnt; ++e) {
+      if (acc_out) acc_out[i + e] = a[e];
+      y[i + e] = o[e];
+    }
+  }
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int RING, int OCC>
@@ -620,7 +646,7 @@ void launch(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w
     zero_kernel<<<(unsigned)((total + 1023) / 1024), 256, 0, st>>>(reinterpret_cast<int32_t*>(y), total);
   gemm_dma_kernel<BM, BN, BK, WM, WN, RING, OCC><<<(unsigned)(tiles_m * tiles_n * splits), 64 * WM * WN, 0, st>>>(
       q, s_a, w, s_w, y, acc, M, N, K, tiles_m, tiles_n, splits);
-  if (splits > 1) finalize_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(y, acc, s_a, s_w, M, N);
+  if (splits > 1) finalize_kernel<<<(unsigned)((total + 1023) / 1024), 256, 0, st>>>(y, acc, s_a, s_w, M, N);
 }
 
 // Block-scale W8A8 on the direct-to-LDS pipeline.  Each stage also carries
@@ -810,8 +836,11 @@ template <int BM, int BN, int WM, int WN, int RING, int OCC>
 void launch_block(const int8_t* q, const float* s_a, const int8_t* w, const uint16_t* d, float* y, int32_t* partials,
                   int M, int N, int K, hipStream_t st) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  // The variant that also stores every block partial keeps more values live
+  // (the partial tiles and their addresses); it is built for one workgroup
+  // per CU so that it has the register file to itself and does not spill.
   if (partials)
-    gemm_block_kernel<BM, BN, WM, WN, RING, OCC, true><<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, 0, st>>>(
+    gemm_block_kernel<BM, BN, WM, WN, RING, 1, true><<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, 0, st>>>(
         q, s_a, w, d, y, partials, M, N, K, tiles_m, tiles_n);
   else
     gemm_block_kernel<BM, BN, WM, WN, RING, OCC, false><<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, 0, st>>>(

@@ -9,6 +9,7 @@ namespace prism {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 // Rows up to this count take the split-K small-M kernels; more rows take the
 // LDS-tiled kernels.  Either choice gives the same bits (exact int32 sums and

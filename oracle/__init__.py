@@ -54,6 +54,8 @@ def bind(lib):
     lib.oracle_f16_to_f32_array.argtypes = [p, p, i64]
     lib.oracle_quantize_rows.restype = ctypes.c_int
     lib.oracle_quantize_rows.argtypes = [p, p, p, i64, i64]
+    lib.oracle_quantize_rows_static.restype = ctypes.c_int
+    lib.oracle_quantize_rows_static.argtypes = [p, p, p, ctypes.c_float, i64, i64]
     for name in ("oracle_gemm_w8a8", "oracle_gemm_w4a8", "oracle_gemm_w8a8_blockscale"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
@@ -103,6 +105,16 @@ def quantize_rows(x):
     q = np.empty((M, K), np.int8)
     s = np.empty((M,), np.float32)
     _check(_load().oracle_quantize_rows(_ptr(x), _ptr(q), _ptr(s), M, K))
+    return q, s
+
+
+def quantize_rows_static(x, scale):
+    """x float32 [M, K], one static fp32 scale -> (q int8 [M, K], s float32 [M])."""
+    x = _c(x, np.float32)
+    M, K = x.shape
+    q = np.empty((M, K), np.int8)
+    s = np.empty((M,), np.float32)
+    _check(_load().oracle_quantize_rows_static(_ptr(x), _ptr(q), _ptr(s), ctypes.c_float(scale), M, K))
     return q, s
 
 

@@ -31,6 +31,11 @@
  *      (float)d[n][b], f); y = f * s_a[m].
  *   R5 4-bit weights: two's-complement nibbles in [-8, 7], two per byte
  *      along K, the low nibble holds the even k.
+ *   R6 static activation scale ("Quick start": ranges measured once, ahead
+ *      of time): one fp32 s > 0 for the whole tensor; q = clamp(rint(x / s),
+ *      -127, 127) saturates values beyond the calibrated range (an infinite
+ *      x gives +-127); a row holding a NaN gets scale NaN and q = 0, every
+ *      other row gets scale s.
  */
 #include <math.h>
 #include <stdint.h>
@@ -111,6 +116,34 @@ int oracle_quantize_rows(const float* x, int8_t* q, float* s, int64_t M, int64_t
         for (int64_t k = 0; k < K; ++k) {
             float t = xr[k] / sc;
             float r = nearbyintf(t); /* default rounding mode: half to even */
+            if (r > 127.0f) r = 127.0f;
+            if (r < -127.0f) r = -127.0f;
+            qr[k] = (int8_t)r;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Activation quantizer with one static scale for the tensor (R6). */
+int oracle_quantize_rows_static(const float* x, int8_t* q, float* s, float scale, int64_t M, int64_t K) {
+    if (M < 0 || K <= 0 || (M > 0 && (!x || !q || !s))) return ORACLE_ERR_ARG;
+    if (!(scale > 0.0f) || isinf(scale)) return ORACLE_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const float* xr = x + m * K;
+        int8_t* qr = q + m * K;
+        int has_nan = 0;
+        for (int64_t k = 0; k < K; ++k)
+            if (isnan(xr[k])) has_nan = 1;
+        if (has_nan) {
+            s[m] = NAN;
+            memset(qr, 0, (size_t)K);
+            continue;
+        }
+        s[m] = scale;
+        for (int64_t k = 0; k < K; ++k) {
+            float t = xr[k] / scale;
+            float r = nearbyintf(t); /* half to even; +-inf stays +-inf */
             if (r > 127.0f) r = 127.0f;
             if (r < -127.0f) r = -127.0f;
             qr[k] = (int8_t)r;

@@ -40,6 +40,14 @@ MUTANTS = [
     ("activation scale applied first", "y[m * N + n] = f * s_a[m];", "y[m * N + n] = f;", 1),
     ("fp16 subnormals off by one", "ldexpf((float)f, -24)", "ldexpf((float)f, -25)", 1),
     ("fp16 bias wrong", "ldexpf((float)(1024 + f), e - 25)", "ldexpf((float)(1024 + f), e - 24)", 1),
+    ("static: round half away from zero", "float r = nearbyintf(t); /* half to even; +-inf stays +-inf */",
+     "float r = roundf(t);", 1),
+    ("static: reciprocal instead of division", "float t = xr[k] / scale;", "float t = xr[k] * (1.0f / scale);", 1),
+    ("static: clamp to -128", "/* half to even; +-inf stays +-inf */\n            if (r > 127.0f) r = 127.0f;\n            if (r < -127.0f) r = -127.0f;",
+     "/* half to even; +-inf stays +-inf */\n            if (r > 127.0f) r = 127.0f;\n            if (r < -128.0f) r = -128.0f;", 1),
+    ("static: NaN rows not isolated", "if (isnan(xr[k])) has_nan = 1;", "", 1),
+    ("static: infinities treated as NaN", "if (isnan(xr[k])) has_nan = 1;", "if (!isfinite(xr[k])) has_nan = 1;", 1),
+    ("static: scale output inverted", "s[m] = scale;", "s[m] = 1.0f / scale;", 1),
     ("no int32 range check", "if (sum >= INT32_LIMIT || sum < -INT32_LIMIT) {", "if (0) {", 0),
 ]
 
@@ -58,6 +66,9 @@ def _checks():
         pins.test_quantizer_scale_exact_many_magnitudes,
         pins.test_quantizer_properties,
         pins.test_quantizer_special_rows_are_local,
+        pins.test_static_quantizer_exact_rationals,
+        pins.test_static_quantizer_hand_table,
+        pins.test_static_quantizer_equals_dynamic_at_row_absmax,
         pins.test_channel_epilogue_exact_rationals,
         pins.test_w4a8_epilogue_exact_rationals,
         pins.test_f16_to_f32_exhaustive_vs_numpy,

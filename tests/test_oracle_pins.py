@@ -257,6 +257,63 @@ def test_quantizer_special_rows_are_local():
     assert np.array_equal(qa, q[[0, 4]]) and np.array_equal(bits(sa), bits(s[[0, 4]]))
 
 
+def test_static_quantizer_exact_rationals():
+    """Static scale: q = clamp(rint(x / s)) with x / s correctly rounded, s copied to every row."""
+    r = _rng(120)
+    x = r.standard_normal((5, 160), dtype=np.float32)
+    x[1] *= np.float32(50.0)           # many values beyond the calibrated range: the clamp binds
+    x[2] *= np.float32(1e-3)           # most codes small, many ties near zero
+    x[3, ::7] = np.float32(2.5) * np.float32(0.0625)   # exact ties at half-integers of x / s
+    for scale in (np.float32(0.0625), np.float32(0.0170001), np.float32(0.0123), np.float32(3.0e-3),
+                  np.float32(2.0 ** -140)):
+        # last row: values next to (n + 1/2) * s, where x / s sits at a rounding tie and a
+        # quotient off by one ulp (e.g. x * (1 / s)) changes the code
+        n = np.arange(-80, 80)
+        t = ((n + 0.5) * scale).astype(np.float32)
+        x[4] = np.where(n % 2 == 0, t, np.nextafter(t, np.float32(np.inf) * np.sign(n + 0.5)))
+        q, s = oracle.quantize_rows_static(x, float(scale))
+        assert np.array_equal(bits(s), np.full(5, bits(np.float32(scale))))
+        for m in range(x.shape[0]):
+            for xv, qv in zip(x[m], q[m]):
+                t = round_f32(frac(xv) / frac(scale))
+                if np.isinf(t):
+                    ref = 127 if t > 0 else -127
+                else:
+                    ref = max(-127, min(127, rint_half_even(frac(t))))
+                assert int(qv) == ref, (scale, xv, qv, ref)
+
+
+def test_static_quantizer_hand_table():
+    x = np.array([[0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 126.5, 127.5],
+                  [1e30, -1e30, np.inf, -np.inf, 200.0, -200.0, 0.0, -0.0],
+                  [1.0, np.nan, 2.0, 3.0, 4.0, 5.0, 6.0, 7.0],
+                  [0.0] * 8], np.float32)
+    q, s = oracle.quantize_rows_static(x, 1.0)
+    assert q[0].tolist() == [0, 2, 2, 0, -2, -2, 126, 127]
+    assert q[1].tolist() == [127, -127, 127, -127, 127, -127, 0, 0]
+    assert np.isnan(s[2]) and not q[2].any()
+    assert not q[3].any() and s[3] == 1.0 and s[0] == 1.0 and s[1] == 1.0
+    # rows are independent
+    qa, sa = oracle.quantize_rows_static(x[[0, 1, 3]], 1.0)
+    assert np.array_equal(qa, q[[0, 1, 3]]) and np.array_equal(bits(sa), bits(s[[0, 1, 3]]))
+
+
+def test_static_quantizer_equals_dynamic_at_row_absmax():
+    """With s = amax / 127 of a finite row, the static and the dynamic quantizer agree bit for bit."""
+    r = _rng(121)
+    x = r.standard_normal((8, 200), dtype=np.float32) * np.float32(3.0)
+    qd, sd = oracle.quantize_rows(x)
+    for m in range(x.shape[0]):
+        qs, ss = oracle.quantize_rows_static(x[m:m + 1], float(sd[m]))
+        assert np.array_equal(qs[0], qd[m]) and bits(ss)[0] == bits(sd)[m]
+
+
+@pytest.mark.parametrize("bad", [0.0, -1.0, float("inf"), float("nan")])
+def test_static_quantizer_rejects_bad_scale(bad):
+    with pytest.raises(oracle.OracleError):
+        oracle.quantize_rows_static(np.ones((1, 4), np.float32), bad)
+
+
 # ------------------------------------------------------------------ epilogues
 
 def test_channel_epilogue_exact_rationals():

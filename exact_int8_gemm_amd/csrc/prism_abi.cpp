@@ -93,6 +93,19 @@ int prism_quantize_rows(const float* x, int8_t* q, float* scale, int64_t M, int6
   return prism::launch_quantize_rows(x, q, scale, M, K, static_cast<hipStream_t>(stream));
 }
 
+int prism_quantize_rows_static(const float* x, int8_t* q, float* scale, float s, int64_t M, int64_t K,
+                               void* stream) {
+  if (M < 0 || K < 0) return PRISM_ERR_INVALID_ARG;
+  if (!(s > 0.0f) || s == __builtin_inff()) return PRISM_ERR_INVALID_ARG;  // NaN, zero, negative, +inf
+  if (M == 0) return PRISM_OK;
+  if (K == 0 || M > INT_MAX || K > INT_MAX / 4) return PRISM_ERR_INVALID_ARG;
+  if (!x || !q || !scale) return PRISM_ERR_INVALID_ARG;
+  if (K % 16 != 0 || !aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4)) return PRISM_ERR_ALIGNMENT;
+  const int dev = check_device();
+  if (dev != PRISM_OK) return dev;
+  return prism::launch_quantize_rows_static(x, q, scale, s, M, K, static_cast<hipStream_t>(stream));
+}
+
 int prism_gemm_w8a8(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc,
                     int64_t M, int64_t N, int64_t K, void* stream) {
   bool noop;

@@ -19,6 +19,8 @@ constexpr int kSmallMMax = 64;
 // Each launcher assumes its arguments were validated by the C ABI layer and
 // returns a PRISM_* status.
 int launch_quantize_rows(const float* x, int8_t* q, float* s, int64_t M, int64_t K, hipStream_t st);
+int launch_quantize_rows_static(const float* x, int8_t* q, float* s, float scale, int64_t M, int64_t K,
+                                hipStream_t st);
 
 int launch_gemm_small(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
                       float* y, int32_t* acc, int M, int N, int K, hipStream_t st);

@@ -14,6 +14,13 @@
 // with a NaN scale and zero codes for a row holding a non-finite value, and
 // zero codes when s == 0.  The division is the correctly rounded one (the
 // library is built with correctly rounded fp32 division).
+//
+// Static form (the README's ranges measured once, ahead of time): one
+// caller-given s > 0 for the whole tensor replaces amax / 127; the clamp then
+// saturates values beyond the calibrated range (an infinite x or an
+// overflowing x / s gives +-127), and only a NaN marks a row (scale NaN,
+// zero codes).  The same kernels run both forms; the static one skips the
+// absmax and reduces a "no NaN" flag instead.
 #include "prism_internal.h"
 #include "../../include/prism.h"
 
@@ -47,6 +54,10 @@ __device__ inline bool finite4(const float4 v) {
   return isfinite(v.x) && isfinite(v.y) && isfinite(v.z) && isfinite(v.w);
 }
 
+__device__ inline bool nonan4(const float4 v) {
+  return !isnan(v.x) && !isnan(v.y) && !isnan(v.z) && !isnan(v.w);
+}
+
 __device__ inline float absmax4(const float4 v) {
   return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 }
@@ -76,10 +87,11 @@ __device__ inline void row_reduce(float& amax, bool& finite) {
 
 // Register-resident variant: the row's K/4 float4 are spread over the
 // workgroup, chunk c on thread c % blockDim.x, slot c / blockDim.x < CPT.
-template <int CPT>
+// STATIC: `fixed` is the tensor's scale and `finite` below means "no NaN".
+template <int CPT, bool STATIC>
 __global__ __launch_bounds__(kMaxThreads) void quantize_rows_reg(const float* __restrict__ x,
                                                                   int8_t* __restrict__ q, float* __restrict__ s,
-                                                                  int64_t K) {
+                                                                  int64_t K, float fixed) {
   const int64_t row = blockIdx.x;
   const int T = (int)blockDim.x;
   const float4* xr = reinterpret_cast<const float4*>(x + row * K);
@@ -94,13 +106,17 @@ __global__ __launch_bounds__(kMaxThreads) void quantize_rows_reg(const float* __
     const int64_t c = threadIdx.x + (int64_t)T * i;
     if (c < nchunk) {
       v[i] = xr[c];
-      amax = fmaxf(amax, absmax4(v[i]));
-      finite = finite && finite4(v[i]);
+      if (STATIC) {
+        finite = finite && nonan4(v[i]);
+      } else {
+        amax = fmaxf(amax, absmax4(v[i]));
+        finite = finite && finite4(v[i]);
+      }
     }
   }
   row_reduce(amax, finite);
 
-  const float sc = finite ? amax / 127.0f : __builtin_nanf("");
+  const float sc = finite ? (STATIC ? fixed : amax / 127.0f) : __builtin_nanf("");
   if (threadIdx.x == 0) s[row] = sc;
   const bool zero = !finite || sc == 0.0f;
 #pragma unroll
@@ -111,9 +127,10 @@ __global__ __launch_bounds__(kMaxThreads) void quantize_rows_reg(const float* __
 }
 
 // Long rows: first pass reduces, second pass re-reads and quantizes.
+template <bool STATIC>
 __global__ __launch_bounds__(kMaxThreads) void quantize_rows_2pass(const float* __restrict__ x,
                                                                     int8_t* __restrict__ q, float* __restrict__ s,
-                                                                    int64_t K) {
+                                                                    int64_t K, float fixed) {
   const int64_t row = blockIdx.x;
   const float4* xr = reinterpret_cast<const float4*>(x + row * K);
   uint32_t* qr = reinterpret_cast<uint32_t*>(q + row * K);
@@ -123,39 +140,53 @@ __global__ __launch_bounds__(kMaxThreads) void quantize_rows_2pass(const float* 
   bool finite = true;
   for (int64_t c = threadIdx.x; c < nchunk; c += blockDim.x) {
     const float4 v = xr[c];
-    amax = fmaxf(amax, absmax4(v));
-    finite = finite && finite4(v);
+    if (STATIC) {
+      finite = finite && nonan4(v);
+    } else {
+      amax = fmaxf(amax, absmax4(v));
+      finite = finite && finite4(v);
+    }
   }
   row_reduce(amax, finite);
 
-  const float sc = finite ? amax / 127.0f : __builtin_nanf("");
+  const float sc = finite ? (STATIC ? fixed : amax / 127.0f) : __builtin_nanf("");
   if (threadIdx.x == 0) s[row] = sc;
   const bool zero = !finite || sc == 0.0f;
   for (int64_t c = threadIdx.x; c < nchunk; c += blockDim.x) qr[c] = zero ? 0u : pack4(xr[c], sc);
 }
 
-template <int CPT>
-void launch_reg(const float* x, int8_t* q, float* s, int64_t M, int64_t K, hipStream_t st) {
+template <int CPT, bool STATIC>
+void launch_reg(const float* x, int8_t* q, float* s, int64_t M, int64_t K, float fixed, hipStream_t st) {
   const int64_t nchunk = K / 4;
   const int64_t per_cpt = (nchunk + CPT - 1) / CPT;
   const int threads = (int)((per_cpt + 63) / 64 * 64);
-  quantize_rows_reg<CPT><<<(unsigned)M, threads, 0, st>>>(x, q, s, K);
+  quantize_rows_reg<CPT, STATIC><<<(unsigned)M, threads, 0, st>>>(x, q, s, K, fixed);
+}
+
+template <bool STATIC>
+int launch_rows(const float* x, int8_t* q, float* s, int64_t M, int64_t K, float fixed, hipStream_t st) {
+  const int64_t cpt = (K / 4 + kMaxThreads - 1) / kMaxThreads;
+  if (cpt <= 1) launch_reg<1, STATIC>(x, q, s, M, K, fixed, st);
+  else if (cpt <= 2) launch_reg<2, STATIC>(x, q, s, M, K, fixed, st);
+  else if (cpt <= 3) launch_reg<3, STATIC>(x, q, s, M, K, fixed, st);
+  else if (cpt <= 4) launch_reg<4, STATIC>(x, q, s, M, K, fixed, st);
+  else if (cpt <= 6) launch_reg<6, STATIC>(x, q, s, M, K, fixed, st);
+  else if (cpt <= 8) launch_reg<8, STATIC>(x, q, s, M, K, fixed, st);
+  else if (cpt <= 12) launch_reg<12, STATIC>(x, q, s, M, K, fixed, st);
+  else if (cpt <= kMaxCpt) launch_reg<kMaxCpt, STATIC>(x, q, s, M, K, fixed, st);
+  else quantize_rows_2pass<STATIC><<<(unsigned)M, kMaxThreads, 0, st>>>(x, q, s, K, fixed);
+  return launch_status();
 }
 
 }  // namespace
 
 int launch_quantize_rows(const float* x, int8_t* q, float* s, int64_t M, int64_t K, hipStream_t st) {
-  const int64_t cpt = (K / 4 + kMaxThreads - 1) / kMaxThreads;
-  if (cpt <= 1) launch_reg<1>(x, q, s, M, K, st);
-  else if (cpt <= 2) launch_reg<2>(x, q, s, M, K, st);
-  else if (cpt <= 3) launch_reg<3>(x, q, s, M, K, st);
-  else if (cpt <= 4) launch_reg<4>(x, q, s, M, K, st);
-  else if (cpt <= 6) launch_reg<6>(x, q, s, M, K, st);
-  else if (cpt <= 8) launch_reg<8>(x, q, s, M, K, st);
-  else if (cpt <= 12) launch_reg<12>(x, q, s, M, K, st);
-  else if (cpt <= kMaxCpt) launch_reg<kMaxCpt>(x, q, s, M, K, st);
-  else quantize_rows_2pass<<<(unsigned)M, kMaxThreads, 0, st>>>(x, q, s, K);
-  return launch_status();
+  return launch_rows<false>(x, q, s, M, K, 0.0f, st);
+}
+
+int launch_quantize_rows_static(const float* x, int8_t* q, float* s, float scale, int64_t M, int64_t K,
+                                hipStream_t st) {
+  return launch_rows<true>(x, q, s, M, K, scale, st);
 }
 
 }  // namespace prism

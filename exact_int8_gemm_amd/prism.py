@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libprism.so")
 
 PRISM_OK = 0
-ABI_VERSION = 1
+ABI_VERSION = 2
 K_MAX = 131040
 
 
@@ -39,6 +39,8 @@ def _declare(lib):
     lib.prism_status_string.argtypes = [i32]
     lib.prism_quantize_rows.restype = i32
     lib.prism_quantize_rows.argtypes = [p, p, p, i64, i64, p]
+    lib.prism_quantize_rows_static.restype = i32
+    lib.prism_quantize_rows_static.argtypes = [p, p, p, ctypes.c_float, i64, i64, p]
     for name in ("prism_gemm_w8a8", "prism_gemm_w8a8_blockscale", "prism_gemm_w4a8"):
         fn = getattr(lib, name)
         fn.restype = i32
@@ -109,6 +111,22 @@ def quantize_rows(x, q=None, scale=None):
         _need(scale, "scale", torch.float32, (M,), dev)
     with torch.cuda.device(dev):
         _check(lib().prism_quantize_rows(_ptr(x), _ptr(q), _ptr(scale), M, K, _stream(dev)))
+    return q, scale
+
+
+def quantize_rows_static(x, s, q=None, scale=None):
+    """x float32 [M, K] on the GPU and one calibrated scale s > 0 -> (q int8 [M, K], scale float32 [M])."""
+    dev = _gpu(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    M, K = x.shape
+    _need(x, "x", torch.float32, (M, K), dev)
+    q = torch.empty((M, K), dtype=torch.int8, device=dev) if q is None else _need(q, "q", torch.int8, (M, K), dev)
+    scale = torch.empty((M,), dtype=torch.float32, device=dev) if scale is None else \
+        _need(scale, "scale", torch.float32, (M,), dev)
+    with torch.cuda.device(dev):
+        _check(lib().prism_quantize_rows_static(_ptr(x), _ptr(q), _ptr(scale), ctypes.c_float(float(s)), M, K,
+                                                _stream(dev)))
     return q, scale
 
 

@@ -41,7 +41,7 @@ extern "C" {
 #endif
 
 /* Bumped on any change of a signature or of the semantics below. */
-#define PRISM_ABI_VERSION 1
+#define PRISM_ABI_VERSION 2
 
 /* Largest accepted K.  For K <= 131040 every exact sum of K products of two
  * int8 values (|q|, |w| <= 128) lies strictly inside the int32 range. */
@@ -75,6 +75,24 @@ const char* prism_status_string(int status);
  */
 int prism_quantize_rows(const float* x, int8_t* q, float* scale,
                         int64_t M, int64_t K, void* stream);
+
+/*
+ * Int8 activation quantizer with one static, calibrated scale for the whole
+ * tensor (README "Quick start": the int8 activation ranges are measured once
+ * ahead of time, not per batch).
+ *   x      [M][K] fp32, input.
+ *   q      [M][K] int8, output.
+ *   scale  [M] fp32, output: the row scales to hand to the GEMM calls.
+ *   s      the calibrated scale, a host value; must be finite and > 0
+ *          (otherwise PRISM_ERR_INVALID_ARG and nothing is enqueued).
+ * For each row m without a NaN: scale[m] = s and q[m][k] = clamp(rint(x[m][k]
+ * / s), -127, 127) (IEEE division, rint half to even), so values beyond the
+ * calibrated range saturate at +-127, an infinite x included.  A row holding
+ * a NaN gets scale NaN and q = 0.  Rows never influence each other.
+ * K must be a multiple of 16; x and q 16-byte aligned, scale 4-byte aligned.
+ */
+int prism_quantize_rows_static(const float* x, int8_t* q, float* scale, float s,
+                               int64_t M, int64_t K, void* stream);
 
 /*
  * W8A8 GEMM with per-output-channel weight scales (README "Why

@@ -39,9 +39,10 @@ def built():
     return LIB
 
 
-def test_header_declares_the_four_calls():
+def test_header_declares_every_call():
     names = set(_declared_functions())
-    assert {"prism_quantize_rows", "prism_gemm_w8a8", "prism_gemm_w8a8_blockscale", "prism_gemm_w4a8",
+    assert {"prism_quantize_rows", "prism_quantize_rows_static", "prism_gemm_w8a8", "prism_gemm_w8a8_blockscale",
+            "prism_gemm_w4a8",
             "prism_abi_version", "prism_status_string"} <= names
 
 
@@ -72,6 +73,8 @@ lib.prism_status_string.restype = ctypes.c_char_p
 lib.prism_status_string.argtypes = [i32]
 lib.prism_quantize_rows.restype = i32
 lib.prism_quantize_rows.argtypes = [p, p, p, i64, i64, p]
+lib.prism_quantize_rows_static.restype = i32
+lib.prism_quantize_rows_static.argtypes = [p, p, p, ctypes.c_float, i64, i64, p]
 for n in ("prism_gemm_w8a8", "prism_gemm_w8a8_blockscale", "prism_gemm_w4a8"):
     getattr(lib, n).restype = i32
     getattr(lib, n).argtypes = [p, p, p, p, p, p, i64, i64, i64, p]
@@ -108,6 +111,26 @@ CASES = [
     ("prism_quantize_rows", [A + 4, A, A, 4, 64, None], ALIGN),
     ("prism_quantize_rows", [A, A + 8, A, 4, 64, None], ALIGN),
     ("prism_quantize_rows", [A, A, A + 2, 4, 64, None], ALIGN),
+]
+_QS = "prism_quantize_rows_static"
+CASES += [
+    (_QS, [A, A, A, 1.0, 0, 64, None], OK),             # M = 0: no-op
+    (_QS, [None, None, None, 0.5, 0, 0, None], OK),
+    (_QS, [A, A, A, 0.0, 4, 64, None], INVALID),        # the scale must be finite and > 0
+    (_QS, [A, A, A, -1.0, 4, 64, None], INVALID),
+    (_QS, [A, A, A, float("inf"), 4, 64, None], INVALID),
+    (_QS, [A, A, A, float("nan"), 4, 64, None], INVALID),
+    (_QS, [A, A, A, float("nan"), 0, 64, None], INVALID),  # checked even when M = 0
+    (_QS, [A, A, A, 1.0, -1, 64, None], INVALID),
+    (_QS, [A, A, A, 1.0, 4, -16, None], INVALID),
+    (_QS, [A, A, A, 1.0, 4, 0, None], INVALID),
+    (_QS, [None, A, A, 1.0, 4, 64, None], INVALID),
+    (_QS, [A, None, A, 1.0, 4, 64, None], INVALID),
+    (_QS, [A, A, None, 1.0, 4, 64, None], INVALID),
+    (_QS, [A, A, A, 1.0, 4, 40, None], ALIGN),
+    (_QS, [A + 4, A, A, 1.0, 4, 64, None], ALIGN),
+    (_QS, [A, A + 8, A, 1.0, 4, 64, None], ALIGN),
+    (_QS, [A, A, A + 2, 1.0, 4, 64, None], ALIGN),
 ]
 for fn, kmul in (("prism_gemm_w8a8", 16), ("prism_gemm_w4a8", 32), ("prism_gemm_w8a8_blockscale", 32)):
     CASES += [
@@ -173,11 +196,12 @@ def test_validation(child_results, i):
 def test_valid_call_without_a_device_is_unsupported(built):
     """Valid arguments with no visible device: the device check answers, nothing launches."""
     env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", CUDA_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1")
-    payload = json.dumps([["prism_gemm_w8a8", _g()], ["prism_quantize_rows", [A, A, A, 4, 64, None]]])
+    payload = json.dumps([["prism_gemm_w8a8", _g()], ["prism_quantize_rows", [A, A, A, 4, 64, None]],
+                          ["prism_quantize_rows_static", [A, A, A, 0.25, 4, 64, None]]])
     out = subprocess.run([sys.executable, "-c", _CHILD, built, payload], env=env, capture_output=True, text=True,
                          timeout=120)
     assert out.returncode == 0, out.stderr
-    assert json.loads(out.stdout.strip().splitlines()[-1])["status"] == [UNSUP, UNSUP]
+    assert json.loads(out.stdout.strip().splitlines()[-1])["status"] == [UNSUP, UNSUP, UNSUP]
 
 
 def test_build_uses_result_defining_flags():

@@ -56,6 +56,76 @@ def test_quantize_special_rows():
     assert_same_ints(host(q), q_ref, "codes")
 
 
+STATIC_SCALES = [0.0625, 0.0170001, 0.0123, 3.0e-3, 2.0 ** -140]
+
+
+@pytest.mark.parametrize("M,K", [(1, 16), (5, 48), (33, 2560), (8, 9728), (4, 10256), (2, 65552), (3, 131072)])
+@pytest.mark.parametrize("scale", STATIC_SCALES)
+def test_quantize_rows_static(M, K, scale):
+    rng = np.random.default_rng(M * 7919 + K)
+    x = rng.standard_normal((M, K), dtype=np.float32) * np.float32(0.6)
+    x[:, rng.choice(K, max(1, K // 50), replace=False)] *= np.float32(40.0)   # beyond the range: saturate
+    # values next to (n + 1/2) * scale: x / scale sits at a rounding tie
+    n = rng.integers(-130, 130, size=K)
+    t = ((n + 0.5) * np.float32(scale)).astype(np.float32)
+    x[0] = np.where(n % 2 == 0, t, np.nextafter(t, np.float32(np.inf) * np.sign(n + 0.5)))
+    q_ref, s_ref = oracle.quantize_rows_static(x, scale)
+    q, s = prism.quantize_rows_static(dev(x), scale)
+    torch.cuda.synchronize()
+    assert_same_floats(host(s), s_ref, "scale")
+    assert_same_ints(host(q), q_ref, "codes")
+
+
+@pytest.mark.parametrize("scale", [1.0, 1e-3, 2.0 ** -140, 3.0e38])
+def test_quantize_static_special_rows(scale):
+    K = 64
+    rows = []
+    rows.append(np.zeros(K))                                   # all zeros
+    r = np.zeros(K); r[3] = -0.0; rows.append(r)               # negative zeros
+    r = np.ones(K); r[5] = np.nan; rows.append(r)              # NaN: the row is flagged
+    r = np.ones(K); r[0] = np.inf; rows.append(r)              # +inf saturates
+    r = np.ones(K); r[63] = -np.inf; rows.append(r)            # -inf saturates
+    rows.append(np.full(K, 1e-44))                             # subnormal inputs
+    rows.append(np.linspace(-3e38, 3e38, K))                   # huge values: x / s overflows
+    r = np.arange(K) - 32 + 0.5; rows.append(r)                # exact halves at scale 1
+    r = np.full(K, 2.5); r[1] = -127.5; rows.append(r)         # ties to even, clamp at -127
+    x = np.array(rows, dtype=np.float32)
+    q_ref, s_ref = oracle.quantize_rows_static(x, scale)
+    q, s = prism.quantize_rows_static(dev(x), scale)
+    torch.cuda.synchronize()
+    assert_same_floats(host(s), s_ref, "scale")
+    assert_same_ints(host(q), q_ref, "codes")
+
+
+def test_static_quantize_then_gemm():
+    """Static scale end to end: quantize with the calibrated scale, then the W8A8 GEMM."""
+    rng = np.random.default_rng(77)
+    M, N, K = 70, 300, 1040
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    w = wl.int8_weights(rng, N, K)
+    s_w = wl.channel_scales(rng, N)
+    scale = 0.021
+    q_ref, sa_ref = oracle.quantize_rows_static(x, scale)
+    y_ref, acc_ref = oracle.gemm_w8a8(q_ref, sa_ref, w, s_w)
+    q, sa = prism.quantize_rows_static(dev(x), scale)
+    acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    y = prism.gemm_w8a8(q, sa, dev(w), dev(s_w), acc=acc)
+    torch.cuda.synchronize()
+    assert_same_ints(host(acc), acc_ref, "acc")
+    assert_same_floats(host(y), y_ref, "y")
+
+
+@pytest.mark.parametrize("bad", [0.0, -2.0, float("inf"), float("nan")])
+def test_static_quantize_bad_scale_raises_and_writes_nothing(bad):
+    x = dev(np.ones((2, 32), np.float32))
+    q = torch.full((2, 32), 5, dtype=torch.int8, device=DEV)
+    s = torch.full((2,), 9.0, dtype=torch.float32, device=DEV)
+    with pytest.raises(prism.PrismError):
+        prism.quantize_rows_static(x, bad, q=q, scale=s)
+    torch.cuda.synchronize()
+    assert (host(q) == 5).all() and (host(s) == 9.0).all()
+
+
 # ------------------------------------------------------------------ GEMMs
 
 def _case(seed, M, N, K, kind):

@@ -56,6 +56,8 @@ def bind(lib):
     lib.oracle_quantize_rows.argtypes = [p, p, p, i64, i64]
     lib.oracle_quantize_rows_static.restype = ctypes.c_int
     lib.oracle_quantize_rows_static.argtypes = [p, p, p, ctypes.c_float, i64, i64]
+    lib.oracle_repack_q8_0.restype = ctypes.c_int
+    lib.oracle_repack_q8_0.argtypes = [p, p, p, i64, i64]
     for name in ("oracle_gemm_w8a8", "oracle_gemm_w4a8", "oracle_gemm_w8a8_blockscale"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
@@ -116,6 +118,16 @@ def quantize_rows_static(x, scale):
     s = np.empty((M,), np.float32)
     _check(_load().oracle_quantize_rows_static(_ptr(x), _ptr(q), _ptr(s), ctypes.c_float(scale), M, K))
     return q, s
+
+
+def repack_q8_0(blocks, N, K):
+    """Q8_0 blocks (uint8, N * K/32 * 34 bytes) -> (w int8 [N, K], d uint16 [N, K/32] binary16 bits)."""
+    blocks = _c(blocks, np.uint8).reshape(-1)
+    assert blocks.size == N * (K // 32) * 34
+    w = np.empty((N, K), np.int8)
+    d = np.empty((N, K // 32), np.uint16)
+    _check(_load().oracle_repack_q8_0(_ptr(blocks), _ptr(w), _ptr(d), N, K))
+    return w, d
 
 
 def gemm_w8a8(q, s_a, w, s_w):

@@ -31,6 +31,12 @@
  *      (float)d[n][b], f); y = f * s_a[m].
  *   R5 4-bit weights: two's-complement nibbles in [-8, 7], two per byte
  *      along K, the low nibble holds the even k.
+ *   R7 Q8_0 weight blocks (the public GGUF layout; the pages only say that
+ *      Q8_0 files run as int8 with no conversion step): 34 bytes per block,
+ *      a little-endian binary16 scale then the 32 int8 codes of k = 32 b ..
+ *      32 b + 31 of row n; blocks follow each other row by row, block
+ *      n * (K / 32) + b.  A block stands for the values scale * code, which
+ *      is exactly the block-scale operand pair (w, d) of R4.
  *   R6 static activation scale ("Quick start": ranges measured once, ahead
  *      of time): one fp32 s > 0 for the whole tensor; q = clamp(rint(x / s),
  *      -127, 127) saturates values beyond the calibrated range (an infinite
@@ -147,6 +153,20 @@ int oracle_quantize_rows_static(const float* x, int8_t* q, float* s, float scale
             if (r > 127.0f) r = 127.0f;
             if (r < -127.0f) r = -127.0f;
             qr[k] = (int8_t)r;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Q8_0 blocks -> int8 codes w [N][K] and binary16 scale bits d [N][K/32] (R7). */
+int oracle_repack_q8_0(const uint8_t* blocks, int8_t* w, uint16_t* d, int64_t N, int64_t K) {
+    if (N < 0 || K <= 0 || K % 32 != 0 || (N > 0 && (!blocks || !w || !d))) return ORACLE_ERR_ARG;
+    const int64_t NB = K / 32;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t b = 0; b < NB; ++b) {
+            const uint8_t* blk = blocks + (n * NB + b) * 34;
+            d[n * NB + b] = (uint16_t)(blk[0] | (blk[1] << 8));
+            for (int64_t j = 0; j < 32; ++j) w[n * K + b * 32 + j] = (int8_t)blk[2 + j];
         }
     }
     return ORACLE_OK;

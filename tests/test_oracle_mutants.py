@@ -48,6 +48,11 @@ MUTANTS = [
     ("static: NaN rows not isolated", "if (isnan(xr[k])) has_nan = 1;", "", 1),
     ("static: infinities treated as NaN", "if (isnan(xr[k])) has_nan = 1;", "if (!isfinite(xr[k])) has_nan = 1;", 1),
     ("static: scale output inverted", "s[m] = scale;", "s[m] = 1.0f / scale;", 1),
+    ("q8_0: big-endian scale", "(uint16_t)(blk[0] | (blk[1] << 8))", "(uint16_t)(blk[1] | (blk[0] << 8))", 1),
+    ("q8_0: codes one byte early", "(int8_t)blk[2 + j]", "(int8_t)blk[1 + j]", 1),
+    ("q8_0: block stride 33", "(n * NB + b) * 34", "(n * NB + b) * 33", 1),
+    ("q8_0: codes reversed", "w[n * K + b * 32 + j] = (int8_t)blk[2 + j];",
+     "w[n * K + b * 32 + (31 - j)] = (int8_t)blk[2 + j];", 1),
     ("no int32 range check", "if (sum >= INT32_LIMIT || sum < -INT32_LIMIT) {", "if (0) {", 0),
 ]
 
@@ -69,6 +74,8 @@ def _checks():
         pins.test_static_quantizer_exact_rationals,
         pins.test_static_quantizer_hand_table,
         pins.test_static_quantizer_equals_dynamic_at_row_absmax,
+        pins.test_q8_0_hand_fixture,
+        pins.test_q8_0_round_trip_with_struct_packer,
         pins.test_channel_epilogue_exact_rationals,
         pins.test_w4a8_epilogue_exact_rationals,
         pins.test_f16_to_f32_exhaustive_vs_numpy,

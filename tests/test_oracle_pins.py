@@ -314,6 +314,44 @@ def test_static_quantizer_rejects_bad_scale(bad):
         oracle.quantize_rows_static(np.ones((1, 4), np.float32), bad)
 
 
+# ------------------------------------------------------------------ Q8_0 blocks
+
+def _pack_q8_0(w, d_values):
+    """Q8_0 bytes from the format's definition, with Python's struct (binary16 'e', little-endian)."""
+    import struct
+    N, K = w.shape
+    out = bytearray()
+    for n in range(N):
+        for b in range(K // 32):
+            out += struct.pack("<e", float(d_values[n, b]))
+            out += struct.pack("<32b", *[int(v) for v in w[n, 32 * b:32 * b + 32]])
+    return np.frombuffer(bytes(out), np.uint8)
+
+
+def test_q8_0_hand_fixture():
+    # two rows of one block each: scale 1.0 (bits 0x3c00) and -2.0 (0xc000), codes written out
+    codes0 = [-128, -1, 0, 1, 127] + [5] * 27
+    codes1 = list(range(-16, 16))
+    raw = bytes([0x00, 0x3C]) + bytes(c & 0xFF for c in codes0) + bytes([0x00, 0xC0]) + bytes(c & 0xFF for c in codes1)
+    w, d = oracle.repack_q8_0(np.frombuffer(raw, np.uint8), 2, 32)
+    assert d.tolist() == [[0x3C00], [0xC000]]
+    assert w[0].tolist() == codes0 and w[1].tolist() == codes1
+
+
+def test_q8_0_round_trip_with_struct_packer():
+    r = _rng(130)
+    N, K = 5, 192
+    w = r.integers(-128, 128, (N, K), dtype=np.int8)
+    dv = (r.standard_normal((N, K // 32)) * 0.01).astype(np.float16)
+    dv[0, 0] = np.float16(6.0e-8)      # subnormal binary16
+    dv[1, 2] = np.float16(-0.0)
+    blocks = _pack_q8_0(w, dv)
+    assert blocks.size == N * (K // 32) * 34
+    w2, d2 = oracle.repack_q8_0(blocks, N, K)
+    assert np.array_equal(w2, w)
+    assert np.array_equal(d2, dv.view(np.uint16))
+
+
 # ------------------------------------------------------------------ epilogues
 
 def test_channel_epilogue_exact_rationals():

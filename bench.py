@@ -45,7 +45,7 @@ def _args():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy three times (scale for HBM byte counters)")
     ap.add_argument("--only", default=None, help="run only one kernel measurement (for profiling): "
-                    "step | w4a8 | block | stress")
+                    "step | w4a8 | block | repack | stress")
     return ap.parse_args()
 
 
@@ -63,6 +63,17 @@ class Launcher:
     def quantize(self, x, q, s):
         M, K = x.shape
         f, a = self.lib.prism_quantize_rows, (self.p(x), self.p(q), self.p(s), M, K, self.stream)
+        return lambda: f(*a)
+
+    def quantize_static(self, x, q, s, scale):
+        M, K = x.shape
+        f, a = self.lib.prism_quantize_rows_static, (self.p(x), self.p(q), self.p(s), ctypes.c_float(scale), M, K,
+                                                     self.stream)
+        return lambda: f(*a)
+
+    def repack(self, blocks, w, d):
+        N, K = w.shape
+        f, a = self.lib.prism_repack_q8_0, (self.p(blocks), self.p(w), self.p(d), N, K, self.stream)
         return lambda: f(*a)
 
     def w8a8(self, q, sa, w, sw, y):
@@ -275,13 +286,29 @@ def kernels(torch, prism, wl, only=None):
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
         t1, t = _time_launches(torch, [L.block(q, sa, w, d, y) for w, d in ws], 10)
         ops = 2 * M * N * K
-        # fp32 VALU bound of the block epilogue: one convert and one fma per 32-k partial,
-        # 256 CUs x 64 lanes x 2.4 GHz lane-operations per second
-        valu_s = M * N * (K // 32) * 2 / (256 * 64 * 2.4e9)
+        # VALU bound of the block epilogue: one int32 -> fp32 convert and one fp32 fma per
+        # 32-k partial; a wave64 fma occupies a SIMD for 4 cycles and a convert for 2
+        # (measured on MI355X), i.e. 6 cycles per 64 partials on each of 1024 SIMDs at 2.4 GHz
+        valu_s = M * N * (K // 32) * 6 / 64 / (1024 * 2.4e9)
         out["block_scale_m2048"] = dict(us=t * 1e6, tops=ops / t / 1e12, mfma_frac=ops / t / 1e12 / PEAK_INT8_TOPS,
                                         valu_bound_us=valu_s * 1e6, valu_frac=valu_s / t, us_single_launch=t1 * 1e6,
                                         copies=R)
         del ws
+    if only in (None, "repack"):
+        # Q8_0 blocks of the block-scale weight matrix (17408 x 5120): 34 bytes read and
+        # 34 bytes written per 32-weight block
+        N, K = 17408, 5120
+        nblk = N * (K // 32)
+        g = torch.Generator(device=dev).manual_seed(11)
+        R = _copies(2 * 34 * nblk)
+        srcs = [torch.randint(0, 256, (nblk * 34,), dtype=torch.uint8, device=dev, generator=g) for _ in range(R)]
+        w = torch.empty((N, K), dtype=torch.int8, device=dev)
+        d = torch.empty((N, K // 32), dtype=torch.int16, device=dev)
+        t1, t = _time_launches(torch, [L.repack(b, w, d) for b in srcs], 20)
+        nbytes = 2 * 34 * nblk
+        out["repack_q8_0_17408x5120"] = dict(us=t * 1e6, gbs=nbytes / t / 1e9, hbm_frac=nbytes / t / 1e9 / PEAK_HBM_GBS,
+                                             us_single_launch=t1 * 1e6, algorithmic_bytes=nbytes, copies=R)
+        del srcs
     if only in (None, "stress"):
         st = wl.stress()
         w, sw = T(st["w"]), T(st["s_w"])
@@ -292,6 +319,8 @@ def kernels(torch, prism, wl, only=None):
             q = torch.empty((M, K), dtype=torch.int8, device=dev)
             sa = torch.empty((M,), dtype=torch.float32, device=dev)
             _, tq = _time_launches(torch, [L.quantize(x, q, sa)], 20)
+            _, tqs = _time_launches(torch, [L.quantize_static(x, q, sa, 0.03)], 20)
+            _check(L.quantize(x, q, sa)())   # the GEMM below runs on the per-row codes
             y = torch.empty((M, N), dtype=torch.float32, device=dev)
             t1, t = _time_launches(torch, [L.w8a8(q, sa, w, sw, y)], 20 if M > 1 else 100)
             nbytes = N * K + 4 * N + M * K + 4 * M + 4 * M * N
@@ -299,7 +328,9 @@ def kernels(torch, prism, wl, only=None):
                                          mfma_frac=2 * M * N * K / t / 1e12 / PEAK_INT8_TOPS,
                                          gbs=nbytes / t / 1e9, hbm_frac=nbytes / t / 1e9 / PEAK_HBM_GBS,
                                          quantize_us=tq * 1e6, us_single_launch=t1 * 1e6,
-                                         quantize_gbs=(5 * M * K + 4 * M) / tq / 1e9)
+                                         quantize_gbs=(5 * M * K + 4 * M) / tq / 1e9,
+                                         quantize_static_us=tqs * 1e6,
+                                         quantize_static_gbs=(5 * M * K + 4 * M) / tqs / 1e9)
     return out
 
 

@@ -106,6 +106,18 @@ int prism_quantize_rows_static(const float* x, int8_t* q, float* scale, float s,
   return prism::launch_quantize_rows_static(x, q, scale, s, M, K, static_cast<hipStream_t>(stream));
 }
 
+int prism_repack_q8_0(const uint8_t* blocks, int8_t* w, uint16_t* d, int64_t N, int64_t K, void* stream) {
+  if (N < 0 || K < 0) return PRISM_ERR_INVALID_ARG;
+  if (N == 0) return PRISM_OK;
+  if (K == 0 || N > INT_MAX || K > INT_MAX) return PRISM_ERR_INVALID_ARG;
+  if (!blocks || !w || !d) return PRISM_ERR_INVALID_ARG;
+  if (K % 32 != 0 || !aligned(blocks, 16) || !aligned(w, 16) || !aligned(d, 2)) return PRISM_ERR_ALIGNMENT;
+  if ((N * (K / 32) + 255) / 256 > INT_MAX) return PRISM_ERR_INVALID_ARG;  // grid size
+  const int dev = check_device();
+  if (dev != PRISM_OK) return dev;
+  return prism::launch_repack_q8_0(blocks, w, d, N, K, static_cast<hipStream_t>(stream));
+}
+
 int prism_gemm_w8a8(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc,
                     int64_t M, int64_t N, int64_t K, void* stream) {
   bool noop;

@@ -41,6 +41,8 @@ def _declare(lib):
     lib.prism_quantize_rows.argtypes = [p, p, p, i64, i64, p]
     lib.prism_quantize_rows_static.restype = i32
     lib.prism_quantize_rows_static.argtypes = [p, p, p, ctypes.c_float, i64, i64, p]
+    lib.prism_repack_q8_0.restype = i32
+    lib.prism_repack_q8_0.argtypes = [p, p, p, i64, i64, p]
     for name in ("prism_gemm_w8a8", "prism_gemm_w8a8_blockscale", "prism_gemm_w4a8"):
         fn = getattr(lib, name)
         fn.restype = i32
@@ -128,6 +130,23 @@ def quantize_rows_static(x, s, q=None, scale=None):
         _check(lib().prism_quantize_rows_static(_ptr(x), _ptr(q), _ptr(scale), ctypes.c_float(float(s)), M, K,
                                                 _stream(dev)))
     return q, scale
+
+
+def repack_q8_0(blocks, N, K, w=None, d=None):
+    """Q8_0 blocks (uint8 tensor of N * K/32 * 34 bytes on the GPU) -> (w int8 [N, K], d int16 [N, K/32]).
+
+    ``d`` holds the binary16 bit patterns of the block scales (the dtype the block-scale GEMM takes)."""
+    dev = _gpu(blocks, "blocks")
+    N, K = int(N), int(K)
+    if K <= 0 or K % 32:
+        raise ValueError("K must be a positive multiple of 32")
+    _need(blocks, "blocks", torch.uint8, (N * (K // 32) * 34,), dev)
+    w = torch.empty((N, K), dtype=torch.int8, device=dev) if w is None else _need(w, "w", torch.int8, (N, K), dev)
+    d = torch.empty((N, K // 32), dtype=torch.int16, device=dev) if d is None else \
+        _need(d, "d", torch.int16, (N, K // 32), dev)
+    with torch.cuda.device(dev):
+        _check(lib().prism_repack_q8_0(_ptr(blocks), _ptr(w), _ptr(d), N, K, _stream(dev)))
+    return w, d
 
 
 def _gemm_args(q, s_a, w, w_cols, wdtype, s_w_name, s_w, s_w_dtype, s_w_shape_fn):

@@ -95,6 +95,22 @@ int prism_quantize_rows_static(const float* x, int8_t* q, float* scale, float s,
                                int64_t M, int64_t K, void* stream);
 
 /*
+ * Q8_0 weight blocks -> the (w, d) planes of prism_gemm_w8a8_blockscale
+ * (README "Why StartLux-Prism": released Q8_0 files run as int8 W8A8 with no
+ * conversion step).  The block layout is the public GGUF one, not given by
+ * the pages: 34 bytes per block, a little-endian binary16 scale followed by
+ * the 32 int8 codes of k = 32 b .. 32 b + 31 of weight row n; blocks are
+ * stored row by row, block n * (K/32) + b.
+ *   blocks [N * K/32][34] bytes, input (16-byte aligned).
+ *   w      [N][K] int8, output: the codes (16-byte aligned).
+ *   d      [N][K/32] binary16 bit patterns, output: the scales (2-byte aligned).
+ * Pure byte movement: every output equals an input byte pair or byte.
+ * K must be a positive multiple of 32; N = 0 is a no-op.
+ */
+int prism_repack_q8_0(const uint8_t* blocks, int8_t* w, uint16_t* d,
+                      int64_t N, int64_t K, void* stream);
+
+/*
  * W8A8 GEMM with per-output-channel weight scales (README "Why
  * StartLux-Prism": Q8_0 weights as int8 W8A8, summed exactly in int32).
  *   q    [M][K] int8 activations, s_a [M] fp32 row scales.

@@ -41,8 +41,8 @@ def built():
 
 def test_header_declares_every_call():
     names = set(_declared_functions())
-    assert {"prism_quantize_rows", "prism_quantize_rows_static", "prism_gemm_w8a8", "prism_gemm_w8a8_blockscale",
-            "prism_gemm_w4a8",
+    assert {"prism_quantize_rows", "prism_quantize_rows_static", "prism_repack_q8_0", "prism_gemm_w8a8",
+            "prism_gemm_w8a8_blockscale", "prism_gemm_w4a8",
             "prism_abi_version", "prism_status_string"} <= names
 
 
@@ -75,6 +75,8 @@ lib.prism_quantize_rows.restype = i32
 lib.prism_quantize_rows.argtypes = [p, p, p, i64, i64, p]
 lib.prism_quantize_rows_static.restype = i32
 lib.prism_quantize_rows_static.argtypes = [p, p, p, ctypes.c_float, i64, i64, p]
+lib.prism_repack_q8_0.restype = i32
+lib.prism_repack_q8_0.argtypes = [p, p, p, i64, i64, p]
 for n in ("prism_gemm_w8a8", "prism_gemm_w8a8_blockscale", "prism_gemm_w4a8"):
     getattr(lib, n).restype = i32
     getattr(lib, n).argtypes = [p, p, p, p, p, p, i64, i64, i64, p]
@@ -131,6 +133,22 @@ CASES += [
     (_QS, [A + 4, A, A, 1.0, 4, 64, None], ALIGN),
     (_QS, [A, A + 8, A, 1.0, 4, 64, None], ALIGN),
     (_QS, [A, A, A + 2, 1.0, 4, 64, None], ALIGN),
+]
+_RP = "prism_repack_q8_0"
+CASES += [
+    (_RP, [A, A, A, 0, 64, None], OK),                  # N = 0: no-op
+    (_RP, [None, None, None, 0, 0, None], OK),
+    (_RP, [A, A, A, -1, 64, None], INVALID),
+    (_RP, [A, A, A, 4, -32, None], INVALID),
+    (_RP, [A, A, A, 4, 0, None], INVALID),
+    (_RP, [A, A, A, 1 << 31, 64, None], INVALID),
+    (_RP, [None, A, A, 4, 64, None], INVALID),
+    (_RP, [A, None, A, 4, 64, None], INVALID),
+    (_RP, [A, A, None, 4, 64, None], INVALID),
+    (_RP, [A, A, A, 4, 48, None], ALIGN),               # K % 32
+    (_RP, [A + 4, A, A, 4, 64, None], ALIGN),
+    (_RP, [A, A + 8, A, 4, 64, None], ALIGN),
+    (_RP, [A, A, A + 1, 4, 64, None], ALIGN),
 ]
 for fn, kmul in (("prism_gemm_w8a8", 16), ("prism_gemm_w4a8", 32), ("prism_gemm_w8a8_blockscale", 32)):
     CASES += [
@@ -197,11 +215,12 @@ def test_valid_call_without_a_device_is_unsupported(built):
     """Valid arguments with no visible device: the device check answers, nothing launches."""
     env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", CUDA_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1")
     payload = json.dumps([["prism_gemm_w8a8", _g()], ["prism_quantize_rows", [A, A, A, 4, 64, None]],
-                          ["prism_quantize_rows_static", [A, A, A, 0.25, 4, 64, None]]])
+                          ["prism_quantize_rows_static", [A, A, A, 0.25, 4, 64, None]],
+                          ["prism_repack_q8_0", [A, A, A, 4, 64, None]]])
     out = subprocess.run([sys.executable, "-c", _CHILD, built, payload], env=env, capture_output=True, text=True,
                          timeout=120)
     assert out.returncode == 0, out.stderr
-    assert json.loads(out.stdout.strip().splitlines()[-1])["status"] == [UNSUP, UNSUP, UNSUP]
+    assert json.loads(out.stdout.strip().splitlines()[-1])["status"] == [UNSUP, UNSUP, UNSUP, UNSUP]
 
 
 def test_build_uses_result_defining_flags():

@@ -126,6 +126,41 @@ def test_static_quantize_bad_scale_raises_and_writes_nothing(bad):
     assert (host(q) == 5).all() and (host(s) == 9.0).all()
 
 
+# ------------------------------------------------------------------ Q8_0 blocks
+
+@pytest.mark.parametrize("N,K", [(1, 32), (3, 96), (255, 32), (257, 32), (7, 1056), (100, 5120), (17408, 5120)])
+def test_repack_q8_0(N, K):
+    """Random bytes (any bit pattern is a valid block): every output byte must equal the oracle's."""
+    rng = np.random.default_rng(N * 31 + K)
+    blocks = rng.integers(0, 256, N * (K // 32) * 34, dtype=np.uint8)
+    w_ref, d_ref = oracle.repack_q8_0(blocks, N, K)
+    w, d = prism.repack_q8_0(dev(blocks), N, K)
+    torch.cuda.synchronize()
+    assert_same_ints(host(w), w_ref, "codes")
+    assert_same_ints(host(d).view(np.uint16), d_ref, "scales")
+
+
+def test_repack_q8_0_then_blockscale_gemm():
+    """Q8_0 file bytes -> repack -> block-scale GEMM, against the oracle on the same bytes."""
+    rng = np.random.default_rng(91)
+    M, N, K = 65, 300, 1056
+    w = wl.int8_weights(rng, N, K)
+    dbits = wl.block_scale_bits(rng, N, K // 32)
+    blocks = np.empty((N, K // 32, 34), np.uint8)
+    blocks[:, :, 0:2] = dbits.astype("<u2").view(np.uint8).reshape(N, K // 32, 2)
+    blocks[:, :, 2:] = w.reshape(N, K // 32, 32).view(np.uint8)
+    blocks = blocks.reshape(-1)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    q_ref, sa_ref = oracle.quantize_rows(x)
+    w_ref, d_ref = oracle.repack_q8_0(blocks, N, K)
+    y_ref, _ = oracle.gemm_w8a8_blockscale(q_ref, sa_ref, w_ref, d_ref, False)
+    q, sa = prism.quantize_rows(dev(x))
+    wg, dg = prism.repack_q8_0(dev(blocks), N, K)
+    y = prism.gemm_w8a8_blockscale(q, sa, wg, dg)
+    torch.cuda.synchronize()
+    assert_same_floats(host(y), y_ref, "y")
+
+
 # ------------------------------------------------------------------ GEMMs
 
 def _case(seed, M, N, K, kind):

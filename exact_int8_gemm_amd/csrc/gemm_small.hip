@@ -207,7 +207,33 @@ void pick_mb(const int8_t* q, const float* s_a, const int8_t* w, const float* s_
   else pick_cb<4, W4>(q, s_a, w, s_w, y, acc, M, N, K, st);
 }
 
+template <bool W4>
+bool pick_variant(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc,
+                  int M, int N, int K, int cb, int waves, hipStream_t st) {
+#define PRISM_SMALL_CASE(MB)                                                                              \
+  if (cb == 1 && waves == 4) launch_small<MB, 1, W4, 4>(q, s_a, w, s_w, y, acc, M, N, K, st);           \
+  else if (cb == 1 && waves == 8) launch_small<MB, 1, W4, 8>(q, s_a, w, s_w, y, acc, M, N, K, st);      \
+  else if (cb == 1 && waves == 16) launch_small<MB, 1, W4, 16>(q, s_a, w, s_w, y, acc, M, N, K, st);    \
+  else if (cb == 2 && waves == 4) launch_small<MB, 2, W4, 4>(q, s_a, w, s_w, y, acc, M, N, K, st);      \
+  else if (cb == 2 && waves == 8) launch_small<MB, 2, W4, 8>(q, s_a, w, s_w, y, acc, M, N, K, st);      \
+  else if (cb == 2 && waves == 16) launch_small<MB, 2, W4, 16>(q, s_a, w, s_w, y, acc, M, N, K, st);    \
+  else return false;
+  if (M <= 16) { PRISM_SMALL_CASE(1) }
+  else if (M <= 32) { PRISM_SMALL_CASE(2) }
+  else { PRISM_SMALL_CASE(4) }
+#undef PRISM_SMALL_CASE
+  return true;
+}
+
 }  // namespace
+
+int launch_gemm_small_variant(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
+                              float* y, int32_t* acc, int M, int N, int K, int cb, int waves, hipStream_t st) {
+  const int8_t* wb = static_cast<const int8_t*>(w);
+  const bool ok = w_is_int4 ? pick_variant<true>(q, s_a, wb, s_w, y, acc, M, N, K, cb, waves, st)
+                            : pick_variant<false>(q, s_a, wb, s_w, y, acc, M, N, K, cb, waves, st);
+  return ok ? launch_status() : PRISM_ERR_INVALID_ARG;
+}
 
 int launch_gemm_small(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
                       float* y, int32_t* acc, int M, int N, int K, hipStream_t st) {

@@ -48,6 +48,31 @@ void pick_int4(const int8_t* q, const float* s_a, const int8_t* w, const float* 
 
 }  // namespace
 
+// One named entry of the table above (7: 256 x 256, 8: 256 x 128, 9..12:
+// 128 x 128 with K split over 1..4 workgroups; the 4-bit path has only 9).
+int launch_gemm_tiled_variant(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
+                              float* y, int32_t* acc, int M, int N, int K, int variant, hipStream_t st) {
+  const int8_t* wb = static_cast<const int8_t*>(w);
+  if (w_is_int4) {
+    if (variant != 9) return PRISM_ERR_INVALID_ARG;
+    pick_int4(q, s_a, wb, s_w, y, acc, M, N, K, st);
+    return launch_status();
+  }
+  if (variant == 7) {
+    tiled::dma::launch<256, 256, 128, 4, 2, 2, 1>(q, s_a, wb, s_w, y, acc, M, N, K, st);
+  } else if (variant == 8) {
+    tiled::dma::launch<256, 128, 128, 4, 2, 3, 1>(q, s_a, wb, s_w, y, acc, M, N, K, st);
+  } else if (variant >= 9 && variant <= 12) {
+    const int stages = (K + 127) / 128;
+    int splits = variant - 8;
+    if (splits > stages) splits = stages;
+    tiled::dma::launch<128, 128, 128, 2, 2, 4, 1>(q, s_a, wb, s_w, y, acc, M, N, K, st, splits);
+  } else {
+    return PRISM_ERR_INVALID_ARG;
+  }
+  return launch_status();
+}
+
 int launch_gemm_tiled(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w, float* y,
                       int32_t* acc, int M, int N, int K, hipStream_t st) {
   const int8_t* wb = static_cast<const int8_t*>(w);

@@ -65,6 +65,25 @@ int check_gemm(const void* q, const void* s_a, const void* w, const void* scale_
 // Grid limits of the tiled kernels (128 x 128 tiles at the smallest).
 bool grid_fits(int64_t M, int64_t N) { return ((M + 127) / 128) * ((N + 127) / 128) <= INT_MAX; }
 
+// Variant dispatch shared by the two _variant calls (arguments already checked).
+int run_variant(const int8_t* q, const float* s_a, const void* w, bool w4, const float* s_w, float* y, int32_t* acc,
+                int64_t M, int64_t N, int64_t K, int variant, hipStream_t s) {
+  static const int kSmall[7][2] = {{0, 0}, {1, 4}, {1, 8}, {1, 16}, {2, 4}, {2, 8}, {2, 16}};
+  if (variant == PRISM_VARIANT_AUTO) {
+    if (M <= prism::kSmallMMax) return prism::launch_gemm_small(q, s_a, w, w4, s_w, y, acc, (int)M, (int)N, (int)K, s);
+    return prism::launch_gemm_tiled(q, s_a, w, w4, s_w, y, acc, (int)M, (int)N, (int)K, s);
+  }
+  if (variant >= PRISM_VARIANT_SMALL_1x4 && variant <= PRISM_VARIANT_SMALL_2x16) {
+    if (M > prism::kSmallMMax) return PRISM_ERR_INVALID_ARG;
+    return prism::launch_gemm_small_variant(q, s_a, w, w4, s_w, y, acc, (int)M, (int)N, (int)K, kSmall[variant][0],
+                                            kSmall[variant][1], s);
+  }
+  if (variant >= PRISM_VARIANT_TILE_256x256 && variant < PRISM_VARIANT_COUNT)
+    return prism::launch_gemm_tiled_variant(q, s_a, w, w4, s_w, y, acc, (int)M, (int)N, (int)K, variant, s);
+  return PRISM_ERR_INVALID_ARG;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -142,6 +161,30 @@ int prism_gemm_w4a8(const int8_t* q, const float* s_a, const uint8_t* w4, const 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (M <= prism::kSmallMMax) return prism::launch_gemm_small(q, s_a, w4, true, s_w, y, acc, (int)M, (int)N, (int)K, s);
   return prism::launch_gemm_tiled(q, s_a, w4, true, s_w, y, acc, (int)M, (int)N, (int)K, s);
+}
+
+int prism_gemm_w8a8_variant(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y,
+                            int32_t* acc, int64_t M, int64_t N, int64_t K, int variant, void* stream) {
+  if (variant < 0 || variant >= PRISM_VARIANT_COUNT) return PRISM_ERR_INVALID_ARG;
+  bool noop;
+  int st = check_gemm(q, s_a, w, s_w, y, acc, M, N, K, 16, &noop);
+  if (st != PRISM_OK || noop) return st;
+  if (!aligned(s_w, 4)) return PRISM_ERR_ALIGNMENT;
+  if (!grid_fits(M, N)) return PRISM_ERR_INVALID_ARG;
+  if ((st = check_device()) != PRISM_OK) return st;
+  return run_variant(q, s_a, w, false, s_w, y, acc, M, N, K, variant, static_cast<hipStream_t>(stream));
+}
+
+int prism_gemm_w4a8_variant(const int8_t* q, const float* s_a, const uint8_t* w4, const float* s_w, float* y,
+                            int32_t* acc, int64_t M, int64_t N, int64_t K, int variant, void* stream) {
+  if (variant < 0 || variant >= PRISM_VARIANT_COUNT) return PRISM_ERR_INVALID_ARG;
+  bool noop;
+  int st = check_gemm(q, s_a, w4, s_w, y, acc, M, N, K, 32, &noop);
+  if (st != PRISM_OK || noop) return st;
+  if (!aligned(s_w, 4)) return PRISM_ERR_ALIGNMENT;
+  if (!grid_fits(M, N)) return PRISM_ERR_INVALID_ARG;
+  if ((st = check_device()) != PRISM_OK) return st;
+  return run_variant(q, s_a, w4, true, s_w, y, acc, M, N, K, variant, static_cast<hipStream_t>(stream));
 }
 
 int prism_gemm_w8a8_blockscale(const int8_t* q, const float* s_a, const int8_t* w, const uint16_t* d, float* y,

@@ -29,6 +29,10 @@ int launch_gemm_small(const int8_t* q, const float* s_a, const void* w, bool w_i
 int launch_gemm_tiled(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
                       float* y, int32_t* acc, int M, int N, int K, hipStream_t st);
 
+int launch_gemm_small_variant(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
+                              float* y, int32_t* acc, int M, int N, int K, int cb, int waves, hipStream_t st);
+int launch_gemm_tiled_variant(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
+                              float* y, int32_t* acc, int M, int N, int K, int variant, hipStream_t st);
 int launch_gemm_blockscale(const int8_t* q, const float* s_a, const int8_t* w, const uint16_t* d, float* y,
                            int32_t* partials, int M, int N, int K, hipStream_t st);
 

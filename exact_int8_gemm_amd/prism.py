@@ -21,6 +21,11 @@ PRISM_OK = 0
 ABI_VERSION = 2
 K_MAX = 131040
 
+# Dispatch-table entries of the W8A8 / W4A8 calls (PRISM_VARIANT_* in include/prism.h).
+VARIANTS = {"auto": 0, "small_1x4": 1, "small_1x8": 2, "small_1x16": 3, "small_2x4": 4, "small_2x8": 5,
+            "small_2x16": 6, "tile_256x256": 7, "tile_256x128": 8, "tile_128x128": 9, "tile_128x128_split2": 10,
+            "tile_128x128_split3": 11, "tile_128x128_split4": 12}
+
 
 class PrismError(RuntimeError):
     def __init__(self, status: int, text: str):
@@ -43,6 +48,10 @@ def _declare(lib):
     lib.prism_quantize_rows_static.argtypes = [p, p, p, ctypes.c_float, i64, i64, p]
     lib.prism_repack_q8_0.restype = i32
     lib.prism_repack_q8_0.argtypes = [p, p, p, i64, i64, p]
+    for name in ("prism_gemm_w8a8_variant", "prism_gemm_w4a8_variant"):
+        fn = getattr(lib, name)
+        fn.restype = i32
+        fn.argtypes = [p, p, p, p, p, p, i64, i64, i64, i32, p]
     for name in ("prism_gemm_w8a8", "prism_gemm_w8a8_blockscale", "prism_gemm_w4a8"):
         fn = getattr(lib, name)
         fn.restype = i32
@@ -173,6 +182,32 @@ def gemm_w8a8(q, s_a, w, s_w, y=None, acc=None):
     with torch.cuda.device(dev):
         _check(lib().prism_gemm_w8a8(_ptr(q), _ptr(s_a), _ptr(w), _ptr(s_w), _ptr(y), _ptr(acc), M, N, K,
                                      _stream(dev)))
+    return y
+
+
+def gemm_w8a8_variant(q, s_a, w, s_w, variant, y=None, acc=None):
+    """gemm_w8a8 through one named dispatch-table entry (``VARIANTS``); for verifying that every
+    entry gives the same bits."""
+    dev, M, N, K = _gemm_args(q, s_a, w, lambda k: k, torch.int8, "s_w", s_w, torch.float32, lambda n, k: (n,))
+    y = torch.empty((M, N), dtype=torch.float32, device=dev) if y is None else _need(y, "y", torch.float32, (M, N), dev)
+    if acc is not None:
+        _need(acc, "acc", torch.int32, (M, N), dev)
+    with torch.cuda.device(dev):
+        _check(lib().prism_gemm_w8a8_variant(_ptr(q), _ptr(s_a), _ptr(w), _ptr(s_w), _ptr(y), _ptr(acc), M, N, K,
+                                             VARIANTS[variant], _stream(dev)))
+    return y
+
+
+def gemm_w4a8_variant(q, s_a, w4, s_w, variant, y=None, acc=None):
+    """gemm_w4a8 through one named dispatch-table entry (``VARIANTS``)."""
+    dev, M, N, K = _gemm_args(q, s_a, w4, lambda k: k // 2, torch.uint8, "s_w", s_w, torch.float32,
+                              lambda n, k: (n,))
+    y = torch.empty((M, N), dtype=torch.float32, device=dev) if y is None else _need(y, "y", torch.float32, (M, N), dev)
+    if acc is not None:
+        _need(acc, "acc", torch.int32, (M, N), dev)
+    with torch.cuda.device(dev):
+        _check(lib().prism_gemm_w4a8_variant(_ptr(q), _ptr(s_a), _ptr(w4), _ptr(s_w), _ptr(y), _ptr(acc), M, N, K,
+                                             VARIANTS[variant], _stream(dev)))
     return y
 
 

@@ -153,6 +153,46 @@ int prism_gemm_w8a8_blockscale(const int8_t* q, const float* s_a, const int8_t* 
 int prism_gemm_w4a8(const int8_t* q, const float* s_a, const uint8_t* w4, const float* s_w,
                     float* y, int32_t* acc, int64_t M, int64_t N, int64_t K, void* stream);
 
+/*
+ * The shape-dependent kernel choice of prism_gemm_w8a8 / prism_gemm_w4a8,
+ * one entry at a time (README "Why StartLux-Prism": kernels are picked per
+ * GPU from measured tables; that is safe here because every entry computes
+ * the same exact int32 sums and the same per-element epilogue).  These calls
+ * exist to verify that claim: the result of every applicable variant is bit
+ * for bit the result of PRISM_VARIANT_AUTO, which is what the plain calls run.
+ * Same arguments and checks as the plain calls, plus `variant`:
+ *   PRISM_VARIANT_AUTO            the plain call's choice;
+ *   PRISM_VARIANT_SMALL_<c>x<w>   the small-M kernel with c column blocks of
+ *                                 16 and w waves per workgroup (M <= 64 only);
+ *   PRISM_VARIANT_TILE_*          the LDS-tiled kernels: 256x256, 256x128 and
+ *                                 128x128 (int8 weights only), and 128x128 with
+ *                                 K split over 2, 3 or 4 workgroups whose exact
+ *                                 int32 partials are added atomically into y
+ *                                 (int8 only); the 4-bit path has TILE_128x128.
+ * A variant that does not apply to the call returns PRISM_ERR_INVALID_ARG.
+ */
+#define PRISM_VARIANT_AUTO 0
+#define PRISM_VARIANT_SMALL_1x4 1
+#define PRISM_VARIANT_SMALL_1x8 2
+#define PRISM_VARIANT_SMALL_1x16 3
+#define PRISM_VARIANT_SMALL_2x4 4
+#define PRISM_VARIANT_SMALL_2x8 5
+#define PRISM_VARIANT_SMALL_2x16 6
+#define PRISM_VARIANT_TILE_256x256 7
+#define PRISM_VARIANT_TILE_256x128 8
+#define PRISM_VARIANT_TILE_128x128 9
+#define PRISM_VARIANT_TILE_128x128_SPLIT2 10
+#define PRISM_VARIANT_TILE_128x128_SPLIT3 11
+#define PRISM_VARIANT_TILE_128x128_SPLIT4 12
+#define PRISM_VARIANT_COUNT 13
+
+int prism_gemm_w8a8_variant(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w,
+                            float* y, int32_t* acc, int64_t M, int64_t N, int64_t K, int variant,
+                            void* stream);
+int prism_gemm_w4a8_variant(const int8_t* q, const float* s_a, const uint8_t* w4, const float* s_w,
+                            float* y, int32_t* acc, int64_t M, int64_t N, int64_t K, int variant,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

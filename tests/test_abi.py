@@ -42,7 +42,7 @@ def built():
 def test_header_declares_every_call():
     names = set(_declared_functions())
     assert {"prism_quantize_rows", "prism_quantize_rows_static", "prism_repack_q8_0", "prism_gemm_w8a8",
-            "prism_gemm_w8a8_blockscale", "prism_gemm_w4a8",
+            "prism_gemm_w8a8_blockscale", "prism_gemm_w4a8", "prism_gemm_w8a8_variant", "prism_gemm_w4a8_variant",
             "prism_abi_version", "prism_status_string"} <= names
 
 
@@ -77,6 +77,9 @@ lib.prism_quantize_rows_static.restype = i32
 lib.prism_quantize_rows_static.argtypes = [p, p, p, ctypes.c_float, i64, i64, p]
 lib.prism_repack_q8_0.restype = i32
 lib.prism_repack_q8_0.argtypes = [p, p, p, i64, i64, p]
+for n in ("prism_gemm_w8a8_variant", "prism_gemm_w4a8_variant"):
+    getattr(lib, n).restype = i32
+    getattr(lib, n).argtypes = [p, p, p, p, p, p, i64, i64, i64, i32, p]
 for n in ("prism_gemm_w8a8", "prism_gemm_w8a8_blockscale", "prism_gemm_w4a8"):
     getattr(lib, n).restype = i32
     getattr(lib, n).argtypes = [p, p, p, p, p, p, i64, i64, i64, p]
@@ -150,6 +153,25 @@ CASES += [
     (_RP, [A, A + 8, A, 4, 64, None], ALIGN),
     (_RP, [A, A, A + 1, 4, 64, None], ALIGN),
 ]
+
+def _v(variant, **kw):
+    a = _g(**kw)
+    return a[:9] + [variant, None]
+
+
+for fn in ("prism_gemm_w8a8_variant", "prism_gemm_w4a8_variant"):
+    CASES += [
+        (fn, _v(-1), INVALID),                 # unknown variant: refused before anything else
+        (fn, _v(13), INVALID),
+        (fn, _v(13, M=0), INVALID),
+        (fn, _v(0, M=0), OK),
+        (fn, _v(3, M=0), OK),
+        (fn, _v(0, q=None), INVALID),
+        (fn, _v(9, K=0), INVALID),
+        (fn, _v(9, K=40), ALIGN),
+        (fn, _v(9, y=A + 2), ALIGN),
+        (fn, _v(9, sw=A + 2), ALIGN),
+    ]
 for fn, kmul in (("prism_gemm_w8a8", 16), ("prism_gemm_w4a8", 32), ("prism_gemm_w8a8_blockscale", 32)):
     CASES += [
         (fn, _g(M=0), OK),
@@ -216,11 +238,12 @@ def test_valid_call_without_a_device_is_unsupported(built):
     env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", CUDA_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1")
     payload = json.dumps([["prism_gemm_w8a8", _g()], ["prism_quantize_rows", [A, A, A, 4, 64, None]],
                           ["prism_quantize_rows_static", [A, A, A, 0.25, 4, 64, None]],
-                          ["prism_repack_q8_0", [A, A, A, 4, 64, None]]])
+                          ["prism_repack_q8_0", [A, A, A, 4, 64, None]],
+                          ["prism_gemm_w8a8_variant", _g()[:9] + [7, None]]])
     out = subprocess.run([sys.executable, "-c", _CHILD, built, payload], env=env, capture_output=True, text=True,
                          timeout=120)
     assert out.returncode == 0, out.stderr
-    assert json.loads(out.stdout.strip().splitlines()[-1])["status"] == [UNSUP, UNSUP, UNSUP, UNSUP]
+    assert json.loads(out.stdout.strip().splitlines()[-1])["status"] == [UNSUP, UNSUP, UNSUP, UNSUP, UNSUP]
 
 
 def test_build_uses_result_defining_flags():
@@ -230,3 +253,12 @@ def test_build_uses_result_defining_flags():
     for flag in ("--offload-arch=gfx950", "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
                  "-fno-gpu-flush-denormals-to-zero", "-packed-fp32-ops"):
         assert flag in cmd, flag
+
+
+def test_variant_table_matches_header():
+    sys.path.insert(0, ROOT)
+    from exact_int8_gemm_amd import prism
+    d = _defines()
+    for name, v in prism.VARIANTS.items():
+        assert d["PRISM_VARIANT_" + name.upper().replace("X", "x")] == v, name
+    assert d["PRISM_VARIANT_COUNT"] == len(prism.VARIANTS)

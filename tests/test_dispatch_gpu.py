@@ -1,0 +1,80 @@
+"""Every entry of the W8A8 / W4A8 dispatch table gives the same bits (GPU).
+
+The plain calls pick a kernel, a tile shape and a K split from (M, N, K).
+That choice may vary with M only because every entry computes the same exact
+int32 sums and the same per-element fp32 epilogue.  Here each applicable
+entry is run on its own through the ``*_variant`` calls and compared with the
+CPU oracle bit for bit; entries that do not apply must be refused.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_int8_gemm_amd import prism
+from exact_int8_gemm_amd import workloads as wl
+from gpu_util import DEV, assert_same_floats, assert_same_ints, dev, host
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["small_1x4", "small_1x8", "small_1x16", "small_2x4", "small_2x8", "small_2x16"]
+TILES8 = ["tile_256x256", "tile_256x128", "tile_128x128", "tile_128x128_split2", "tile_128x128_split3",
+          "tile_128x128_split4"]
+
+
+def _inputs(seed, M, N, K, w4=False):
+    rng = np.random.default_rng(seed)
+    q = rng.integers(-128, 128, (M, K), dtype=np.int8)      # the whole int8 range, -128 included
+    s_a = rng.uniform(1e-3, 1e-2, M).astype(np.float32)
+    s_w = wl.channel_scales(rng, N)
+    if w4:
+        w = rng.integers(-8, 8, (N, K), dtype=np.int8)
+        return q, s_a, wl.pack_int4(w), s_w
+    return q, s_a, wl.int8_weights(rng, N, K), s_w
+
+
+def _run_all(fn, names, q, s_a, w, s_w, y_ref, acc_ref):
+    M, N = y_ref.shape
+    for name in names:
+        acc = torch.full((M, N), 7, dtype=torch.int32, device=DEV)
+        y = torch.full((M, N), 3.0, dtype=torch.float32, device=DEV)
+        fn(q, s_a, w, s_w, name, y=y, acc=acc)
+        torch.cuda.synchronize()
+        assert_same_ints(host(acc), acc_ref, "acc (%s)" % name)
+        assert_same_floats(host(y), y_ref, "y (%s)" % name)
+
+
+@pytest.mark.parametrize("M", [1, 5, 16, 17, 33, 64])
+@pytest.mark.parametrize("N,K", [(100, 160), (300, 2064)])
+def test_w8a8_every_entry_small_m(M, N, K):
+    q, s_a, w, s_w = _inputs(M * 1000 + N + K, M, N, K)
+    y_ref, acc_ref = oracle.gemm_w8a8(q, s_a, w, s_w)
+    _run_all(prism.gemm_w8a8_variant, ["auto"] + SMALL + TILES8, dev(q), dev(s_a), dev(w), dev(s_w), y_ref, acc_ref)
+
+
+@pytest.mark.parametrize("M", [65, 129, 300])
+@pytest.mark.parametrize("N,K", [(100, 160), (257, 4112)])
+def test_w8a8_every_entry_large_m(M, N, K):
+    q, s_a, w, s_w = _inputs(M * 1000 + N + K, M, N, K)
+    y_ref, acc_ref = oracle.gemm_w8a8(q, s_a, w, s_w)
+    qd, sad, wd, swd = dev(q), dev(s_a), dev(w), dev(s_w)
+    _run_all(prism.gemm_w8a8_variant, ["auto"] + TILES8, qd, sad, wd, swd, y_ref, acc_ref)
+    y = torch.full((M, N), 3.0, dtype=torch.float32, device=DEV)
+    for name in SMALL:   # the small-M kernel holds at most 64 rows: refused, nothing written
+        with pytest.raises(prism.PrismError):
+            prism.gemm_w8a8_variant(qd, sad, wd, swd, name, y=y)
+    torch.cuda.synchronize()
+    assert (host(y) == 3.0).all()
+
+
+@pytest.mark.parametrize("M", [1, 16, 33, 64, 65, 200])
+def test_w4a8_every_entry(M):
+    N, K = 300, 1056
+    q, s_a, w4, s_w = _inputs(M * 7 + 1, M, N, K, w4=True)
+    y_ref, acc_ref = oracle.gemm_w4a8(q, s_a, w4, s_w)
+    qd, sad, wd, swd = dev(q), dev(s_a), dev(w4), dev(s_w)
+    names = ["auto", "tile_128x128"] + (SMALL if M <= 64 else [])
+    _run_all(prism.gemm_w4a8_variant, names, qd, sad, wd, swd, y_ref, acc_ref)
+    for name in [n for n in TILES8 if n != "tile_128x128"]:   # int8-only tiles
+        with pytest.raises(prism.PrismError):
+            prism.gemm_w4a8_variant(qd, sad, wd, swd, name)

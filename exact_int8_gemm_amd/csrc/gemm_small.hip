@@ -181,30 +181,32 @@ void launch_small(const int8_t* q, const float* s_a, const int8_t* w, const floa
   gemm_small_kernel<MB, CB, W4, WAVES, U><<<grid, 64 * WAVES, 0, st>>>(q, s_a, w, s_w, y, acc, M, N, K);
 }
 
-template <int MB, int CB, bool W4>
-void pick_waves(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc,
-                int M, int N, int K, hipStream_t st) {
-  // About four 128-k units per wave, between 4 and 16 waves per workgroup.
+// Column blocks per workgroup and waves per workgroup, from a sweep of six
+// (N, K) shapes x M in {1, 16, 33, 64} x both weight formats on MI355X (the
+// README's kernels are likewise picked per GPU from measured tables).  Every
+// choice computes the same exact sums, so this only moves time.
+//  * M <= 32: column blocks chosen so that the workgroups spread evenly over
+//    the 256 CUs (fewest rounds x work per workgroup, ties to two blocks);
+//    4-bit weights take 8 waves once K >= 3072 (four 128-k units per wave),
+//    int8 weights 4 waves up to K = 5120 and 8 above.
+//  * M > 32: two column blocks of 4 waves once N >= 5120 (each activation
+//    fragment then feeds two column blocks), else one block of 16 waves
+//    (N >= 4096) or 8.
+void choose_small(int M, int N, int K, bool w4, int& cb, int& waves) {
   const int64_t nunits = (K + kUnitK - 1) / kUnitK;
-  if (nunits >= 64) launch_small<MB, CB, W4, 16>(q, s_a, w, s_w, y, acc, M, N, K, st);
-  else if (nunits >= 24) launch_small<MB, CB, W4, 8>(q, s_a, w, s_w, y, acc, M, N, K, st);
-  else launch_small<MB, CB, W4, 4>(q, s_a, w, s_w, y, acc, M, N, K, st);
-}
-
-template <int MB, bool W4>
-void pick_cb(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc, int M,
-             int N, int K, hipStream_t st) {
-  // Two column blocks per workgroup when that still leaves one workgroup per CU.
-  if ((N + 31) / 32 >= 256) pick_waves<MB, 2, W4>(q, s_a, w, s_w, y, acc, M, N, K, st);
-  else pick_waves<MB, 1, W4>(q, s_a, w, s_w, y, acc, M, N, K, st);
-}
-
-template <bool W4>
-void pick_mb(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc, int M,
-             int N, int K, hipStream_t st) {
-  if (M <= 16) pick_cb<1, W4>(q, s_a, w, s_w, y, acc, M, N, K, st);
-  else if (M <= 32) pick_cb<2, W4>(q, s_a, w, s_w, y, acc, M, N, K, st);
-  else pick_cb<4, W4>(q, s_a, w, s_w, y, acc, M, N, K, st);
+  if (M <= 32) {
+    const int64_t g1 = (N + 15) / 16, g2 = (N + 31) / 32;
+    const int64_t c1 = (g1 + 255) / 256, c2 = 2 * ((g2 + 255) / 256);
+    cb = c2 <= c1 ? 2 : 1;
+    if (w4) waves = nunits >= 24 ? 8 : 4;
+    else waves = nunits <= 40 ? 4 : 8;
+  } else if (N >= 5120) {
+    cb = 2;
+    waves = 4;
+  } else {
+    cb = 1;
+    waves = N >= 4096 ? 16 : 8;
+  }
 }
 
 template <bool W4>
@@ -237,10 +239,9 @@ int launch_gemm_small_variant(const int8_t* q, const float* s_a, const void* w, 
 
 int launch_gemm_small(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
                       float* y, int32_t* acc, int M, int N, int K, hipStream_t st) {
-  const int8_t* wb = static_cast<const int8_t*>(w);
-  if (w_is_int4) pick_mb<true>(q, s_a, wb, s_w, y, acc, M, N, K, st);
-  else pick_mb<false>(q, s_a, wb, s_w, y, acc, M, N, K, st);
-  return launch_status();
+  int cb, waves;
+  choose_small(M, N, K, w_is_int4, cb, waves);
+  return launch_gemm_small_variant(q, s_a, w, w_is_int4, s_w, y, acc, M, N, K, cb, waves, st);
 }
 
 }  // namespace prism

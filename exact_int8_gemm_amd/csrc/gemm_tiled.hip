@@ -12,26 +12,31 @@ using tiled::launch_tiled;
 
 inline int64_t tiles(int64_t M, int64_t N, int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
 
-// int8 weights: direct-to-LDS pipelines (gemm_tiled_kernels.h, namespace dma),
-// chosen by how many tiles of each shape the problem has (measured on
-// MI355X for the 4B-class prefill projections and M = 2048 / 8192 shapes):
-//  * 256 x 256 tiles (8 waves of 64 x 128, 128-byte stages, 2-deep ring)
-//    once they give every CU a tile;
-//  * 256 x 128 tiles (8 waves of 64 x 64, 3-deep ring) when those still give
-//    at least half of the CUs a tile;
-//  * 128 x 128 tiles (4 waves of 64 x 64, 4-deep ring) otherwise, with K
-//    split over floor(256 / tiles) workgroups per tile (at most 4, at least 8
-//    stages each) whose exact int32 partial tiles are added atomically.
+// int8 weights: direct-to-LDS pipelines (gemm_tiled_kernels.h, namespace dma).
+// A launch runs in waves of up to 256 tiles (one per CU), so its time is
+// about ceil(tiles / 256) times the time of one wave of tiles.  Per wave, a
+// 256 x 128 tile takes 0.60 and a 128 x 128 tile 0.45 of the time of a
+// 256 x 256 tile (measured on MI355X at M = 8192 for three (N, K) shapes);
+// the shape with the smallest estimate wins, ties to the larger tile:
+//  * 256 x 256 tiles: 8 waves of 64 x 128, 128-byte stages, 2-deep ring;
+//  * 256 x 128 tiles: 8 waves of 64 x 64, 3-deep ring;
+//  * 128 x 128 tiles: 4 waves of 64 x 64, 4-deep ring, with K split over
+//    floor(256 / tiles) workgroups per tile (at most 4, at least 8 stages
+//    each) whose exact int32 partial tiles are added atomically.
+// A sweep of M from 65 to 8192 on four projection shapes puts this choice
+// within 8% of the fastest entry of the table everywhere.
 void pick_int8(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc, int M,
                int N, int K, hipStream_t st) {
-  if (tiles(M, N, 256, 256) >= 256) {
+  const int64_t t1 = tiles(M, N, 256, 256), t2 = tiles(M, N, 256, 128), t3 = tiles(M, N, 128, 128);
+  const double c1 = (double)((t1 + 255) / 256), c2 = 0.60 * (double)((t2 + 255) / 256),
+               c3 = 0.45 * (double)((t3 + 255) / 256);
+  if (c1 <= c2 && c1 <= c3) {
     tiled::dma::launch<256, 256, 128, 4, 2, 2, 1>(q, s_a, w, s_w, y, acc, M, N, K, st);
-  } else if (tiles(M, N, 256, 128) >= 128) {
+  } else if (c2 <= c3) {
     tiled::dma::launch<256, 128, 128, 4, 2, 3, 1>(q, s_a, w, s_w, y, acc, M, N, K, st);
   } else {
-    const int64_t t = tiles(M, N, 128, 128);
     const int64_t stages = (K + 127) / 128;
-    int64_t splits = 256 / t;
+    int64_t splits = 256 / t3;
     if (splits > 4) splits = 4;
     if (splits > stages / 8) splits = stages / 8;
     if (splits < 1) splits = 1;

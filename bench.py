@@ -261,8 +261,9 @@ def kernels(torch, prism, wl, only=None):
         R = _copies(c["w4"].nbytes)
         ws = [T(c["w4"]) for _ in range(R)]
         sw = T(c["s_w"])
-        for M in (1, 4, 16, 64):
-            x = T(c["x"][:M].copy())
+        for M in (1, 4, 16, 64, 512, 2048):
+            # M > 64 (prefill, tiled path): the 64 seeded rows repeated (values do not change timing)
+            x = T(c["x"][:M].copy() if M <= 64 else c["x"][[i % 64 for i in range(M)]])
             q = torch.empty((M, K), dtype=torch.int8, device=dev)
             sa = torch.empty((M,), dtype=torch.float32, device=dev)
             _check(L.quantize(x, q, sa)())

@@ -12,6 +12,17 @@ using tiled::launch_tiled;
 
 inline int64_t tiles(int64_t M, int64_t N, int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
 
+// K split of a 128 x 128 launch with t tiles: floor(256 / t) workgroups per
+// tile, at most 4, each with at least 8 stages of 128 k.
+int split_for(int64_t t, int K) {
+  const int64_t stages = (K + 127) / 128;
+  int64_t splits = 256 / t;
+  if (splits > 4) splits = 4;
+  if (splits > stages / 8) splits = stages / 8;
+  if (splits < 1) splits = 1;
+  return (int)splits;
+}
+
 // int8 weights: direct-to-LDS pipelines (gemm_tiled_kernels.h, namespace dma).
 // A launch runs in waves of up to 256 tiles (one per CU), so its time is
 // about ceil(tiles / 256) times the time of one wave of tiles.  Per wave, a
@@ -35,32 +46,33 @@ void pick_int8(const int8_t* q, const float* s_a, const int8_t* w, const float* 
   } else if (c2 <= c3) {
     tiled::dma::launch<256, 128, 128, 4, 2, 3, 1>(q, s_a, w, s_w, y, acc, M, N, K, st);
   } else {
-    const int64_t stages = (K + 127) / 128;
-    int64_t splits = 256 / t3;
-    if (splits > 4) splits = 4;
-    if (splits > stages / 8) splits = stages / 8;
-    if (splits < 1) splits = 1;
-    tiled::dma::launch<128, 128, 128, 2, 2, 4, 1>(q, s_a, w, s_w, y, acc, M, N, K, st, (int)splits);
+    tiled::dma::launch<128, 128, 128, 2, 2, 4, 1>(q, s_a, w, s_w, y, acc, M, N, K, st, split_for(t3, K));
   }
 }
 
 // 4-bit weights: register-staged pipeline that unpacks the nibbles on their
-// way into LDS.
+// way into LDS; 128 x 128 tiles, with K split as for the int8 128 x 128 tiles
+// when there are fewer tiles than CUs.
+
 void pick_int4(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc, int M,
                int N, int K, hipStream_t st) {
-  launch_tiled<128, 128, 128, 2, 2, true, 2>(q, s_a, w, s_w, y, acc, M, N, K, st);
+  launch_tiled<128, 128, 128, 2, 2, true, 2>(q, s_a, w, s_w, y, acc, M, N, K, st,
+                                              split_for(tiles(M, N, 128, 128), K));
 }
 
 }  // namespace
 
 // One named entry of the table above (7: 256 x 256, 8: 256 x 128, 9..12:
-// 128 x 128 with K split over 1..4 workgroups; the 4-bit path has only 9).
+// 128 x 128 with K split over 1..4 workgroups; the 4-bit path has 9..12).
 int launch_gemm_tiled_variant(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
                               float* y, int32_t* acc, int M, int N, int K, int variant, hipStream_t st) {
   const int8_t* wb = static_cast<const int8_t*>(w);
   if (w_is_int4) {
-    if (variant != 9) return PRISM_ERR_INVALID_ARG;
-    pick_int4(q, s_a, wb, s_w, y, acc, M, N, K, st);
+    if (variant < 9 || variant > 12) return PRISM_ERR_INVALID_ARG;
+    const int stages = (K + 127) / 128;
+    int splits = variant - 8;
+    if (splits > stages) splits = stages;
+    launch_tiled<128, 128, 128, 2, 2, true, 2>(q, s_a, wb, s_w, y, acc, M, N, K, st, splits);
     return launch_status();
   }
   if (variant == 7) {

@@ -248,6 +248,10 @@ __device__ inline void mma_stage(const int8_t* lds, int wm, int wn, int lane,
   }
 }
 
+// splits > 1: as in the direct-to-LDS kernel below, workgroup (tile, split)
+// sums one contiguous range of stages and adds its partial tile into y
+// viewed as int32 (4-bit: each partial is a multiple of 16 on its own and is
+// shifted back before the add, so the sum needs no further step).
 template <int BM, int BN, int BK, int WM, int WN, bool W4, int OCC>
 __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_tiled_kernel(const int8_t* __restrict__ q,
                                                                        const float* __restrict__ s_a,
@@ -255,12 +259,12 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_tiled_kernel(const int
                                                                        const float* __restrict__ s_w,
                                                                        float* __restrict__ y,
                                                                        int32_t* __restrict__ acc_out, int M, int N,
-                                                                       int K, int tiles_m, int tiles_n) {
+                                                                       int K, int tiles_m, int tiles_n, int splits) {
   using G = Geometry<BM, BN, BK, WM, WN>;
   __shared__ __attribute__((aligned(16))) int8_t lds[2][G::kLds];
 
-  int tm, tn;
-  tile_of(tiles_m, tiles_n, tm, tn);
+  int tm, tn, split;
+  tile_of_split(tiles_m, tiles_n, splits, tm, tn, split);
   const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -274,28 +278,32 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_tiled_kernel(const int
   StageAddr<BM, BN, BK, G::kNT, W4> ad;
   ad.init(q, w, m0, n0, M, N, K);
   Stage<BM, BN, BK, G::kNT, W4> s0, s1;
+  // This split's stages [kb, ke); loads are bounded by kend, so stages past
+  // ke read zeros instead of another split's k.
   const int nk = (K + BK - 1) / BK;
+  const int kb = (int)((int64_t)split * nk / splits), ke = (int)((int64_t)(split + 1) * nk / splits);
+  const int kend = ke * BK < K ? ke * BK : K;
   auto mma = [&](int buf) __attribute__((always_inline)) { mma_stage<BM, BN, BK, WM, WN>(lds[buf], wm, wn, lane, acc); };
 
   // Pipeline: stage k is in LDS buffer k % 2, stage k+1 waits in a register
   // set, stage k+2 is being loaded into the other set.  The stage count is
-  // rounded up to even: stages at or past K load as zeros (every chunk is out
-  // of range), so the loop needs no tail and no conditions.
-  ad.load(s0, 0, K);
-  ad.load(s1, BK, K);
+  // rounded up to even: stages at or past kend load as zeros (every chunk is
+  // out of range), so the loop needs no tail and no conditions.
+  ad.load(s0, kb * BK, kend);
+  ad.load(s1, (kb + 1) * BK, kend);
   ad.store(s0, lds[0]);
   __syncthreads();
   // The scheduling barriers keep the global loads of a stage ahead of the
   // MFMAs (so they have two stages of work to arrive) and the LDS writes of
   // the waiting stage behind them.
-  for (int k = 0; k < nk; k += 2) {
-    ad.load(s0, (k + 2) * BK, K);
+  for (int k = kb; k < ke; k += 2) {
+    ad.load(s0, (k + 2) * BK, kend);
     __builtin_amdgcn_sched_barrier(0);
     mma(0);
     __builtin_amdgcn_sched_barrier(0);
     ad.store(s1, lds[1]);
     __syncthreads();
-    ad.load(s1, (k + 3) * BK, K);
+    ad.load(s1, (k + 3) * BK, kend);
     __builtin_amdgcn_sched_barrier(0);
     mma(1);
     __builtin_amdgcn_sched_barrier(0);
@@ -304,6 +312,25 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_tiled_kernel(const int
   }
 
   const int rl = lane & 31;
+  if (splits > 1) {
+    int32_t* yi = reinterpret_cast<int32_t*>(y);
+#pragma unroll
+    for (int j = 0; j < G::kTN; ++j) {
+      const int n = n0 + wn * G::kWTN + j * 32 + rl;
+      if (n >= N) continue;
+#pragma unroll
+      for (int i = 0; i < G::kTM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm * G::kWTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const int a = W4 ? (acc[i][j][r] >> 4) : acc[i][j][r];  // exact: each 4-bit partial is a multiple of 16
+          if (m < M)
+            __hip_atomic_fetch_add(yi + (size_t)m * (size_t)N + (size_t)n, a, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < G::kTN; ++j) {
     const int n = n0 + wn * G::kWTN + j * 32 + rl;
@@ -851,10 +878,14 @@ void launch_block(const int8_t* q, const float* s_a, const int8_t* w, const uint
 
 template <int BM, int BN, int BK, int WM, int WN, bool W4, int OCC>
 void launch_tiled(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc,
-                  int M, int N, int K, hipStream_t st) {
+                  int M, int N, int K, hipStream_t st, int splits = 1) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  gemm_tiled_kernel<BM, BN, BK, WM, WN, W4, OCC>
-      <<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, 0, st>>>(q, s_a, w, s_w, y, acc, M, N, K, tiles_m, tiles_n);
+  const int64_t total = (int64_t)M * N;
+  if (splits > 1)
+    dma::zero_kernel<<<(unsigned)((total + 1023) / 1024), 256, 0, st>>>(reinterpret_cast<int32_t*>(y), total);
+  gemm_tiled_kernel<BM, BN, BK, WM, WN, W4, OCC><<<(unsigned)(tiles_m * tiles_n * splits), 64 * WM * WN, 0, st>>>(
+      q, s_a, w, s_w, y, acc, M, N, K, tiles_m, tiles_n, splits);
+  if (splits > 1) dma::finalize_kernel<<<(unsigned)((total + 1023) / 1024), 256, 0, st>>>(y, acc, s_a, s_w, M, N);
 }
 
 }  // namespace tiled

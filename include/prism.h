@@ -164,11 +164,10 @@ int prism_gemm_w4a8(const int8_t* q, const float* s_a, const uint8_t* w4, const 
  *   PRISM_VARIANT_AUTO            the plain call's choice;
  *   PRISM_VARIANT_SMALL_<c>x<w>   the small-M kernel with c column blocks of
  *                                 16 and w waves per workgroup (M <= 64 only);
- *   PRISM_VARIANT_TILE_*          the LDS-tiled kernels: 256x256, 256x128 and
- *                                 128x128 (int8 weights only), and 128x128 with
+ *   PRISM_VARIANT_TILE_*          the LDS-tiled kernels: 256x256 and 256x128
+ *                                 (int8 weights only), 128x128, and 128x128 with
  *                                 K split over 2, 3 or 4 workgroups whose exact
- *                                 int32 partials are added atomically into y
- *                                 (int8 only); the 4-bit path has TILE_128x128.
+ *                                 int32 partials are added atomically into y.
  * A variant that does not apply to the call returns PRISM_ERR_INVALID_ARG.
  */
 #define PRISM_VARIANT_AUTO 0

@@ -20,6 +20,7 @@ pytestmark = pytest.mark.gpu
 SMALL = ["small_1x4", "small_1x8", "small_1x16", "small_2x4", "small_2x8", "small_2x16"]
 TILES8 = ["tile_256x256", "tile_256x128", "tile_128x128", "tile_128x128_split2", "tile_128x128_split3",
           "tile_128x128_split4"]
+TILES4 = ["tile_128x128", "tile_128x128_split2", "tile_128x128_split3", "tile_128x128_split4"]
 
 
 def _inputs(seed, M, N, K, w4=False):
@@ -68,13 +69,13 @@ def test_w8a8_every_entry_large_m(M, N, K):
 
 
 @pytest.mark.parametrize("M", [1, 16, 33, 64, 65, 200])
-def test_w4a8_every_entry(M):
-    N, K = 300, 1056
+@pytest.mark.parametrize("N,K", [(300, 1056), (130, 4128)])
+def test_w4a8_every_entry(M, N, K):
     q, s_a, w4, s_w = _inputs(M * 7 + 1, M, N, K, w4=True)
     y_ref, acc_ref = oracle.gemm_w4a8(q, s_a, w4, s_w)
     qd, sad, wd, swd = dev(q), dev(s_a), dev(w4), dev(s_w)
-    names = ["auto", "tile_128x128"] + (SMALL if M <= 64 else [])
+    names = ["auto"] + TILES4 + (SMALL if M <= 64 else [])
     _run_all(prism.gemm_w4a8_variant, names, qd, sad, wd, swd, y_ref, acc_ref)
-    for name in [n for n in TILES8 if n != "tile_128x128"]:   # int8-only tiles
+    for name in [n for n in TILES8 if n not in TILES4]:   # int8-only tiles
         with pytest.raises(prism.PrismError):
             prism.gemm_w4a8_variant(qd, sad, wd, swd, name)

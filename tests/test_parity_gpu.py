@@ -317,6 +317,18 @@ def test_invalid_shapes_raise_before_launch():
     assert e.value.status == -2
 
 
+@pytest.mark.parametrize("M,N,K", [(65, 130, 2080), (129, 257, 4128), (100, 2560, 9728)])
+def test_w4a8_split_k(M, N, K):
+    """The 4-bit tiled path splits K the same way; each partial is shifted back from 16 w exactly."""
+    c, q, s_a = _case(8, M, N, K, "w4a8")
+    y_ref, acc_ref = oracle.gemm_w4a8(q, s_a, c["w4"], c["s_w"])
+    acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    y = prism.gemm_w4a8(dev(q), dev(s_a), dev(c["w4"]), dev(c["s_w"]), acc=acc)
+    torch.cuda.synchronize()
+    assert_same_ints(host(acc), acc_ref, "acc")
+    assert_same_floats(host(y), y_ref, "y")
+
+
 @pytest.mark.parametrize("M,N,K", [(65, 130, 2064), (200, 300, 4096), (129, 257, 4112), (100, 2560, 9728)])
 def test_w8a8_split_k(M, N, K):
     """Few output tiles and a long K: the tiled path splits K over several

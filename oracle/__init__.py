@@ -58,6 +58,10 @@ def bind(lib):
     lib.oracle_quantize_rows_static.argtypes = [p, p, p, ctypes.c_float, i64, i64]
     lib.oracle_repack_q8_0.restype = ctypes.c_int
     lib.oracle_repack_q8_0.argtypes = [p, p, p, i64, i64]
+    lib.oracle_repack_q4_k.restype = ctypes.c_int
+    lib.oracle_repack_q4_k.argtypes = [p, p, p, p, i64, i64]
+    lib.oracle_gemm_w4a8_q4k.restype = ctypes.c_int
+    lib.oracle_gemm_w4a8_q4k.argtypes = [p, p, p, p, i64, i64, i64]
     for name in ("oracle_gemm_w8a8", "oracle_gemm_w4a8", "oracle_gemm_w8a8_blockscale"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
@@ -128,6 +132,29 @@ def repack_q8_0(blocks, N, K):
     d = np.empty((N, K // 32), np.uint16)
     _check(_load().oracle_repack_q8_0(_ptr(blocks), _ptr(w), _ptr(d), N, K))
     return w, d
+
+
+def repack_q4_k(blocks, N, K):
+    """Q4_K super-blocks (uint8, N * K/256 * 144 bytes) -> (codes int8 [N, K] in 0..15,
+    D float32 [N, K/32] = d * sc, Mn float32 [N, K/32] = dmin * m)."""
+    blocks = _c(blocks, np.uint8).reshape(-1)
+    assert blocks.size == N * (K // 256) * 144
+    w = np.empty((N, K), np.int8)
+    D = np.empty((N, K // 32), np.float32)
+    Mn = np.empty((N, K // 32), np.float32)
+    _check(_load().oracle_repack_q4_k(_ptr(blocks), _ptr(w), _ptr(D), _ptr(Mn), N, K))
+    return w, D, Mn
+
+
+def gemm_w4a8_q4k(q, s_a, blocks, N):
+    """q int8 [M, K], s_a f32 [M], Q4_K blocks of an [N, K] weight matrix -> y f32 [M, N]."""
+    q, s_a = _c(q, np.int8), _c(s_a, np.float32)
+    blocks = _c(blocks, np.uint8).reshape(-1)
+    M, K = q.shape
+    assert blocks.size == N * (K // 256) * 144 and s_a.shape == (M,)
+    y = np.empty((M, N), np.float32)
+    _check(_load().oracle_gemm_w4a8_q4k(_ptr(q), _ptr(s_a), _ptr(blocks), _ptr(y), M, N, K))
+    return y
 
 
 def gemm_w8a8(q, s_a, w, s_w):

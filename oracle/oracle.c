@@ -37,6 +37,18 @@
  *      32 b + 31 of row n; blocks follow each other row by row, block
  *      n * (K / 32) + b.  A block stands for the values scale * code, which
  *      is exactly the block-scale operand pair (w, d) of R4.
+ *   R8 Q4_K weight blocks (the public GGUF layout; the pages only say that
+ *      Q4_K_M files run on their own 4-bit values): a super-block of 256
+ *      weights in 144 bytes: binary16 d, binary16 dmin (little-endian), 12
+ *      bytes of 6-bit sub-block scales sc_j and mins m_j (j = 0..7: for j < 4
+ *      sc_j = s[j] & 63, m_j = s[j+4] & 63; for j >= 4 sc_j = (s[j+4] & 15) |
+ *      (s[j-4] >> 6) << 4, m_j = (s[j+4] >> 4) | (s[j] >> 6) << 4), then 128
+ *      bytes of codes: byte 32 g + l holds the code of weight 64 g + l in its
+ *      low nibble and of weight 64 g + 32 + l in its high nibble.  Weight =
+ *      d sc_j code - dmin m_j.  Per 32-weight sub-block the sums P = sum
+ *      code * a and S = sum a are exact integers, D = d * sc_j and Mn = dmin
+ *      * m_j are exact in fp32, and f = +0; for each sub-block in ascending
+ *      k: f = fmaf((float)P, D, f); f = fmaf(-(float)S, Mn, f); y = f * s_a.
  *   R6 static activation scale ("Quick start": ranges measured once, ahead
  *      of time): one fp32 s > 0 for the whole tensor; q = clamp(rint(x / s),
  *      -127, 127) saturates values beyond the calibrated range (an infinite
@@ -167,6 +179,79 @@ int oracle_repack_q8_0(const uint8_t* blocks, int8_t* w, uint16_t* d, int64_t N,
             const uint8_t* blk = blocks + (n * NB + b) * 34;
             d[n * NB + b] = (uint16_t)(blk[0] | (blk[1] << 8));
             for (int64_t j = 0; j < 32; ++j) w[n * K + b * 32 + j] = (int8_t)blk[2 + j];
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Q4_K super-block helpers (R8). */
+static void oracle_q4k_scale_min(const uint8_t* sb, int j, int* sc, int* mn) {
+    const uint8_t* s = sb + 4;
+    if (j < 4) {
+        *sc = s[j] & 63;
+        *mn = s[j + 4] & 63;
+    } else {
+        *sc = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);
+        *mn = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+    }
+}
+
+static int oracle_q4k_code(const uint8_t* sb, int i) { /* i = 0..255 within the super-block */
+    const uint8_t* qs = sb + 16;
+    const int g = i / 64, l = i % 64;
+    return l < 32 ? (qs[32 * g + l] & 15) : (qs[32 * g + l - 32] >> 4);
+}
+
+/* Q4_K blocks -> codes w [N][K] (0..15 as int8), D [N][K/32] = d*sc and Mn [N][K/32] = dmin*m (fp32). */
+int oracle_repack_q4_k(const uint8_t* blocks, int8_t* w, float* D, float* Mn, int64_t N, int64_t K) {
+    if (N < 0 || K <= 0 || K % 256 != 0 || (N > 0 && (!blocks || !w || !D || !Mn))) return ORACLE_ERR_ARG;
+    const int64_t NS = K / 256;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t t = 0; t < NS; ++t) {
+            const uint8_t* sb = blocks + (n * NS + t) * 144;
+            const float d = oracle_f16_to_f32((uint16_t)(sb[0] | (sb[1] << 8)));
+            const float dmin = oracle_f16_to_f32((uint16_t)(sb[2] | (sb[3] << 8)));
+            for (int j = 0; j < 8; ++j) {
+                int sc, mn;
+                oracle_q4k_scale_min(sb, j, &sc, &mn);
+                D[n * (K / 32) + t * 8 + j] = d * (float)sc;
+                Mn[n * (K / 32) + t * 8 + j] = dmin * (float)mn;
+            }
+            for (int i = 0; i < 256; ++i) w[n * K + t * 256 + i] = (int8_t)oracle_q4k_code(sb, i);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* W4A8 on Q4_K blocks (R8), straight from the blocks. */
+int oracle_gemm_w4a8_q4k(const int8_t* q, const float* s_a, const uint8_t* blocks, float* y,
+                         int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N <= 0 || K <= 0 || K % 256 != 0) return ORACLE_ERR_ARG;
+    if (M > 0 && (!q || !s_a || !blocks || !y)) return ORACLE_ERR_ARG;
+    const int64_t NS = K / 256;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            float f = 0.0f;
+            for (int64_t t = 0; t < NS; ++t) {
+                const uint8_t* sb = blocks + (n * NS + t) * 144;
+                const float d = oracle_f16_to_f32((uint16_t)(sb[0] | (sb[1] << 8)));
+                const float dmin = oracle_f16_to_f32((uint16_t)(sb[2] | (sb[3] << 8)));
+                for (int j = 0; j < 8; ++j) {
+                    int sc, mn;
+                    oracle_q4k_scale_min(sb, j, &sc, &mn);
+                    int64_t p = 0, sa = 0;
+                    for (int i = 32 * j; i < 32 * j + 32; ++i) {
+                        const int64_t a = q[m * K + t * 256 + i];
+                        p += (int64_t)oracle_q4k_code(sb, i) * a;
+                        sa += a;
+                    }
+                    const float D = d * (float)sc, Mn = dmin * (float)mn;
+                    f = fmaf((float)p, D, f);
+                    f = fmaf(-(float)sa, Mn, f);
+                }
+            }
+            y[m * N + n] = f * s_a[m];
         }
     }
     return ORACLE_OK;

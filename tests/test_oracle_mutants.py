@@ -53,6 +53,16 @@ MUTANTS = [
     ("q8_0: block stride 33", "(n * NB + b) * 34", "(n * NB + b) * 33", 1),
     ("q8_0: codes reversed", "w[n * K + b * 32 + j] = (int8_t)blk[2 + j];",
      "w[n * K + b * 32 + (31 - j)] = (int8_t)blk[2 + j];", 1),
+    ("q4k: high scale bits from the wrong nibble", "*sc = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);",
+     "*sc = (s[j + 4] >> 4) | ((s[j - 4] >> 6) << 4);", 1),
+    ("q4k: low/high code halves swapped", "return l < 32 ? (qs[32 * g + l] & 15) : (qs[32 * g + l - 32] >> 4);",
+     "return l < 32 ? (qs[32 * g + l] >> 4) : (qs[32 * g + l - 32] & 15);", 1),
+    ("q4k: codes paired along k", "return l < 32 ? (qs[32 * g + l] & 15) : (qs[32 * g + l - 32] >> 4);",
+     "return (i % 2 == 0) ? (qs[i / 2] & 15) : (qs[i / 2] >> 4);", 1),
+    ("q4k: min added", "f = fmaf(-(float)sa, Mn, f);", "f = fmaf((float)sa, Mn, f);", 1),
+    ("q4k: min term dropped", "f = fmaf(-(float)sa, Mn, f);", "", 1),
+    ("q4k: d and dmin swapped", "const float d = oracle_f16_to_f32((uint16_t)(sb[0] | (sb[1] << 8)));",
+     "const float d = oracle_f16_to_f32((uint16_t)(sb[2] | (sb[3] << 8)));", 0),
     ("no int32 range check", "if (sum >= INT32_LIMIT || sum < -INT32_LIMIT) {", "if (0) {", 0),
 ]
 
@@ -76,6 +86,10 @@ def _checks():
         pins.test_static_quantizer_equals_dynamic_at_row_absmax,
         pins.test_q8_0_hand_fixture,
         pins.test_q8_0_round_trip_with_struct_packer,
+        pins.test_q4_k_hand_fixture,
+        pins.test_q4_k_round_trip_with_independent_packer,
+        pins.test_q4_k_gemm_within_bound_of_exact_dot_product,
+        pins.test_q4_k_gemm_without_mins_is_the_block_scale_gemm,
         pins.test_channel_epilogue_exact_rationals,
         pins.test_w4a8_epilogue_exact_rationals,
         pins.test_f16_to_f32_exhaustive_vs_numpy,

@@ -352,6 +352,113 @@ def test_q8_0_round_trip_with_struct_packer():
     assert np.array_equal(d2, dv.view(np.uint16))
 
 
+# ------------------------------------------------------------------ Q4_K blocks
+
+def _pack_q4_k(codes, d16, dmin16, sc, mn):
+    """Q4_K super-blocks from the layout's description (not from the oracle's unpacking):
+    d, dmin little-endian binary16; 12 scale bytes holding 6-bit sc_j / m_j (j < 4 in the low
+    6 bits of bytes j and j + 4; j >= 4 as a low nibble pair in byte j + 4 plus the top 2 bits
+    of bytes j - 4 and j); 128 code bytes, byte 32 g + l = code[64 g + l] | code[64 g + 32 + l] << 4."""
+    import struct
+    N, K = codes.shape
+    out = bytearray()
+    for n in range(N):
+        for t in range(K // 256):
+            s = [0] * 12
+            for j in range(8):
+                c, m = int(sc[n, 8 * t + j]), int(mn[n, 8 * t + j])
+                if j < 4:
+                    s[j] |= c & 63
+                    s[j + 4] |= m & 63
+                else:
+                    s[j + 4] |= (c & 15) | ((m & 15) << 4)
+                    s[j - 4] |= (c >> 4) << 6
+                    s[j] |= (m >> 4) << 6
+            blk = codes[n, 256 * t:256 * t + 256].astype(np.int64)
+            qs = [0] * 128
+            for g in range(4):
+                for l in range(32):
+                    qs[32 * g + l] = int(blk[64 * g + l]) | (int(blk[64 * g + 32 + l]) << 4)
+            out += struct.pack("<e", float(d16[n, t])) + struct.pack("<e", float(dmin16[n, t]))
+            out += bytes(s) + bytes(qs)
+    return np.frombuffer(bytes(out), np.uint8)
+
+
+def _q4k_case(seed, N, K, zero_mins=False):
+    r = _rng(seed)
+    codes = r.integers(0, 16, (N, K), dtype=np.int8)
+    d16 = (r.uniform(0.5, 1.0, (N, K // 256)) * 2.0 ** r.integers(-14, -4, (N, K // 256))).astype(np.float16)
+    dmin16 = (r.uniform(0.5, 1.0, (N, K // 256)) * 2.0 ** r.integers(-14, -4, (N, K // 256))).astype(np.float16)
+    sc = r.integers(0, 64, (N, K // 32))
+    mn = np.zeros((N, K // 32), np.int64) if zero_mins else r.integers(0, 64, (N, K // 32))
+    return codes, d16, dmin16, sc, mn
+
+
+def test_q4_k_hand_fixture():
+    # sub-block 0: sc 1, m 2; sub-block 4: sc 0b11_1010 = 58, m 0b01_0101 = 21; the rest 0
+    s = [0] * 12
+    s[0] = 0b11000001     # sc0 = 1, top bits = high bits of sc4
+    s[4] = 0b01000010     # m0 = 2, top bits = high bits of m4
+    s[8] = 0x5A           # sc4 low nibble 0xA, m4 low nibble 0x5
+    qs = [0] * 128
+    qs[0] = 0x73          # weight 0: code 3; weight 32: code 7
+    qs[32 + 5] = 0xF0     # weight 64 + 5: code 0; weight 96 + 5: code 15
+    raw = bytes([0x00, 0x3C, 0x00, 0x38]) + bytes(s) + bytes(qs)   # d = 1.0, dmin = 0.5
+    w, D, Mn = oracle.repack_q4_k(np.frombuffer(raw, np.uint8), 1, 256)
+    assert D[0].tolist() == [1.0, 0, 0, 0, 58.0, 0, 0, 0]
+    assert Mn[0].tolist() == [1.0, 0, 0, 0, 10.5, 0, 0, 0]
+    expect = np.zeros(256, np.int8)
+    expect[0], expect[32], expect[101] = 3, 7, 15
+    assert np.array_equal(w[0], expect)
+
+
+def test_q4_k_round_trip_with_independent_packer():
+    codes, d16, dmin16, sc, mn = _q4k_case(140, 3, 512)
+    d16[0, 0] = np.float16(6.0e-8)     # subnormal binary16 scale
+    w, D, Mn = oracle.repack_q4_k(_pack_q4_k(codes, d16, dmin16, sc, mn), 3, 512)
+    assert np.array_equal(w, codes)
+    dd = np.repeat(d16.astype(np.float64), 8, axis=1)
+    dm = np.repeat(dmin16.astype(np.float64), 8, axis=1)
+    # d * sc and dmin * m are exact in fp32 (11 + 6 significant bits)
+    assert np.array_equal(bits(D), bits((dd * sc).astype(np.float32)))
+    assert np.array_equal(bits(Mn), bits((dm * mn).astype(np.float32)))
+
+
+def test_q4_k_gemm_within_bound_of_exact_dot_product():
+    """|y - s_a * sum_k w_k a_k| stays within the rounding bound of the fp32 chain (exact sum in fp64)."""
+    N, K, M = 6, 1024, 4
+    codes, d16, dmin16, sc, mn = _q4k_case(141, N, K)
+    blocks = _pack_q4_k(codes, d16, dmin16, sc, mn)
+    r = _rng(142)
+    q = r.integers(-127, 128, (M, K), dtype=np.int8)
+    s_a = r.uniform(1e-3, 1e-2, M).astype(np.float32)
+    y = oracle.gemm_w4a8_q4k(q, s_a, blocks, N)
+    dd = np.repeat(np.repeat(d16.astype(np.float64), 8, axis=1) * sc, 32, axis=1)     # d * sc per weight
+    dm = np.repeat(np.repeat(dmin16.astype(np.float64), 8, axis=1) * mn, 32, axis=1)  # dmin * m per weight
+    wv = dd * codes - dm                                                                 # exact in fp64
+    for m in range(M):
+        a = q[m].astype(np.float64)
+        exact = (wv * a).sum(axis=1)
+        mag = (np.abs(dd * codes) * np.abs(a)).sum(axis=1) + (np.abs(dm) * np.abs(a)).sum(axis=1)
+        bound = 2 * (K // 32) * 2.0 ** -24 * mag + 2.0 ** -23 * np.abs(exact)
+        assert (np.abs(y[m] / s_a[m].astype(np.float64) - exact) <= bound + 1e-30).all(), m
+
+
+def test_q4_k_gemm_without_mins_is_the_block_scale_gemm():
+    """Zero mins and d * sc exact in binary16: the Q4_K path is the pinned block-scale path, bit for bit."""
+    N, K, M = 5, 512, 3
+    codes, _, dmin16, sc, mn = _q4k_case(143, N, K, zero_mins=True)
+    d16 = np.full((N, K // 256), np.float16(2.0 ** -10))
+    blocks = _pack_q4_k(codes, d16, dmin16, sc, mn)
+    r = _rng(144)
+    q = r.integers(-127, 128, (M, K), dtype=np.int8)
+    s_a = r.uniform(1e-3, 1e-2, M).astype(np.float32)
+    y = oracle.gemm_w4a8_q4k(q, s_a, blocks, N)
+    dbits = (np.float64(2.0 ** -10) * sc).astype(np.float16).view(np.uint16)   # exact: sc < 64
+    y_b, _ = oracle.gemm_w8a8_blockscale(q, s_a, codes, dbits)
+    assert np.array_equal(bits(y), bits(y_b))
+
+
 # ------------------------------------------------------------------ epilogues
 
 def test_channel_epilogue_exact_rationals():

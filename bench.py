@@ -45,7 +45,7 @@ def _args():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy three times (scale for HBM byte counters)")
     ap.add_argument("--only", default=None, help="run only one kernel measurement (for profiling): "
-                    "step | w4a8 | block | repack | stress")
+                    "step | w4a8 | block | repack | q4k | stress")
     return ap.parse_args()
 
 
@@ -74,6 +74,18 @@ class Launcher:
     def repack(self, blocks, w, d):
         N, K = w.shape
         f, a = self.lib.prism_repack_q8_0, (self.p(blocks), self.p(w), self.p(d), N, K, self.stream)
+        return lambda: f(*a)
+
+    def repack_q4k(self, blocks, w, D, Mn):
+        N, K = w.shape
+        f, a = self.lib.prism_repack_q4_k, (self.p(blocks), self.p(w), self.p(D), self.p(Mn), N, K, self.stream)
+        return lambda: f(*a)
+
+    def q4k(self, q, sa, w, D, Mn, y):
+        M, K = q.shape
+        N = w.shape[0]
+        f, a = self.lib.prism_gemm_w4a8_q4k, (self.p(q), self.p(sa), self.p(w), self.p(D), self.p(Mn), self.p(y),
+                                              M, N, K, self.stream)
         return lambda: f(*a)
 
     def w8a8(self, q, sa, w, sw, y):
@@ -310,6 +322,43 @@ def kernels(torch, prism, wl, only=None):
         out["repack_q8_0_17408x5120"] = dict(us=t * 1e6, gbs=nbytes / t / 1e9, hbm_frac=nbytes / t / 1e9 / PEAK_HBM_GBS,
                                              us_single_launch=t1 * 1e6, algorithmic_bytes=nbytes, copies=R)
         del srcs
+    if only in (None, "q4k"):
+        # Q4_K weights for the block-scale shape (17408 x 5120): random super-block bytes
+        # (timing only), repacked once per copy, then the GEMM at M = 2048 and M = 1
+        N, K = 17408, 5120
+        nsb = N * (K // 256)
+        g = torch.Generator(device=dev).manual_seed(12)
+        R = _copies(N * K + 8 * N * (K // 32))
+        planes = []
+        srcs = [torch.randint(0, 256, (nsb * 144,), dtype=torch.uint8, device=dev, generator=g) for _ in range(2)]
+        for i in range(R):
+            w = torch.empty((N, K), dtype=torch.int8, device=dev)
+            D = torch.empty((N, K // 32), dtype=torch.float32, device=dev)
+            Mn = torch.empty((N, K // 32), dtype=torch.float32, device=dev)
+            D.fill_(1e-3)
+            Mn.fill_(1e-4)
+            planes.append((w, D, Mn))
+        t1, t = _time_launches(torch, [L.repack_q4k(srcs[i % 2], *planes[i]) for i in range(2)], 20)
+        nbytes = nsb * 144 + N * K + 8 * N * (K // 32)
+        out["repack_q4_k_17408x5120"] = dict(us=t * 1e6, gbs=nbytes / t / 1e9, hbm_frac=nbytes / t / 1e9 / PEAK_HBM_GBS,
+                                             us_single_launch=t1 * 1e6, algorithmic_bytes=nbytes)
+        for _, D, Mn in planes:          # sane scales for the GEMM timing (random bytes may hold NaN)
+            D.fill_(1e-3)
+            Mn.fill_(1e-4)
+        xb = wl.block()["x"]
+        for M in (2048, 1):
+            x = torch.from_numpy(xb[:M].copy()).to(dev)
+            q = torch.empty((M, K), dtype=torch.int8, device=dev)
+            sa = torch.empty((M,), dtype=torch.float32, device=dev)
+            _check(L.quantize(x, q, sa)())
+            y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            t1, t = _time_launches(torch, [L.q4k(q, sa, *p, y) for p in planes], 10 if M > 1 else 50)
+            ops = 2 * M * N * K
+            nb = N * K + 8 * N * (K // 32) + M * K + 4 * M + 4 * M * N
+            out["q4k_m%d" % M] = dict(us=t * 1e6, tops=ops / t / 1e12, mfma_frac=ops / t / 1e12 / PEAK_INT8_TOPS,
+                                      gbs=nb / t / 1e9, hbm_frac=nb / t / 1e9 / PEAK_HBM_GBS,
+                                      us_single_launch=t1 * 1e6, copies=R)
+        del planes, srcs
     if only in (None, "stress"):
         st = wl.stress()
         w, sw = T(st["w"]), T(st["s_w"])

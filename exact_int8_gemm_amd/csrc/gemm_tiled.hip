@@ -108,4 +108,12 @@ int launch_gemm_blockscale(const int8_t* q, const float* s_a, const int8_t* w, c
   return launch_status();
 }
 
+// Q4_K-native W4A8 on the repacked planes: the block-scale pipeline with fp32
+// sub-block scales and mins (128 x 128 tiles, two workgroups per CU).
+int launch_gemm_q4k(const int8_t* q, const float* s_a, const int8_t* w, const float* D, const float* Mn, float* y,
+                    int M, int N, int K, hipStream_t st) {
+  tiled::dma::launch_q4k<128, 128, 2, 2, 2, 2>(q, s_a, w, D, Mn, y, M, N, K, st);
+  return launch_status();
+}
+
 }  // namespace prism

@@ -414,6 +414,17 @@ __device__ inline void copy2_to_lds(const v4i rsrc, uint32_t lds_addr, uint32_t 
                : "memory");
 }
 
+// The same for 4-byte elements: lane i's dword lands at lds_addr + 4 * lane.
+__device__ inline void copy4_to_lds(const v4i rsrc, uint32_t lds_addr, uint32_t voff) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+  const v4i r = v4i{__builtin_amdgcn_readfirstlane(rsrc[0]), __builtin_amdgcn_readfirstlane(rsrc[1]),
+                    __builtin_amdgcn_readfirstlane(rsrc[2]), __builtin_amdgcn_readfirstlane(rsrc[3])};
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(r)
+               : "memory");
+}
+
 // s_waitcnt with vmcnt <= n and no wait on the other counters (gfx9 encoding).
 template <int N>
 __device__ inline void wait_vmcnt() {
@@ -872,6 +883,197 @@ void launch_block(const int8_t* q, const float* s_a, const int8_t* w, const uint
   else
     gemm_block_kernel<BM, BN, WM, WN, RING, OCC, false><<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, 0, st>>>(
         q, s_a, w, d, y, nullptr, M, N, K, tiles_m, tiles_n);
+}
+
+// Q4_K-native W4A8 on repacked planes: codes w [N][K] (0..15 as int8),
+// D = d * sc and Mn = dmin * m [N][K/32] fp32 (exact products).  Per 32-k
+// sub-block: P = sum code * a and S = sum a, both exact int32 from MFMAs
+// started at zero (S from a B operand of ones, so it lands in the same
+// row-per-register layout as P), folded in ascending sub-block order:
+// f = fmaf((float)P, D, f); f = fmaf(-(float)S, Mn, f); y = f * s_a[m].
+// Same direct-to-LDS pipeline as gemm_block_kernel; D and Mn of the stage's
+// blocks ride along (4-byte copies), D of block ks, column c at dword
+// ks * BN + c of the scale area and Mn KS * BN dwords further.
+template <int BM, int BN, int WM, int WN, int RING, int OCC>
+__global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_q4k_kernel(const int8_t* __restrict__ q,
+                                                                     const float* __restrict__ s_a,
+                                                                     const int8_t* __restrict__ w,
+                                                                     const float* __restrict__ Dp,
+                                                                     const float* __restrict__ Mp,
+                                                                     float* __restrict__ y, int M, int N, int K,
+                                                                     int tiles_m, int tiles_n) {
+  constexpr int BK = 128;
+  constexpr int KS = BK / 32;  // sub-blocks per stage
+  using C = Cfg<BM, BN, BK, WM, WN, RING>;
+  constexpr int kSCopies = 2 * KS * BN / 64;  // D and Mn
+  constexpr int kPerWaveS = kSCopies / C::kNW;
+  static_assert(kSCopies % C::kNW == 0, "scale copies must divide among waves");
+  constexpr int kPerWave = C::kPerWave + kPerWaveS;
+  constexpr int kSOff = (BM + BN) * BK;  // scale area within a stage
+  constexpr int kStage = kSOff + 2 * KS * BN * 4;
+  static_assert(RING * kStage <= 160 * 1024, "LDS ring exceeds 160 KiB");
+  static_assert((RING - 2) * kPerWave < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) int8_t lds0[kStage];
+  __shared__ __attribute__((aligned(1024))) int8_t lds1[kStage];
+  __shared__ __attribute__((aligned(1024))) int8_t lds2[RING > 2 ? kStage : 16];
+  __shared__ __attribute__((aligned(1024))) int8_t lds3[RING > 3 ? kStage : 16];
+
+  int tm, tn;
+  tile_of(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int NB = K / 32;
+
+  const v4i ra = rsrc_words(q + (size_t)m0 * (size_t)K, (int64_t)(M - m0) * K);
+  const v4i rb = rsrc_words(w + (size_t)n0 * (size_t)K, (int64_t)(N - n0) * K);
+  const v4i rD = rsrc_words(Dp + (size_t)n0 * (size_t)NB, (int64_t)(N - n0) * NB * 4);
+  const v4i rM = rsrc_words(Mp + (size_t)n0 * (size_t)NB, (int64_t)(N - n0) * NB * 4);
+  uint32_t off[C::kPerWave];
+  int kc[C::kPerWave];
+#pragma unroll
+  for (int s = 0; s < C::kPerWave; ++s) {
+    const bool isA = s < C::kPerWaveA;
+    const int copy = isA ? wave * C::kPerWaveA + s : wave * C::kPerWaveB + (s - C::kPerWaveA);
+    const int row = copy * C::kRowsPerCopy + lane / C::kChunks;
+    const int chunk = (lane % C::kChunks) ^ C::swz(row);
+    kc[s] = chunk * 16;
+    const bool valid = isA ? (m0 + row < M) : (n0 + row < N);
+    off[s] = valid ? (uint32_t)(row * K + chunk * 16) : kOutOfRange;
+  }
+  // Scale copies of this wave: copy c is array c / (KS * BN / 64) (D, then Mn),
+  // block (c % (KS * BN / 64)) / (BN / 64), columns ((c % (BN / 64)) * 64 + lane).
+  uint32_t soff[kPerWaveS];
+  int sks[kPerWaveS];
+#pragma unroll
+  for (int s = 0; s < kPerWaveS; ++s) {
+    const int c = (wave * kPerWaveS + s) % (KS * BN / 64);
+    const int col = (c % (BN / 64)) * 64 + lane;
+    sks[s] = c / (BN / 64);
+    soff[s] = (n0 + col < N) ? (uint32_t)(col * NB * 4) : kOutOfRange;
+  }
+  auto issue = [&](int8_t* base, int stage) __attribute__((always_inline)) {
+    const int k0 = stage * BK;
+#pragma unroll
+    for (int s = 0; s < C::kPerWave; ++s) {
+      const bool isA = s < C::kPerWaveA;
+      const int copy = isA ? wave * C::kPerWaveA + s : wave * C::kPerWaveB + (s - C::kPerWaveA);
+      const uint32_t o = (k0 + kc[s] < K) ? off[s] + (uint32_t)k0 : kOutOfRange;
+      const int8_t* dst = base + (isA ? 0 : BM * BK) + copy * 1024;
+      copy_to_lds(isA ? ra : rb, lds_addr(dst), o);
+    }
+#pragma unroll
+    for (int s = 0; s < kPerWaveS; ++s) {
+      const int cg = wave * kPerWaveS + s;  // 0 .. kSCopies - 1; the first half is D
+      const int b = stage * KS + sks[s];
+      const uint32_t o = (b < NB) ? soff[s] + (uint32_t)(b * 4) : kOutOfRange;
+      const int8_t* dst = base + kSOff + cg * 256;
+      copy4_to_lds(cg < kSCopies / 2 ? rD : rM, lds_addr(dst), o);
+    }
+  };
+
+  float f[C::kTM][C::kTN][16];
+#pragma unroll
+  for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::kTN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) f[i][j][r] = 0.0f;
+
+  const int rl = lane & 31;
+  const int sw = C::swz(rl);
+  const int arow = (wm * C::kWTM + rl) * BK;
+  const int brow = (BM + wn * C::kWTN + rl) * BK;
+  int ncol[C::kTN];
+#pragma unroll
+  for (int j = 0; j < C::kTN; ++j) ncol[j] = wn * C::kWTN + j * 32 + rl;
+
+  auto compute = [&](const int8_t* buf) __attribute__((always_inline)) {
+    const v16i zero = v16i{};
+    const v4i ones = v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      // Sub-blocks past K read zero operands and zero scales: both fmas
+      // return f unchanged (f starts at +0 and never becomes -0).
+      const int c = ((2 * ks + (lane >> 5)) ^ sw) * 16;
+      v4i af[C::kTM], bf[C::kTN];
+      float dv[C::kTN], mv[C::kTN];
+#pragma unroll
+      for (int i = 0; i < C::kTM; ++i) af[i] = *reinterpret_cast<const v4i*>(buf + arow + i * 32 * BK + c);
+#pragma unroll
+      for (int j = 0; j < C::kTN; ++j) {
+        bf[j] = *reinterpret_cast<const v4i*>(buf + brow + j * 32 * BK + c);
+        dv[j] = *reinterpret_cast<const float*>(buf + kSOff + (ks * BN + ncol[j]) * 4);
+        mv[j] = *reinterpret_cast<const float*>(buf + kSOff + ((KS + ks) * BN + ncol[j]) * 4);
+      }
+#pragma unroll
+      for (int i = 0; i < C::kTM; ++i) {
+        const v16i sa = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], ones, zero, 0, 0, 0);
+        float ns[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ns[r] = -(float)sa[r];
+#pragma unroll
+        for (int j = 0; j < C::kTN; ++j) {
+          const v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], zero, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            f[i][j][r] = __builtin_fmaf((float)p[r], dv[j], f[i][j][r]);
+            f[i][j][r] = __builtin_fmaf(ns[r], mv[j], f[i][j][r]);
+          }
+        }
+      }
+    }
+  };
+  auto step = [&](const int8_t* cur, int8_t* nxt, int stage) __attribute__((always_inline)) {
+    wait_vmcnt<(RING - 2) * kPerWave>();
+    __syncthreads();
+    issue(nxt, stage + RING - 1);
+    compute(cur);
+  };
+
+  const int nk = (K + BK - 1) / BK;
+  const int nkr = (nk + RING - 1) / RING * RING;
+  issue(lds0, 0);
+  if constexpr (RING > 2) issue(lds1, 1);
+  if constexpr (RING > 3) issue(lds2, 2);
+  for (int k = 0; k < nkr; k += RING) {
+    if constexpr (RING == 2) {
+      step(lds0, lds1, k);
+      step(lds1, lds0, k + 1);
+    } else if constexpr (RING == 3) {
+      step(lds0, lds2, k);
+      step(lds1, lds0, k + 1);
+      step(lds2, lds1, k + 2);
+    } else {
+      step(lds0, lds3, k);
+      step(lds1, lds0, k + 1);
+      step(lds2, lds1, k + 2);
+      step(lds3, lds2, k + 3);
+    }
+  }
+  wait_vmcnt<0>();
+
+#pragma unroll
+  for (int j = 0; j < C::kTN; ++j) {
+    const int n = n0 + ncol[j];
+    if (n >= N) continue;
+#pragma unroll
+    for (int i = 0; i < C::kTM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * C::kWTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (m < M) y[(size_t)m * (size_t)N + (size_t)n] = f[i][j][r] * s_a[m];
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int RING, int OCC>
+void launch_q4k(const int8_t* q, const float* s_a, const int8_t* w, const float* D, const float* Mn, float* y, int M,
+                int N, int K, hipStream_t st) {
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  gemm_q4k_kernel<BM, BN, WM, WN, RING, OCC><<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, 0, st>>>(
+      q, s_a, w, D, Mn, y, M, N, K, tiles_m, tiles_n);
 }
 
 }  // namespace dma

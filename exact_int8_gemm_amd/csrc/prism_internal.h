@@ -21,6 +21,9 @@ constexpr int kSmallMMax = 64;
 int launch_quantize_rows(const float* x, int8_t* q, float* s, int64_t M, int64_t K, hipStream_t st);
 int launch_quantize_rows_static(const float* x, int8_t* q, float* s, float scale, int64_t M, int64_t K,
                                 hipStream_t st);
+int launch_repack_q4_k(const uint8_t* blocks, int8_t* w, float* D, float* Mn, int64_t N, int64_t K, hipStream_t st);
+int launch_gemm_q4k(const int8_t* q, const float* s_a, const int8_t* w, const float* D, const float* Mn, float* y,
+                    int M, int N, int K, hipStream_t st);
 int launch_repack_q8_0(const uint8_t* blocks, int8_t* w, uint16_t* d, int64_t N, int64_t K, hipStream_t st);
 
 int launch_gemm_small(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,

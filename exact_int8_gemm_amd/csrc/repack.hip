@@ -90,7 +90,73 @@ __global__ __launch_bounds__(kPerGroup) void repack_q8_0_kernel(const uint8_t* _
   }
 }
 
+// Q4_K super-blocks (public GGUF layout, 144 bytes per 256 weights): binary16
+// d and dmin, 12 bytes of 6-bit sub-block scales sc_j and mins m_j, 128 bytes
+// of 4-bit codes (byte 32 g + l: weight 64 g + l in the low nibble, weight
+// 64 g + 32 + l in the high one).  Output planes: the codes as int8 [N][K]
+// (0..15), D = d * sc_j and Mn = dmin * m_j as fp32 [N][K/32]; both products
+// are exact in fp32 (11 + 6 significant bits).  One workgroup moves 64
+// super-blocks (9216 bytes, a whole number of 16-byte pieces, each
+// super-block 16-byte aligned) through LDS.
+constexpr int kQ4kBytes = 144;
+constexpr int kQ4kPerGroup = 64;
+
+__global__ __launch_bounds__(256) void repack_q4_k_kernel(const uint8_t* __restrict__ blocks, int8_t* __restrict__ w,
+                                                          float* __restrict__ D, float* __restrict__ Mn,
+                                                          int64_t nsuper) {
+  __shared__ __attribute__((aligned(16))) uint8_t buf[kQ4kPerGroup * kQ4kBytes];
+  const int64_t s0 = (int64_t)blockIdx.x * kQ4kPerGroup;
+  const int ns = nsuper - s0 < kQ4kPerGroup ? (int)(nsuper - s0) : kQ4kPerGroup;
+  const uint32_t nbytes = (uint32_t)ns * kQ4kBytes;  // a multiple of 16
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blocks + s0 * kQ4kBytes), (short)0, (int)nbytes,
+                                        0x00020000);
+  for (uint32_t i = threadIdx.x; i < nbytes / 16; i += 256)
+    *reinterpret_cast<v4i*>(buf + 16 * i) = __builtin_amdgcn_raw_buffer_load_b128(r, i * 16, 0, 0);
+  __syncthreads();
+
+  // Codes: piece h covers codes 16 h' .. 16 h' + 15 of super-block h / 16 (h' = h % 16),
+  // all within one half of one 64-code group, so one 16-byte read of qs gives them.
+  for (int h = threadIdx.x; h < ns * 16; h += 256) {
+    const int sb = h >> 4, k0 = (h & 15) * 16, g = k0 >> 6, l = k0 & 63;
+    const v4i v = *reinterpret_cast<const v4i*>(buf + sb * kQ4kBytes + 16 + 32 * g + (l & 31));
+    v4i o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (int)(l < 32 ? ((uint32_t)v[e] & 0x0f0f0f0fu) : (((uint32_t)v[e] >> 4) & 0x0f0f0f0fu));
+    *reinterpret_cast<v4i*>(w + (s0 + sb) * 256 + k0) = o;
+  }
+  // Scales: thread t handles sub-blocks 2 (t % 4) and 2 (t % 4) + 1 of super-block t / 4.
+  const int t = threadIdx.x, sb = t >> 2;
+  if (sb < ns) {
+    const uint8_t* b = buf + sb * kQ4kBytes;
+    const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(b[0] | (b[1] << 8)));
+    const float dmin = (float)__builtin_bit_cast(_Float16, (uint16_t)(b[2] | (b[3] << 8)));
+    const uint8_t* sc = b + 4;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int j = 2 * (t & 3) + e;
+      int c, m;
+      if (j < 4) {
+        c = sc[j] & 63;
+        m = sc[j + 4] & 63;
+      } else {
+        c = (sc[j + 4] & 15) | ((sc[j - 4] >> 6) << 4);
+        m = (sc[j + 4] >> 4) | ((sc[j] >> 6) << 4);
+      }
+      D[(s0 + sb) * 8 + j] = d * (float)c;
+      Mn[(s0 + sb) * 8 + j] = dmin * (float)m;
+    }
+  }
+}
+
 }  // namespace
+
+int launch_repack_q4_k(const uint8_t* blocks, int8_t* w, float* D, float* Mn, int64_t N, int64_t K, hipStream_t st) {
+  const int64_t nsuper = N * (K / 256);
+  const int64_t groups = (nsuper + kQ4kPerGroup - 1) / kQ4kPerGroup;
+  repack_q4_k_kernel<<<(unsigned)groups, 256, 0, st>>>(blocks, w, D, Mn, nsuper);
+  return launch_status();
+}
 
 int launch_repack_q8_0(const uint8_t* blocks, int8_t* w, uint16_t* d, int64_t N, int64_t K, hipStream_t st) {
   const int64_t nblocks = N * (K / 32);

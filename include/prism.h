@@ -111,6 +111,36 @@ int prism_repack_q8_0(const uint8_t* blocks, int8_t* w, uint16_t* d,
                       int64_t N, int64_t K, void* stream);
 
 /*
+ * Q4_K weight super-blocks -> the planes of prism_gemm_w4a8_q4k (README "Why
+ * StartLux-Prism": released Q4_K_M files run on their own 4-bit values).  The
+ * super-block layout is the public GGUF one, not given by the pages: 144
+ * bytes per 256 consecutive weights of one row: binary16 d and dmin
+ * (little-endian), 12 bytes of 6-bit sub-block scales sc_j and mins m_j
+ * (j < 4: sc_j = s[j] & 63, m_j = s[j+4] & 63; j >= 4: sc_j = (s[j+4] & 15) |
+ * (s[j-4] >> 6) << 4, m_j = (s[j+4] >> 4) | (s[j] >> 6) << 4), then 128 bytes of
+ * codes (byte 32 g + l: weight 64 g + l in the low nibble, 64 g + 32 + l in
+ * the high one).  Weight = d * sc_j * code - dmin * m_j.
+ *   blocks [N * K/256][144] bytes, input (16-byte aligned).
+ *   w      [N][K] int8 output: the codes, 0..15 (16-byte aligned).
+ *   D, Mn  [N][K/32] fp32 outputs: d * sc_j and dmin * m_j, exact (4-byte aligned).
+ * K must be a positive multiple of 256; N = 0 is a no-op.
+ */
+int prism_repack_q4_k(const uint8_t* blocks, int8_t* w, float* D, float* Mn,
+                      int64_t N, int64_t K, void* stream);
+
+/*
+ * W4A8 on Q4_K weights (the planes of prism_repack_q4_k).
+ *   q [M][K] int8, s_a [M] fp32, w [N][K] int8 codes, D and Mn [N][K/32] fp32.
+ *   y [M][N] fp32 output.
+ * Per 32-k sub-block b: P_b = sum q[m][k] * w[n][k] and S_b = sum q[m][k],
+ * both exact integers; f = +0; for b ascending: f = fmaf((float)P_b,
+ * D[n][b], f); f = fmaf(-(float)S_b, Mn[n][b], f); then y[m][n] = f * s_a[m].
+ * K must be a multiple of 32.
+ */
+int prism_gemm_w4a8_q4k(const int8_t* q, const float* s_a, const int8_t* w, const float* D,
+                        const float* Mn, float* y, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * W8A8 GEMM with per-output-channel weight scales (README "Why
  * StartLux-Prism": Q8_0 weights as int8 W8A8, summed exactly in int32).
  *   q    [M][K] int8 activations, s_a [M] fp32 row scales.

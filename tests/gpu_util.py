@@ -13,6 +13,8 @@ DEV = torch.device("cuda:0")
 
 def dev(a):
     a = np.ascontiguousarray(a)
+    if not a.flags.writeable:
+        a = a.copy()
     if a.dtype == np.uint16:
         a = a.view(np.int16)
     return torch.from_numpy(a).to(DEV)

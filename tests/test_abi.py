@@ -43,6 +43,7 @@ def test_header_declares_every_call():
     names = set(_declared_functions())
     assert {"prism_quantize_rows", "prism_quantize_rows_static", "prism_repack_q8_0", "prism_gemm_w8a8",
             "prism_gemm_w8a8_blockscale", "prism_gemm_w4a8", "prism_gemm_w8a8_variant", "prism_gemm_w4a8_variant",
+            "prism_repack_q4_k", "prism_gemm_w4a8_q4k",
             "prism_abi_version", "prism_status_string"} <= names
 
 
@@ -77,6 +78,10 @@ lib.prism_quantize_rows_static.restype = i32
 lib.prism_quantize_rows_static.argtypes = [p, p, p, ctypes.c_float, i64, i64, p]
 lib.prism_repack_q8_0.restype = i32
 lib.prism_repack_q8_0.argtypes = [p, p, p, i64, i64, p]
+lib.prism_repack_q4_k.restype = i32
+lib.prism_repack_q4_k.argtypes = [p, p, p, p, i64, i64, p]
+lib.prism_gemm_w4a8_q4k.restype = i32
+lib.prism_gemm_w4a8_q4k.argtypes = [p, p, p, p, p, p, i64, i64, i64, p]
 for n in ("prism_gemm_w8a8_variant", "prism_gemm_w4a8_variant"):
     getattr(lib, n).restype = i32
     getattr(lib, n).argtypes = [p, p, p, p, p, p, i64, i64, i64, i32, p]
@@ -153,6 +158,38 @@ CASES += [
     (_RP, [A, A + 8, A, 4, 64, None], ALIGN),
     (_RP, [A, A, A + 1, 4, 64, None], ALIGN),
 ]
+_RK = "prism_repack_q4_k"
+CASES += [
+    (_RK, [A, A, A, A, 0, 256, None], OK),
+    (_RK, [A, A, A, A, -1, 256, None], INVALID),
+    (_RK, [A, A, A, A, 4, 0, None], INVALID),
+    (_RK, [None, A, A, A, 4, 256, None], INVALID),
+    (_RK, [A, A, A, None, 4, 256, None], INVALID),
+    (_RK, [A, A, A, A, 4, 288, None], ALIGN),          # K % 256
+    (_RK, [A + 8, A, A, A, 4, 256, None], ALIGN),
+    (_RK, [A, A, A + 2, A, 4, 256, None], ALIGN),
+    (_RK, [A, A, A, A + 2, 4, 256, None], ALIGN),
+]
+_GK = "prism_gemm_w4a8_q4k"
+
+
+def _k(q=A, sa=A, w=A, D=A, Mn=A, y=A, M=4, N=16, K=256):
+    return [q, sa, w, D, Mn, y, M, N, K, None]
+
+
+CASES += [
+    (_GK, _k(M=0), OK),
+    (_GK, _k(M=-1), INVALID),
+    (_GK, _k(K=0), INVALID),
+    (_GK, _k(Mn=None), INVALID),
+    (_GK, _k(D=None), INVALID),
+    (_GK, _k(q=None), INVALID),
+    (_GK, _k(K=48), ALIGN),
+    (_GK, _k(D=A + 2), ALIGN),
+    (_GK, _k(Mn=A + 2), ALIGN),
+    (_GK, _k(w=A + 8), ALIGN),
+]
+
 
 def _v(variant, **kw):
     a = _g(**kw)
@@ -239,11 +276,12 @@ def test_valid_call_without_a_device_is_unsupported(built):
     payload = json.dumps([["prism_gemm_w8a8", _g()], ["prism_quantize_rows", [A, A, A, 4, 64, None]],
                           ["prism_quantize_rows_static", [A, A, A, 0.25, 4, 64, None]],
                           ["prism_repack_q8_0", [A, A, A, 4, 64, None]],
-                          ["prism_gemm_w8a8_variant", _g()[:9] + [7, None]]])
+                          ["prism_gemm_w8a8_variant", _g()[:9] + [7, None]],
+                          ["prism_gemm_w4a8_q4k", _k()]])
     out = subprocess.run([sys.executable, "-c", _CHILD, built, payload], env=env, capture_output=True, text=True,
                          timeout=120)
     assert out.returncode == 0, out.stderr
-    assert json.loads(out.stdout.strip().splitlines()[-1])["status"] == [UNSUP, UNSUP, UNSUP, UNSUP, UNSUP]
+    assert json.loads(out.stdout.strip().splitlines()[-1])["status"] == [UNSUP, UNSUP, UNSUP, UNSUP, UNSUP, UNSUP]
 
 
 def test_build_uses_result_defining_flags():

@@ -161,6 +161,38 @@ def test_repack_q8_0_then_blockscale_gemm():
     assert_same_floats(host(y), y_ref, "y")
 
 
+# ------------------------------------------------------------------ Q4_K blocks
+
+@pytest.mark.parametrize("N,K", [(1, 256), (3, 512), (63, 256), (65, 768), (100, 5120)])
+def test_repack_q4_k(N, K):
+    """Random bytes (every pattern is a block, NaN and infinite scales included)."""
+    rng = np.random.default_rng(N * 17 + K)
+    blocks = rng.integers(0, 256, N * (K // 256) * 144, dtype=np.uint8)
+    w_ref, D_ref, M_ref = oracle.repack_q4_k(blocks, N, K)
+    w, D, Mn = prism.repack_q4_k(dev(blocks), N, K)
+    torch.cuda.synchronize()
+    assert_same_ints(host(w), w_ref, "codes")
+    assert_same_floats(host(D), D_ref, "d * sc")
+    assert_same_floats(host(Mn), M_ref, "dmin * m")
+
+
+@pytest.mark.parametrize("M", [1, 7, 65, 129, 257])
+@pytest.mark.parametrize("N,K", [(100, 256), (300, 1024), (130, 2304)])
+def test_gemm_w4a8_q4k(M, N, K):
+    """Q4_K bytes -> GPU repack -> GPU GEMM, against the oracle straight from the bytes."""
+    from test_oracle_pins import _pack_q4_k, _q4k_case
+    codes, d16, dmin16, sc, mn = _q4k_case(M * 1000 + N + K, N, K)
+    blocks = _pack_q4_k(codes, d16, dmin16, sc, mn)
+    rng = np.random.default_rng(M + 5)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    q_ref, sa_ref = oracle.quantize_rows(x)
+    y_ref = oracle.gemm_w4a8_q4k(q_ref, sa_ref, blocks, N)
+    w, D, Mn = prism.repack_q4_k(dev(blocks), N, K)
+    y = prism.gemm_w4a8_q4k(dev(q_ref), dev(sa_ref), w, D, Mn)
+    torch.cuda.synchronize()
+    assert_same_floats(host(y), y_ref, "y")
+
+
 # ------------------------------------------------------------------ GEMMs
 
 def _case(seed, M, N, K, kind):

@@ -306,6 +306,12 @@ def kernels(torch, prism, wl, only=None):
         out["block_scale_m2048"] = dict(us=t * 1e6, tops=ops / t / 1e12, mfma_frac=ops / t / 1e12 / PEAK_INT8_TOPS,
                                         valu_bound_us=valu_s * 1e6, valu_frac=valu_s / t, us_single_launch=t1 * 1e6,
                                         copies=R)
+        # decode: one row through the small-M block kernel (HBM-bound: weights and scales)
+        q1, sa1, y1 = q[:1].contiguous(), sa[:1].contiguous(), torch.empty((1, N), dtype=torch.float32, device=dev)
+        t1, t = _time_launches(torch, [L.block(q1, sa1, w, d, y1) for w, d in ws], 50)
+        nb1 = N * K + 2 * N * (K // 32) + K + 4 + 4 * N
+        out["block_scale_m1"] = dict(us=t * 1e6, gbs=nb1 / t / 1e9, hbm_frac=nb1 / t / 1e9 / PEAK_HBM_GBS,
+                                     us_single_launch=t1 * 1e6, algorithmic_bytes=nb1, copies=R)
         del ws
     if only in (None, "repack"):
         # Q8_0 blocks of the block-scale weight matrix (17408 x 5120): 34 bytes read and

@@ -227,7 +227,133 @@ bool pick_variant(const int8_t* q, const float* s_a, const int8_t* w, const floa
   return true;
 }
 
+// ---------------------------------------------------------------------------
+// Small-M block-scale GEMMs (M <= 16): fp16 block scales (Q8_0 style) or the
+// Q4_K planes (fp32 D = d * sc and Mn = dmin * m).  The fp32 fold over the
+// blocks is a chain in ascending k that cannot be split, but the exact int32
+// block sums can: a workgroup owns 16 output columns and walks K in chunks of
+// 32 blocks.  Phase 1: the waves compute each block's P = sum q * w (and for
+// Q4_K S = sum q, from a B operand of ones) with v_mfma_i32_16x16x32_i8 (one
+// 32-k block per instruction; lane l holds row / column l % 16 and k-slice
+// 8 (l / 16) of A and B, so each output sums the block's 32 k) into LDS, and
+// every thread moves one of the chunk's 32 x 16 scales into LDS.  Phase 2:
+// thread (m, n) folds the chunk's blocks into its chain in order,
+// f = fmaf((float)P, d, f) (Q4_K: then f = fmaf(-(float)S, Mn, f)).  The
+// loads of chunk c + 1 are issued before chunk c is consumed.
+template <bool Q4K, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemm_block_small_kernel(
+    const int8_t* __restrict__ q, const float* __restrict__ s_a, const int8_t* __restrict__ w,
+    const uint16_t* __restrict__ d16, const float* __restrict__ Dp, const float* __restrict__ Mp,
+    float* __restrict__ y, int M, int N, int K) {
+  constexpr int CH = 32;           // blocks per chunk
+  constexpr int PER = CH / WAVES;  // blocks per wave per chunk
+  static_assert(CH % WAVES == 0 && CH * 16 == 64 * WAVES, "one scale per thread per chunk");
+  __shared__ int pbuf[CH][16][16];  // [block][row][column]
+  __shared__ int sbuf[Q4K ? CH : 1][16];
+  __shared__ float sdv[CH][16];
+  __shared__ float smv[Q4K ? CH : 1][16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * 16;
+  const int NB = K / 32;
+  const int col = lane & 15, g = lane >> 4;
+
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q, (int64_t)M * K);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + (size_t)n0 * (size_t)K, (int64_t)(N - n0) * K);
+  // Rows / columns outside the matrices start out of range and stay there (+ 32 b < 2^31).
+  // Blocks past K of an in-range row read the next row's bytes; their sums are never stored.
+  const uint32_t qbase = col < M ? (uint32_t)(col * K + 8 * g) : kOutOfRange;
+  const uint32_t wbase = n0 + col < N ? (uint32_t)(col * K + 8 * g) : kOutOfRange;
+  const int64_t ones = 0x0101010101010101LL;
+  // Scales of the 16 columns through one buffer resource; this thread moves
+  // scale (block tb, column tc) of each chunk, zero past K or past N.
+  constexpr int kSB = Q4K ? 4 : 2;
+  const int64_t sbytes = (int64_t)(N - n0) * NB * kSB;
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(Q4K ? (const void*)(Dp + (size_t)n0 * NB) : (const void*)(d16 + (size_t)n0 * NB), sbytes);
+  const __amdgpu_buffer_rsrc_t rm = make_rsrc(Q4K ? (const void*)(Mp + (size_t)n0 * NB) : (const void*)d16,
+                                              Q4K ? sbytes : 0);
+  const int tb = threadIdx.x >> 4, tc = threadIdx.x & 15;
+
+  const int pm = threadIdx.x >> 4, pn = threadIdx.x & 15;  // phase-2 output of this thread
+  const bool chain = pm < M && n0 + pn < N;
+  float f = 0.0f;
+
+  struct Chunk {
+    int64_t a[PER], b[PER];
+    float d, m;
+  };
+  auto load = [&](int b0, Chunk& c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int b = b0 + wave + j * WAVES;
+      c.a[j] = __builtin_bit_cast(int64_t, __builtin_amdgcn_raw_buffer_load_b64(rq, qbase + 32 * b, 0, 0));
+      c.b[j] = __builtin_bit_cast(int64_t, __builtin_amdgcn_raw_buffer_load_b64(rw, wbase + 32 * b, 0, 0));
+    }
+    const uint32_t so = (b0 + tb < NB && n0 + tc < N) ? (uint32_t)(tc * NB + b0 + tb) * kSB : kOutOfRange;
+    if constexpr (Q4K) {
+      c.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, so, 0, 0));
+      c.m = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rm, so, 0, 0));
+    } else {
+      c.d = (float)__builtin_bit_cast(_Float16, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs, so, 0, 0));
+      c.m = 0.0f;
+    }
+  };
+  auto consume = [&](int b0, const Chunk& c) __attribute__((always_inline)) {
+    const int nb = NB - b0 < CH ? NB - b0 : CH;  // may be <= 0 for the padding chunk
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int bl = wave + j * WAVES;
+      const v4i p = __builtin_amdgcn_mfma_i32_16x16x32_i8(c.a[j], c.b[j], v4i{0, 0, 0, 0}, 0, 0, 0);
+      if (bl < nb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * g + i < M) pbuf[bl][4 * g + i][col] = p[i];
+      }
+      if constexpr (Q4K) {
+        const v4i sa = __builtin_amdgcn_mfma_i32_16x16x32_i8(c.a[j], ones, v4i{0, 0, 0, 0}, 0, 0, 0);
+        if (bl < nb && col == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (4 * g + i < M) sbuf[bl][4 * g + i] = sa[i];
+        }
+      }
+    }
+    sdv[tb][tc] = c.d;
+    if constexpr (Q4K) smv[tb][tc] = c.m;
+    __syncthreads();
+    if (chain) {
+      // Blocks past K (i >= nb) hold stale sums but zero scales: an fma with a
+      // zero scale adds a zero and leaves f unchanged (f starts at +0 and never
+      // becomes -0), so the chain runs the whole chunk without a branch.
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        f = __builtin_fmaf((float)pbuf[i][pm][pn], sdv[i][pn], f);
+        if constexpr (Q4K) f = __builtin_fmaf(-(float)sbuf[i][pm], smv[i][pn], f);
+      }
+    }
+    __syncthreads();  // the next chunk reuses the buffers
+  };
+
+  Chunk c0, c1;
+  load(0, c0);
+  for (int b0 = 0; b0 < NB; b0 += 2 * CH) {
+    load(b0 + CH, c1);
+    consume(b0, c0);
+    load(b0 + 2 * CH, c0);
+    consume(b0 + CH, c1);
+  }
+  if (chain) y[(size_t)pm * (size_t)N + (size_t)(n0 + pn)] = f * s_a[pm];
+}
+
 }  // namespace
+
+int launch_gemm_block_small(const int8_t* q, const float* s_a, const int8_t* w, const uint16_t* d16,
+                            const float* D, const float* Mn, float* y, int M, int N, int K, hipStream_t st) {
+  const unsigned grid = (unsigned)((N + 15) / 16);
+  if (D) gemm_block_small_kernel<true, 8><<<grid, 512, 0, st>>>(q, s_a, w, nullptr, D, Mn, y, M, N, K);
+  else gemm_block_small_kernel<false, 8><<<grid, 512, 0, st>>>(q, s_a, w, d16, nullptr, nullptr, y, M, N, K);
+  return launch_status();
+}
 
 int launch_gemm_small_variant(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
                               float* y, int32_t* acc, int M, int N, int K, int cb, int waves, hipStream_t st) {

@@ -104,6 +104,8 @@ int launch_gemm_tiled(const int8_t* q, const float* s_a, const void* w, bool w_i
 // first one waits).
 int launch_gemm_blockscale(const int8_t* q, const float* s_a, const int8_t* w, const uint16_t* d, float* y,
                            int32_t* partials, int M, int N, int K, hipStream_t st) {
+  if (M <= kBlockSmallMMax && !partials)
+    return launch_gemm_block_small(q, s_a, w, d, nullptr, nullptr, y, M, N, K, st);
   tiled::dma::launch_block<128, 128, 2, 2, 2, 2>(q, s_a, w, d, y, partials, M, N, K, st);
   return launch_status();
 }
@@ -112,6 +114,7 @@ int launch_gemm_blockscale(const int8_t* q, const float* s_a, const int8_t* w, c
 // sub-block scales and mins (128 x 128 tiles, two workgroups per CU).
 int launch_gemm_q4k(const int8_t* q, const float* s_a, const int8_t* w, const float* D, const float* Mn, float* y,
                     int M, int N, int K, hipStream_t st) {
+  if (M <= kBlockSmallMMax) return launch_gemm_block_small(q, s_a, w, nullptr, D, Mn, y, M, N, K, st);
   tiled::dma::launch_q4k<128, 128, 2, 2, 2, 2>(q, s_a, w, D, Mn, y, M, N, K, st);
   return launch_status();
 }

@@ -21,6 +21,10 @@ constexpr int kSmallMMax = 64;
 int launch_quantize_rows(const float* x, int8_t* q, float* s, int64_t M, int64_t K, hipStream_t st);
 int launch_quantize_rows_static(const float* x, int8_t* q, float* s, float scale, int64_t M, int64_t K,
                                 hipStream_t st);
+// M <= kBlockSmallMMax: block-scale (d16) or Q4_K (D, Mn) GEMM of the small-M family.
+constexpr int kBlockSmallMMax = 16;
+int launch_gemm_block_small(const int8_t* q, const float* s_a, const int8_t* w, const uint16_t* d16,
+                            const float* D, const float* Mn, float* y, int M, int N, int K, hipStream_t st);
 int launch_repack_q4_k(const uint8_t* blocks, int8_t* w, float* D, float* Mn, int64_t N, int64_t K, hipStream_t st);
 int launch_gemm_q4k(const int8_t* q, const float* s_a, const int8_t* w, const float* D, const float* Mn, float* y,
                     int M, int N, int K, hipStream_t st);

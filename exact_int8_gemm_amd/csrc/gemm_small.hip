@@ -91,6 +91,22 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(const int8_t* __
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) qbase[mb] = (mb * 16 + col < M) ? (uint32_t)((mb * 16 + col) * K) : kOutOfRange;
 
+  // The epilogue scales of this thread's outputs, loaded now so that the
+  // epilogue does not wait for a memory round trip after the reduction.
+  constexpr int kOut = CB * MB * 4 * 64;
+  constexpr int kEpt = (kOut + 64 * WAVES - 1) / (64 * WAVES);
+  float ea[kEpt], ew[kEpt];
+#pragma unroll
+  for (int t = 0; t < kEpt; ++t) {
+    const int e = threadIdx.x + t * 64 * WAVES;
+    const int idx = e >> 6, l = e & 63;
+    const int m = ((idx / 4) % MB) * 16 + (l >> 4) * 4 + idx % 4;
+    const int n = n0 + (idx / (MB * 4)) * 16 + (l & 15);
+    const bool ok = e < kOut && m < M && n < N;
+    ea[t] = ok ? s_a[m] : 0.0f;
+    ew[t] = ok ? s_w[n] : 0.0f;
+  }
+
   v4i acc[CB][MB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
@@ -154,7 +170,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(const int8_t* __
 
   // Output layout of the 16x16 MFMA: lane l, register i -> row 4 * (l / 16) + i,
   // column l % 16.
-  for (int e = threadIdx.x; e < CB * MB * 4 * 64; e += 64 * WAVES) {
+#pragma unroll
+  for (int t = 0; t < kEpt; ++t) {
+    const int e = threadIdx.x + t * 64 * WAVES;
+    if (e >= kOut) break;
     const int idx = e >> 6;
     const int l = e & 63;
     int s = 0;
@@ -167,8 +186,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(const int8_t* __
     if (m < M && n < N) {
       const size_t o = (size_t)m * (size_t)N + (size_t)n;
       if (acc_out) acc_out[o] = s;
-      const float t = (float)s * s_a[m];
-      y[o] = t * s_w[n];
+      const float v = (float)s * ea[t];
+      y[o] = v * ew[t];
     }
   }
 }
@@ -232,22 +251,26 @@ bool pick_variant(const int8_t* q, const float* s_a, const int8_t* w, const floa
 // Q4_K planes (fp32 D = d * sc and Mn = dmin * m).  The fp32 fold over the
 // blocks is a chain in ascending k that cannot be split, but the exact int32
 // block sums can: a workgroup owns 16 output columns and walks K in chunks of
-// 32 blocks.  Phase 1: the waves compute each block's P = sum q * w (and for
-// Q4_K S = sum q, from a B operand of ones) with v_mfma_i32_16x16x32_i8 (one
-// 32-k block per instruction; lane l holds row / column l % 16 and k-slice
-// 8 (l / 16) of A and B, so each output sums the block's 32 k) into LDS, and
-// every thread moves one of the chunk's 32 x 16 scales into LDS.  Phase 2:
+// 4 * WAVES blocks.  Phase 1: each wave computes the sums P = sum q * w of
+// four consecutive blocks (and for Q4_K S = sum q, from a B operand of ones)
+// with v_mfma_i32_16x16x32_i8 (one 32-k block per instruction, lane l holding
+// row / column l % 16) into LDS; operands are fetched as 16 bytes per lane,
+// 64 contiguous bytes per row and load, and regrouped into one block per
+// MFMA with v_permlane32_swap.  Every thread also moves one of the chunk's
+// scales into LDS.  Phase 2:
 // thread (m, n) folds the chunk's blocks into its chain in order,
-// f = fmaf((float)P, d, f) (Q4_K: then f = fmaf(-(float)S, Mn, f)).  The
-// loads of chunk c + 1 are issued before chunk c is consumed.
-template <bool Q4K, int WAVES>
+// f = fmaf((float)P, d, f) (Q4_K: then f = fmaf(-(float)S, Mn, f)).  Chunks
+// rotate through RING register sets: the loads of chunk c + RING - 1 are
+// issued before chunk c is consumed.
+template <bool Q4K, int WAVES, int RING>
 __global__ __launch_bounds__(64 * WAVES) void gemm_block_small_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ s_a, const int8_t* __restrict__ w,
     const uint16_t* __restrict__ d16, const float* __restrict__ Dp, const float* __restrict__ Mp,
     float* __restrict__ y, int M, int N, int K) {
-  constexpr int CH = 32;           // blocks per chunk
+  constexpr int CH = 4 * WAVES;    // blocks per chunk: one scale per thread
   constexpr int PER = CH / WAVES;  // blocks per wave per chunk
-  static_assert(CH % WAVES == 0 && CH * 16 == 64 * WAVES, "one scale per thread per chunk");
+  static_assert(WAVES >= 4, "phase 2 needs a thread for each of the 16 x 16 outputs");
+  static_assert(RING >= 2 && RING <= 4, "chunk ring depth");
   __shared__ int pbuf[CH][16][16];  // [block][row][column]
   __shared__ int sbuf[Q4K ? CH : 1][16];
   __shared__ float sdv[CH][16];
@@ -261,8 +284,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_block_small_kernel(
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + (size_t)n0 * (size_t)K, (int64_t)(N - n0) * K);
   // Rows / columns outside the matrices start out of range and stay there (+ 32 b < 2^31).
   // Blocks past K of an in-range row read the next row's bytes; their sums are never stored.
-  const uint32_t qbase = col < M ? (uint32_t)(col * K + 8 * g) : kOutOfRange;
-  const uint32_t wbase = n0 + col < N ? (uint32_t)(col * K + 8 * g) : kOutOfRange;
+  // Lane (col, g) loads 16 bytes at 16 g of each 64-byte pair of blocks.
+  const uint32_t qbase = col < M ? (uint32_t)(col * K + 16 * g) : kOutOfRange;
+  const uint32_t wbase = n0 + col < N ? (uint32_t)(col * K + 16 * g) : kOutOfRange;
   const int64_t ones = 0x0101010101010101LL;
   // Scales of the 16 columns through one buffer resource; this thread moves
   // scale (block tb, column tc) of each chunk, zero past K or past N.
@@ -272,10 +296,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_block_small_kernel(
       make_rsrc(Q4K ? (const void*)(Dp + (size_t)n0 * NB) : (const void*)(d16 + (size_t)n0 * NB), sbytes);
   const __amdgpu_buffer_rsrc_t rm = make_rsrc(Q4K ? (const void*)(Mp + (size_t)n0 * NB) : (const void*)d16,
                                               Q4K ? sbytes : 0);
-  const int tb = threadIdx.x >> 4, tc = threadIdx.x & 15;
+  // Consecutive threads take consecutive blocks of one column, so a wave's
+  // scale load reads a few contiguous runs instead of 16 scattered pieces.
+  const int tb = threadIdx.x % CH, tc = threadIdx.x / CH;
 
   const int pm = threadIdx.x >> 4, pn = threadIdx.x & 15;  // phase-2 output of this thread
   const bool chain = pm < M && n0 + pn < N;
+  const float sam = chain ? s_a[pm] : 0.0f;  // loaded early, used once at the end
   float f = 0.0f;
 
   struct Chunk {
@@ -284,10 +311,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_block_small_kernel(
   };
   auto load = [&](int b0, Chunk& c) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int b = b0 + wave + j * WAVES;
-      c.a[j] = __builtin_bit_cast(int64_t, __builtin_amdgcn_raw_buffer_load_b64(rq, qbase + 32 * b, 0, 0));
-      c.b[j] = __builtin_bit_cast(int64_t, __builtin_amdgcn_raw_buffer_load_b64(rw, wbase + 32 * b, 0, 0));
+    for (int j = 0; j < PER; j += 2) {
+      const int b = b0 + wave * PER + j;
+      const v4i x = __builtin_amdgcn_raw_buffer_load_b128(rq, qbase + 32 * b, 0, 0);
+      const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rw, wbase + 32 * b, 0, 0);
+      c.a[j] = ((int64_t)(uint32_t)x[1] << 32) | (uint32_t)x[0];
+      c.a[j + 1] = ((int64_t)(uint32_t)x[3] << 32) | (uint32_t)x[2];
+      c.b[j] = ((int64_t)(uint32_t)v[1] << 32) | (uint32_t)v[0];
+      c.b[j + 1] = ((int64_t)(uint32_t)v[3] << 32) | (uint32_t)v[2];
     }
     const uint32_t so = (b0 + tb < NB && n0 + tc < N) ? (uint32_t)(tc * NB + b0 + tb) * kSB : kOutOfRange;
     if constexpr (Q4K) {
@@ -299,18 +330,42 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_block_small_kernel(
     }
   };
   auto consume = [&](int b0, const Chunk& c) __attribute__((always_inline)) {
-    const int nb = NB - b0 < CH ? NB - b0 : CH;  // may be <= 0 for the padding chunk
+    const int nb = NB - b0 < CH ? NB - b0 : CH;
+    int64_t av[PER], bv[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      const int bl = wave + j * WAVES;
-      const v4i p = __builtin_amdgcn_mfma_i32_16x16x32_i8(c.a[j], c.b[j], v4i{0, 0, 0, 0}, 0, 0, 0);
+      av[j] = c.a[j];
+      bv[j] = c.b[j];
+    }
+    // Lanes 0-31 (g = 0, 1) loaded 16 bytes of block j, lanes 32-63 16
+    // bytes of block j + 1, as two 8-byte halves av[j] and av[j + 1].  A
+    // v_permlane32_swap of av[j + 1] on lanes 0-31 with av[j] on lanes 32-63
+    // leaves every lane with one 8-byte slice of block j in av[j] and one of
+    // block j + 1 in av[j + 1]; both operands move alike, so lane l holds the
+    // same k of A and B and each MFMA below sums exactly one block.
+#pragma unroll
+    for (int j = 0; j < PER; j += 2) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        int64_t& lo = h ? bv[j] : av[j];
+        int64_t& hi = h ? bv[j + 1] : av[j + 1];
+        const auto s0 = __builtin_amdgcn_permlane32_swap((uint32_t)lo, (uint32_t)hi, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap((uint32_t)(lo >> 32), (uint32_t)(hi >> 32), false, false);
+        lo = ((int64_t)s1[0] << 32) | (uint32_t)s0[0];
+        hi = ((int64_t)s1[1] << 32) | (uint32_t)s0[1];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int bl = wave * PER + j;
+      const v4i p = __builtin_amdgcn_mfma_i32_16x16x32_i8(av[j], bv[j], v4i{0, 0, 0, 0}, 0, 0, 0);
       if (bl < nb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (4 * g + i < M) pbuf[bl][4 * g + i][col] = p[i];
       }
       if constexpr (Q4K) {
-        const v4i sa = __builtin_amdgcn_mfma_i32_16x16x32_i8(c.a[j], ones, v4i{0, 0, 0, 0}, 0, 0, 0);
+        const v4i sa = __builtin_amdgcn_mfma_i32_16x16x32_i8(av[j], ones, v4i{0, 0, 0, 0}, 0, 0, 0);
         if (bl < nb && col == 0) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -334,15 +389,20 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_block_small_kernel(
     __syncthreads();  // the next chunk reuses the buffers
   };
 
-  Chunk c0, c1;
-  load(0, c0);
-  for (int b0 = 0; b0 < NB; b0 += 2 * CH) {
-    load(b0 + CH, c1);
-    consume(b0, c0);
-    load(b0 + 2 * CH, c0);
-    consume(b0 + CH, c1);
+  // Chunks past K load zero scales (and sums that are never stored); the
+  // loop stops at the first chunk past K, the same point for every thread.
+  Chunk c[RING];
+#pragma unroll
+  for (int r = 0; r < RING - 1; ++r) load(r * CH, c[r]);
+  for (int b0 = 0; b0 < NB; b0 += RING * CH) {
+#pragma unroll
+    for (int r = 0; r < RING; ++r) {
+      if (b0 + r * CH >= NB) break;
+      load(b0 + (r + RING - 1) * CH, c[(r + RING - 1) % RING]);
+      consume(b0 + r * CH, c[r]);
+    }
   }
-  if (chain) y[(size_t)pm * (size_t)N + (size_t)(n0 + pn)] = f * s_a[pm];
+  if (chain) y[(size_t)pm * (size_t)N + (size_t)(n0 + pn)] = f * sam;
 }
 
 }  // namespace
@@ -350,8 +410,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_block_small_kernel(
 int launch_gemm_block_small(const int8_t* q, const float* s_a, const int8_t* w, const uint16_t* d16,
                             const float* D, const float* Mn, float* y, int M, int N, int K, hipStream_t st) {
   const unsigned grid = (unsigned)((N + 15) / 16);
-  if (D) gemm_block_small_kernel<true, 8><<<grid, 512, 0, st>>>(q, s_a, w, nullptr, D, Mn, y, M, N, K);
-  else gemm_block_small_kernel<false, 8><<<grid, 512, 0, st>>>(q, s_a, w, d16, nullptr, nullptr, y, M, N, K);
+  // 4 waves (16-block chunks), two chunks in flight: the fastest of waves in
+  // {4, 8, 16} x ring depth in {2, 3, 4} at 17408 x 5120, M = 1 and 16.
+  if (D) gemm_block_small_kernel<true, 4, 2><<<grid, 256, 0, st>>>(q, s_a, w, nullptr, D, Mn, y, M, N, K);
+  else gemm_block_small_kernel<false, 4, 2><<<grid, 256, 0, st>>>(q, s_a, w, d16, nullptr, nullptr, y, M, N, K);
   return launch_status();
 }
 

@@ -176,7 +176,7 @@ def test_repack_q4_k(N, K):
     assert_same_floats(host(Mn), M_ref, "dmin * m")
 
 
-@pytest.mark.parametrize("M", [1, 7, 65, 129, 257])
+@pytest.mark.parametrize("M", [1, 7, 16, 17, 65, 129, 257])
 @pytest.mark.parametrize("N,K", [(100, 256), (300, 1024), (130, 2304)])
 def test_gemm_w4a8_q4k(M, N, K):
     """Q4_K bytes -> GPU repack -> GPU GEMM, against the oracle straight from the bytes."""
@@ -225,7 +225,7 @@ def test_w4a8(M, N, K):
     assert_same_floats(host(y), y_ref, "y")
 
 
-@pytest.mark.parametrize("M", [1, 7, 64, 65, 129, 257])
+@pytest.mark.parametrize("M", [1, 7, 16, 17, 64, 65, 129, 257])
 @pytest.mark.parametrize("N,K", [(16, 32), (100, 160), (300, 1056)])
 def test_w8a8_blockscale(M, N, K):
     c, q, s_a = _case(3, M, N, K, "block")

@@ -45,7 +45,7 @@ def _args():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy three times (scale for HBM byte counters)")
     ap.add_argument("--only", default=None, help="run only one kernel measurement (for profiling): "
-                    "step | w4a8 | block | repack | q4k | stress")
+                    "step | w4a8 | block | repack | q4k | decode | vendor | stress")
     return ap.parse_args()
 
 
@@ -365,9 +365,49 @@ def kernels(torch, prism, wl, only=None):
                                       gbs=nb / t / 1e9, hbm_frac=nb / t / 1e9 / PEAK_HBM_GBS,
                                       us_single_launch=t1 * 1e6, copies=R)
         del planes, srcs
+    if only in (None, "decode"):
+        # One activation row (decode) through the two projections of the step.
+        for name, c in (("proj_up", wl.proj_up()), ("proj_down", wl.proj_down())):
+            N, K = c["w"].shape
+            R = _copies(c["w"].nbytes)
+            ws = [T(c["w"]) for _ in range(R)]
+            sw = T(c["s_w"])
+            x = T(c["x"][:1].copy())
+            q = torch.empty((1, K), dtype=torch.int8, device=dev)
+            sa = torch.empty((1,), dtype=torch.float32, device=dev)
+            _check(L.quantize(x, q, sa)())
+            y = torch.empty((1, N), dtype=torch.float32, device=dev)
+            t1, t = _time_launches(torch, [L.w8a8(q, sa, w, sw, y) for w in ws], 100)
+            nbytes = N * K + 4 * N + K + 4 + 4 * N
+            out["decode_m1_" + name] = dict(us=t * 1e6, gbs=nbytes / t / 1e9, hbm_frac=nbytes / t / 1e9 / PEAK_HBM_GBS,
+                                            us_single_launch=t1 * 1e6, algorithmic_bytes=nbytes, copies=R)
+            del ws
+    if only in (None, "vendor"):
+        # Context: the vendor int8 GEMM (hipBLASLt through torch._int_mm) on the
+        # same shapes, int32 output only (no activation or weight scales, so it
+        # does less work than prism_gemm_w8a8); weights rotated as above.
+        g = torch.Generator(device=dev)
+        g.manual_seed(11)
+        for name, (M, N, K) in (("proj_up", (512, 9728, 2560)), ("proj_down", (512, 2560, 9728)),
+                                ("stress_m8192", (8192, 5120, 5120))):
+            R = _copies(N * K)
+            q = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev, generator=g)
+            wts = [torch.randint(-127, 128, (N, K), dtype=torch.int8, device=dev, generator=g) for _ in range(R)]
+            try:
+                def mm(wt):
+                    return lambda: (torch._int_mm(q, wt.t()), 0)[1]
+                t1, t = _time_launches(torch, [mm(wt) for wt in wts], 20)
+                out["vendor_int_mm_" + name] = dict(us=t * 1e6, tops=2 * M * N * K / t / 1e12,
+                                                    mfma_frac=2 * M * N * K / t / 1e12 / PEAK_INT8_TOPS,
+                                                    us_single_launch=t1 * 1e6, copies=R)
+            except RuntimeError as e:   # not every torch build exposes an int8 GEMM
+                out["vendor_int_mm_" + name] = dict(error=str(e)[:120])
+            del wts
     if only in (None, "stress"):
         st = wl.stress()
-        w, sw = T(st["w"]), T(st["s_w"])
+        R = _copies(st["w"].nbytes)
+        ws = [T(st["w"]) for _ in range(R)]   # rotated, so that no launch finds W in the MALL
+        sw = T(st["s_w"])
         K = N = 5120
         x_over, _ = wl.stress_overwrite(st)
         for M, xa in ((8192, x_over), (1, st["x_probe"][:1].copy())):
@@ -378,9 +418,9 @@ def kernels(torch, prism, wl, only=None):
             _, tqs = _time_launches(torch, [L.quantize_static(x, q, sa, 0.03)], 20)
             _check(L.quantize(x, q, sa)())   # the GEMM below runs on the per-row codes
             y = torch.empty((M, N), dtype=torch.float32, device=dev)
-            t1, t = _time_launches(torch, [L.w8a8(q, sa, w, sw, y)], 20 if M > 1 else 100)
+            t1, t = _time_launches(torch, [L.w8a8(q, sa, w, sw, y) for w in ws], 20 if M > 1 else 100)
             nbytes = N * K + 4 * N + M * K + 4 * M + 4 * M * N
-            out["stress_m%d" % M] = dict(us=t * 1e6, tops=2 * M * N * K / t / 1e12,
+            out["stress_m%d" % M] = dict(copies=R, us=t * 1e6, tops=2 * M * N * K / t / 1e12,
                                          mfma_frac=2 * M * N * K / t / 1e12 / PEAK_INT8_TOPS,
                                          gbs=nbytes / t / 1e9, hbm_frac=nbytes / t / 1e9 / PEAK_HBM_GBS,
                                          quantize_us=tq * 1e6, us_single_launch=t1 * 1e6,

@@ -405,6 +405,119 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_block_small_kernel(
   if (chain) y[(size_t)pm * (size_t)N + (size_t)(n0 + pn)] = f * sam;
 }
 
+// ---------------------------------------------------------------------------
+// M = 1 with int8 weights (a single activation row): one output per weight
+// row, so no MFMA tile has to cover 16 columns and the rows can be spread
+// evenly over all waves of the grid (each CU then reads an equal share of the
+// weights).  Wave j owns rows [j N / W, (j + 1) N / W) of the W waves and
+// streams each row with fully coalesced 16-byte loads (64 lanes = 1 KB per
+// load): lane l takes the 16-byte pieces l, l + 64, ... of the row.  Products
+// are summed with v_dot4_i32_i8 into an int32 per lane, then over the wave
+// with shuffles (integer addition: exact, any order).  Rows are processed in
+// groups of RG, the loads of the next group in flight while the current one
+// is summed.  Epilogue as everywhere: y = ((float)acc * s_a[0]) * s_w[n].
+// (With 4-bit weights the MFMA kernel is as fast: its rows are half as long.)
+template <int PL, int RG>
+__global__ __launch_bounds__(256) void gemv_kernel(const int8_t* __restrict__ q, const float* __restrict__ s_a,
+                                                   const int8_t* __restrict__ w, const float* __restrict__ s_w,
+                                                   float* __restrict__ y, int32_t* __restrict__ acc_out, int N,
+                                                   int K) {
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  const int r0 = (int)(gw * (int64_t)N / nw), r1 = (int)((gw + 1) * (int64_t)N / nw);
+  const int nrows = r1 - r0;  // at most 64 (the grid is sized for it)
+  const int P = K / 16;       // 16-byte pieces per row, at most 64 * PL
+
+  // The activation bytes of this lane's pieces.
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q, K);
+  v4i a[PL];
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const int pc = lane + 64 * i;
+    a[i] = bload(rq, pc < P ? (uint32_t)(16 * pc) : kOutOfRange);
+  }
+  const float sa = s_a[0];
+  const float sw = lane < nrows ? s_w[r0 + lane] : 0.0f;  // lane j: scale of row r0 + j
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + (size_t)r0 * (size_t)K, (int64_t)nrows * K);
+
+  auto load = [&](v4i (&b)[RG][PL], int j0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < RG; ++r)
+#pragma unroll
+      for (int i = 0; i < PL; ++i) {
+        const int pc = lane + 64 * i;
+        b[r][i] = bload(rw, (j0 + r < nrows && pc < P) ? (uint32_t)((j0 + r) * K + 16 * pc) : kOutOfRange);
+      }
+  };
+  auto sum = [&](const v4i (&b)[RG][PL], int j0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      if (j0 + r >= nrows) break;
+      int s = 0;
+#pragma unroll
+      for (int i = 0; i < PL; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s = __builtin_amdgcn_sdot4(a[i][e], b[r][i][e], s, false);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+      if (lane == j0 + r) {
+        const int n = r0 + j0 + r;
+        if (acc_out) acc_out[n] = s;
+        const float t = (float)s * sa;
+        y[n] = t * sw;
+      }
+    }
+  };
+
+  v4i b0[RG][PL], b1[RG][PL];
+  load(b0, 0);
+  for (int j0 = 0; j0 < nrows; j0 += 2 * RG) {
+    load(b1, j0 + RG);
+    sum(b0, j0);
+    if (j0 + RG >= nrows) break;
+    load(b0, j0 + 2 * RG);
+    sum(b1, j0 + RG);
+  }
+}
+
+// Returns false (nothing launched) for rows longer than 16 KB, which the
+// MFMA kernel takes.  Two workgroups of 4 waves per CU; one row per group
+// from 4 pieces per lane up (the fastest of groups of 1, 2, 4, 8 rows and 1,
+// 2, 4 workgroups per CU at N x K = 5120 x 5120, 2560 x 9728, 9728 x 2560 and
+// 17408 x 5120 on MI355X).
+bool launch_gemv(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc,
+                 int N, int K, hipStream_t st) {
+  const int pl = (K / 16 + 63) / 64;
+  const int64_t need = (N + 255) / 256;  // <= 64 rows per wave
+  const unsigned grid = (unsigned)(need > 512 ? need : 512);
+#define PRISM_GEMV(PLV, RGV)                                                                   \
+  case PLV:                                                                                    \
+    gemv_kernel<PLV, RGV><<<grid, 256, 0, st>>>(q, s_a, w, s_w, y, acc, N, K);                 \
+    return true;
+  switch (pl) {
+    PRISM_GEMV(1, 4)
+    PRISM_GEMV(2, 2)
+    PRISM_GEMV(3, 2)
+    PRISM_GEMV(4, 1)
+    PRISM_GEMV(5, 1)
+    PRISM_GEMV(6, 1)
+    PRISM_GEMV(7, 1)
+    PRISM_GEMV(8, 1)
+    PRISM_GEMV(9, 1)
+    PRISM_GEMV(10, 1)
+    PRISM_GEMV(11, 1)
+    PRISM_GEMV(12, 1)
+    PRISM_GEMV(13, 1)
+    PRISM_GEMV(14, 1)
+    PRISM_GEMV(15, 1)
+    PRISM_GEMV(16, 1)
+    default:
+      return false;
+  }
+#undef PRISM_GEMV
+}
+
 }  // namespace
 
 int launch_gemm_block_small(const int8_t* q, const float* s_a, const int8_t* w, const uint16_t* d16,
@@ -427,6 +540,8 @@ int launch_gemm_small_variant(const int8_t* q, const float* s_a, const void* w, 
 
 int launch_gemm_small(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
                       float* y, int32_t* acc, int M, int N, int K, hipStream_t st) {
+  if (M == 1 && !w_is_int4 && launch_gemv(q, s_a, static_cast<const int8_t*>(w), s_w, y, acc, N, K, st))
+    return launch_status();
   int cb, waves;
   choose_small(M, N, K, w_is_int4, cb, waves);
   return launch_gemm_small_variant(q, s_a, w, w_is_int4, s_w, y, acc, M, N, K, cb, waves, st);

@@ -239,6 +239,37 @@ def test_w8a8_blockscale(M, N, K):
     assert_same_floats(host(y2), y_ref, "y without partials")
 
 
+@pytest.mark.parametrize("w4", [False, True])
+@pytest.mark.parametrize("N,K", [(1, 32), (257, 1024), (1000, 1056), (3000, 4096), (700, 9728), (300, 16384),
+                                 (200, 16416), (100, 32768), (90, 32800), (70000, 32)])
+def test_single_row(w4, N, K):
+    """M = 1: int8 weights take the row-streaming kernel (one output per row,
+    rows spread over all waves) up to 16 KB rows and the MFMA kernel past
+    that; 4-bit weights the MFMA kernel.  Row-length classes on both sides of
+    the hand-over, against the oracle, with -128 codes."""
+    rng = np.random.default_rng(N * 7 + K + w4)
+    q = rng.integers(-128, 128, (1, K), dtype=np.int8)
+    q[0, :8] = -128
+    s_a = rng.uniform(1e-3, 1e-2, 1).astype(np.float32)
+    s_w = wl.channel_scales(rng, N)
+    if w4:
+        w = rng.integers(-8, 8, (N, K), dtype=np.int8)
+        w[:, :8] = -8
+        wp = wl.pack_int4(w)
+        y_ref, acc_ref = oracle.gemm_w4a8(q, s_a, wp, s_w)
+        acc = torch.empty((1, N), dtype=torch.int32, device=DEV)
+        y = prism.gemm_w4a8(dev(q), dev(s_a), dev(wp), dev(s_w), acc=acc)
+    else:
+        w = rng.integers(-128, 128, (N, K), dtype=np.int8)
+        w[:, :8] = -128
+        y_ref, acc_ref = oracle.gemm_w8a8(q, s_a, w, s_w)
+        acc = torch.empty((1, N), dtype=torch.int32, device=DEV)
+        y = prism.gemm_w8a8(dev(q), dev(s_a), dev(w), dev(s_w), acc=acc)
+    torch.cuda.synchronize()
+    assert_same_ints(host(acc), acc_ref, "acc")
+    assert_same_floats(host(y), y_ref, "y")
+
+
 def test_full_int8_range_and_largest_k():
     """-128 codes and weights (valid inputs, though the quantizer never makes -128)
     and the largest accepted K: the exact sums reach K * 16384 < 2^31."""

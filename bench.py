@@ -95,6 +95,13 @@ class Launcher:
                                           self.stream)
         return lambda: f(*a)
 
+    def quantize_w8a8(self, x, q, sa, w, sw, y):
+        M, K = x.shape
+        N = w.shape[0]
+        f, a = self.lib.prism_quantize_gemm_w8a8, (self.p(x), self.p(q), self.p(sa), self.p(w), self.p(sw), self.p(y),
+                                                   None, M, N, K, self.stream)
+        return lambda: f(*a)
+
     def w4a8(self, q, sa, w4, sw, y):
         M, K = q.shape
         N = w4.shape[0]
@@ -121,7 +128,8 @@ def _copies(bytes_per_set):
 
 # Sources of the GEMM kernels: a traffic figure is used only if it was
 # measured on exactly these sources.
-KERNEL_SOURCES = ["gemm_tiled_kernels.h", "gemm_tiled.hip", "gemm_small.hip", "prism_abi.cpp", "prism_internal.h"]
+KERNEL_SOURCES = ["gemm_tiled_kernels.h", "gemm_tiled.hip", "gemm_small.hip", "prism_abi.cpp", "prism_internal.h",
+                  "quant_math.h"]
 
 
 def _src_hash(names):
@@ -381,6 +389,16 @@ def kernels(torch, prism, wl, only=None):
             nbytes = N * K + 4 * N + K + 4 + 4 * N
             out["decode_m1_" + name] = dict(us=t * 1e6, gbs=nbytes / t / 1e9, hbm_frac=nbytes / t / 1e9 / PEAK_HBM_GBS,
                                             us_single_launch=t1 * 1e6, algorithmic_bytes=nbytes, copies=R)
+            # the whole decode step of this projection: quantize x, then the GEMM
+            pairs = []
+            for w in ws:
+                fq, fg = L.quantize(x, q, sa), L.w8a8(q, sa, w, sw, y)
+                pairs.append(lambda fq=fq, fg=fg: fq() or fg())
+            _, t2 = _time_launches(torch, pairs, 100)
+            _, t3 = _time_launches(torch, [L.quantize_w8a8(x, q, sa, w, sw, y) for w in ws], 100)
+            nbytes_x = nbytes - K - 4 + 4 * K   # x read as fp32 instead of the codes
+            out["decode_m1_" + name].update(quantize_then_gemm_us=t2 * 1e6, fused_quantize_gemm_us=t3 * 1e6,
+                                            fused_hbm_frac=nbytes_x / t3 / 1e9 / PEAK_HBM_GBS)
             del ws
     if only in (None, "vendor"):
         # Context: the vendor int8 GEMM (hipBLASLt through torch._int_mm) on the

@@ -26,6 +26,7 @@
 //    recovers acc;
 //  * epilogue per element, in a fixed order: y = ((float)acc * s_a[m]) * s_w[n].
 #include "prism_internal.h"
+#include "quant_math.h"
 #include "../../include/prism.h"
 
 namespace prism {
@@ -417,11 +418,19 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_block_small_kernel(
 // groups of RG, the loads of the next group in flight while the current one
 // is summed.  Epilogue as everywhere: y = ((float)acc * s_a[0]) * s_w[n].
 // (With 4-bit weights the MFMA kernel is as fast: its rows are half as long.)
-template <int PL, int RG>
-__global__ __launch_bounds__(256) void gemv_kernel(const int8_t* __restrict__ q, const float* __restrict__ s_a,
-                                                   const int8_t* __restrict__ w, const float* __restrict__ s_w,
-                                                   float* __restrict__ y, int32_t* __restrict__ acc_out, int N,
-                                                   int K) {
+//
+// FUSED: the row arrives as fp32 x and every workgroup quantizes it itself,
+// into LDS, with the quantizer's arithmetic (quant_math.h): absmax over the
+// row, s = amax / 127, codes clamp(rint(x / s)).  The x loads go out first
+// and the first weight rows right after them, so the quantization runs
+// while those weights are in flight.  Workgroup 0 also writes the codes and the
+// scale to q and s_a, which then hold what prism_quantize_rows would write.
+template <int PL, int RG, bool FUSED>
+__global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, int8_t* __restrict__ q_out,
+                                                   float* __restrict__ s_out, const int8_t* __restrict__ q,
+                                                   const float* __restrict__ s_a, const int8_t* __restrict__ w,
+                                                   const float* __restrict__ s_w, float* __restrict__ y,
+                                                   int32_t* __restrict__ acc_out, int N, int K) {
   const int lane = threadIdx.x & 63;
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t nw = (int64_t)gridDim.x * 4;
@@ -429,17 +438,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(const int8_t* __restrict__ q,
   const int nrows = r1 - r0;  // at most 64 (the grid is sized for it)
   const int P = K / 16;       // 16-byte pieces per row, at most 64 * PL
 
-  // The activation bytes of this lane's pieces.
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q, K);
-  v4i a[PL];
-#pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const int pc = lane + 64 * i;
-    a[i] = bload(rq, pc < P ? (uint32_t)(16 * pc) : kOutOfRange);
-  }
-  const float sa = s_a[0];
   const float sw = lane < nrows ? s_w[r0 + lane] : 0.0f;  // lane j: scale of row r0 + j
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + (size_t)r0 * (size_t)K, (int64_t)nrows * K);
+  v4i a[PL];  // the activation bytes of this lane's pieces
+  float sa;   // the row scale
 
   auto load = [&](v4i (&b)[RG][PL], int j0) __attribute__((always_inline)) {
 #pragma unroll
@@ -471,7 +473,64 @@ __global__ __launch_bounds__(256) void gemv_kernel(const int8_t* __restrict__ q,
   };
 
   v4i b0[RG][PL], b1[RG][PL];
-  load(b0, 0);
+  if constexpr (FUSED) {
+    __shared__ __attribute__((aligned(16))) uint32_t codes[256 * PL];  // K bytes at most
+    __shared__ float red_max[4];
+    __shared__ int red_fin[4];
+    const int nf4 = K / 4;
+    const float4* xr = reinterpret_cast<const float4*>(x);
+    float4 v[PL];
+#pragma unroll
+    for (int j = 0; j < PL; ++j) {
+      const int f = threadIdx.x + 256 * j;
+      v[j] = f < nf4 ? xr[f] : float4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    load(b0, 0);
+    float amax = 0.0f;
+    bool finite = true;
+#pragma unroll
+    for (int j = 0; j < PL; ++j) {
+      amax = fmaxf(amax, quant::absmax4(v[j]));
+      finite = finite && quant::finite4(v[j]);
+    }
+    amax = quant::wave_max(amax);
+    finite = __all(finite);
+    const int wave = threadIdx.x >> 6;
+    if (lane == 0) {
+      red_max[wave] = amax;
+      red_fin[wave] = finite ? 1 : 0;
+    }
+    __syncthreads();
+    amax = fmaxf(fmaxf(red_max[0], red_max[1]), fmaxf(red_max[2], red_max[3]));
+    finite = (red_fin[0] & red_fin[1] & red_fin[2] & red_fin[3]) != 0;
+    sa = quant::row_scale(amax, finite);
+    const bool zero = !finite || sa == 0.0f;
+#pragma unroll
+    for (int j = 0; j < PL; ++j) {
+      const int f = threadIdx.x + 256 * j;
+      if (f < nf4) {
+        const uint32_t c = zero ? 0u : quant::pack4(v[j], sa);
+        codes[f] = c;
+        if (blockIdx.x == 0) reinterpret_cast<uint32_t*>(q_out)[f] = c;
+      }
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) s_out[0] = sa;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int pc = lane + 64 * i;
+      a[i] = pc < P ? *reinterpret_cast<const v4i*>(codes + 4 * pc) : v4i{0, 0, 0, 0};
+    }
+  } else {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q, K);
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int pc = lane + 64 * i;
+      a[i] = bload(rq, pc < P ? (uint32_t)(16 * pc) : kOutOfRange);
+    }
+    sa = s_a[0];
+    load(b0, 0);
+  }
   for (int j0 = 0; j0 < nrows; j0 += 2 * RG) {
     load(b1, j0 + RG);
     sum(b0, j0);
@@ -486,14 +545,22 @@ __global__ __launch_bounds__(256) void gemv_kernel(const int8_t* __restrict__ q,
 // from 4 pieces per lane up (the fastest of groups of 1, 2, 4, 8 rows and 1,
 // 2, 4 workgroups per CU at N x K = 5120 x 5120, 2560 x 9728, 9728 x 2560 and
 // 17408 x 5120 on MI355X).
-bool launch_gemv(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc,
-                 int N, int K, hipStream_t st) {
+// x non-null: the fused form (x quantized inside, codes and scale also
+// written to q and s_a).
+bool launch_gemv(const float* x, int8_t* q_out, float* s_out, const int8_t* q, const float* s_a, const int8_t* w,
+                 const float* s_w, float* y, int32_t* acc, int N, int K, hipStream_t st) {
   const int pl = (K / 16 + 63) / 64;
   const int64_t need = (N + 255) / 256;  // <= 64 rows per wave
-  const unsigned grid = (unsigned)(need > 512 ? need : 512);
-#define PRISM_GEMV(PLV, RGV)                                                                   \
-  case PLV:                                                                                    \
-    gemv_kernel<PLV, RGV><<<grid, 256, 0, st>>>(q, s_a, w, s_w, y, acc, N, K);                 \
+  // Two workgroups per CU; one when fused with rows over 5 KB, since every
+  // workgroup quantizes the whole row again (measured at K = 2560 and 9728).
+  const int64_t base = x && pl > 5 ? 256 : 512;
+  const unsigned grid = (unsigned)(need > base ? need : base);
+#define PRISM_GEMV(PLV, RGV)                                                                                  \
+  case PLV:                                                                                                   \
+    if (x)                                                                                                    \
+      gemv_kernel<PLV, RGV, true><<<grid, 256, 0, st>>>(x, q_out, s_out, nullptr, nullptr, w, s_w, y, acc, N, K); \
+    else                                                                                                      \
+      gemv_kernel<PLV, RGV, false><<<grid, 256, 0, st>>>(nullptr, nullptr, nullptr, q, s_a, w, s_w, y, acc, N, K); \
     return true;
   switch (pl) {
     PRISM_GEMV(1, 4)
@@ -540,11 +607,19 @@ int launch_gemm_small_variant(const int8_t* q, const float* s_a, const void* w, 
 
 int launch_gemm_small(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
                       float* y, int32_t* acc, int M, int N, int K, hipStream_t st) {
-  if (M == 1 && !w_is_int4 && launch_gemv(q, s_a, static_cast<const int8_t*>(w), s_w, y, acc, N, K, st))
+  if (M == 1 && !w_is_int4 &&
+      launch_gemv(nullptr, nullptr, nullptr, q, s_a, static_cast<const int8_t*>(w), s_w, y, acc, N, K, st))
     return launch_status();
   int cb, waves;
   choose_small(M, N, K, w_is_int4, cb, waves);
   return launch_gemm_small_variant(q, s_a, w, w_is_int4, s_w, y, acc, M, N, K, cb, waves, st);
+}
+
+// Quantize + GEMM of one row in one kernel when the row fits the
+// single-row kernel (K <= 16384); otherwise nothing is launched.
+bool launch_quantize_gemv(const float* x, int8_t* q, float* s_a, const int8_t* w, const float* s_w, float* y,
+                          int32_t* acc, int N, int K, hipStream_t st) {
+  return launch_gemv(x, q, s_a, nullptr, nullptr, w, s_w, y, acc, N, K, st);
 }
 
 }  // namespace prism

@@ -175,6 +175,24 @@ int prism_gemm_w8a8(const int8_t* q, const float* s_a, const int8_t* w, const fl
   return prism::launch_gemm_tiled(q, s_a, w, false, s_w, y, acc, (int)M, (int)N, (int)K, s);
 }
 
+int prism_quantize_gemm_w8a8(const float* x, int8_t* q, float* scale, const int8_t* w, const float* s_w, float* y,
+                             int32_t* acc, int64_t M, int64_t N, int64_t K, void* stream) {
+  bool noop;
+  int st = check_gemm(q, scale, w, s_w, y, acc, M, N, K, 16, &noop);
+  if (st != PRISM_OK || noop) return st;
+  if (!x) return PRISM_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(s_w, 4)) return PRISM_ERR_ALIGNMENT;
+  if (!grid_fits(M, N)) return PRISM_ERR_INVALID_ARG;
+  if ((st = check_device()) != PRISM_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M == 1 && prism::launch_quantize_gemv(x, q, scale, w, s_w, y, acc, (int)N, (int)K, s))
+    return prism::launch_status();
+  if ((st = prism::launch_quantize_rows(x, q, scale, M, K, s)) != PRISM_OK) return st;
+  if (M <= prism::kSmallMMax)
+    return prism::launch_gemm_small(q, scale, w, false, s_w, y, acc, (int)M, (int)N, (int)K, s);
+  return prism::launch_gemm_tiled(q, scale, w, false, s_w, y, acc, (int)M, (int)N, (int)K, s);
+}
+
 int prism_gemm_w4a8(const int8_t* q, const float* s_a, const uint8_t* w4, const float* s_w, float* y, int32_t* acc,
                     int64_t M, int64_t N, int64_t K, void* stream) {
   bool noop;

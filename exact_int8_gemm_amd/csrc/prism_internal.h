@@ -32,6 +32,11 @@ int launch_repack_q8_0(const uint8_t* blocks, int8_t* w, uint16_t* d, int64_t N,
 
 int launch_gemm_small(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
                       float* y, int32_t* acc, int M, int N, int K, hipStream_t st);
+// One row (M = 1), int8 weights: quantize x and multiply in one kernel, also
+// writing the codes to q and the scale to s_a.  False (nothing launched) when
+// K is too long for it.
+bool launch_quantize_gemv(const float* x, int8_t* q, float* s_a, const int8_t* w, const float* s_w, float* y,
+                          int32_t* acc, int N, int K, hipStream_t st);
 
 int launch_gemm_tiled(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
                       float* y, int32_t* acc, int M, int N, int K, hipStream_t st);

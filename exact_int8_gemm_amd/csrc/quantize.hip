@@ -21,46 +21,16 @@
 // overflowing x / s gives +-127), and only a NaN marks a row (scale NaN,
 // zero codes).  The same kernels run both forms; the static one skips the
 // absmax and reduces a "no NaN" flag instead.
-#include "prism_internal.h"
+#include "quant_math.h"
 #include "../../include/prism.h"
 
 namespace prism {
 namespace {
 
+using namespace quant;
+
 constexpr int kMaxThreads = 1024;
 constexpr int kMaxCpt = 16;  // float4 per thread kept in registers: K <= 65536
-
-__device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
-}
-
-__device__ inline int code_of(float x, float s) {
-  float r = rintf(x / s);
-  r = fminf(fmaxf(r, -127.0f), 127.0f);
-  return (int)r;
-}
-
-__device__ inline uint32_t pack4(const float4 v, float s) {
-  uint32_t b0 = (uint32_t)(code_of(v.x, s) & 0xff);
-  uint32_t b1 = (uint32_t)(code_of(v.y, s) & 0xff);
-  uint32_t b2 = (uint32_t)(code_of(v.z, s) & 0xff);
-  uint32_t b3 = (uint32_t)(code_of(v.w, s) & 0xff);
-  return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
-}
-
-__device__ inline bool finite4(const float4 v) {
-  return isfinite(v.x) && isfinite(v.y) && isfinite(v.z) && isfinite(v.w);
-}
-
-__device__ inline bool nonan4(const float4 v) {
-  return !isnan(v.x) && !isnan(v.y) && !isnan(v.z) && !isnan(v.w);
-}
-
-__device__ inline float absmax4(const float4 v) {
-  return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-}
 
 // Row absmax and finiteness over the whole workgroup; every thread gets the
 // same answer.
@@ -116,7 +86,7 @@ __global__ __launch_bounds__(kMaxThreads) void quantize_rows_reg(const float* __
   }
   row_reduce(amax, finite);
 
-  const float sc = finite ? (STATIC ? fixed : amax / 127.0f) : __builtin_nanf("");
+  const float sc = STATIC ? (finite ? fixed : __builtin_nanf("")) : row_scale(amax, finite);
   if (threadIdx.x == 0) s[row] = sc;
   const bool zero = !finite || sc == 0.0f;
 #pragma unroll
@@ -149,7 +119,7 @@ __global__ __launch_bounds__(kMaxThreads) void quantize_rows_2pass(const float* 
   }
   row_reduce(amax, finite);
 
-  const float sc = finite ? (STATIC ? fixed : amax / 127.0f) : __builtin_nanf("");
+  const float sc = STATIC ? (finite ? fixed : __builtin_nanf("")) : row_scale(amax, finite);
   if (threadIdx.x == 0) s[row] = sc;
   const bool zero = !finite || sc == 0.0f;
   for (int64_t c = threadIdx.x; c < nchunk; c += blockDim.x) qr[c] = zero ? 0u : pack4(xr[c], sc);

@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libprism.so")
 
 PRISM_OK = 0
-ABI_VERSION = 2
+ABI_VERSION = 3
 K_MAX = 131040
 
 # Dispatch-table entries of the W8A8 / W4A8 calls (PRISM_VARIANT_* in include/prism.h).
@@ -52,6 +52,8 @@ def _declare(lib):
     lib.prism_repack_q4_k.argtypes = [p, p, p, p, i64, i64, p]
     lib.prism_gemm_w4a8_q4k.restype = i32
     lib.prism_gemm_w4a8_q4k.argtypes = [p, p, p, p, p, p, i64, i64, i64, p]
+    lib.prism_quantize_gemm_w8a8.restype = i32
+    lib.prism_quantize_gemm_w8a8.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, p]
     for name in ("prism_gemm_w8a8_variant", "prism_gemm_w4a8_variant"):
         fn = getattr(lib, name)
         fn.restype = i32
@@ -242,6 +244,28 @@ def gemm_w4a8_variant(q, s_a, w4, s_w, variant, y=None, acc=None):
         _check(lib().prism_gemm_w4a8_variant(_ptr(q), _ptr(s_a), _ptr(w4), _ptr(s_w), _ptr(y), _ptr(acc), M, N, K,
                                              VARIANTS[variant], _stream(dev)))
     return y
+
+
+def quantize_gemm_w8a8(x, w, s_w, y=None, q=None, scale=None, acc=None):
+    """Quantize x f32 [M,K] per row and multiply by int8 w [N,K] with s_w f32 [N] in one call:
+    the bits of ``quantize_rows`` then ``gemm_w8a8``.  Returns (y, q, scale); q and scale are
+    the quantizer's outputs.  M = 1 (decode) runs as one kernel."""
+    dev = _gpu(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    M, K = x.shape
+    _need(x, "x", torch.float32, (M, K), dev)
+    q = torch.empty((M, K), dtype=torch.int8, device=dev) if q is None else _need(q, "q", torch.int8, (M, K), dev)
+    scale = (torch.empty((M,), dtype=torch.float32, device=dev) if scale is None
+             else _need(scale, "scale", torch.float32, (M,), dev))
+    dev, M, N, K = _gemm_args(q, scale, w, lambda k: k, torch.int8, "s_w", s_w, torch.float32, lambda n, k: (n,))
+    y = torch.empty((M, N), dtype=torch.float32, device=dev) if y is None else _need(y, "y", torch.float32, (M, N), dev)
+    if acc is not None:
+        _need(acc, "acc", torch.int32, (M, N), dev)
+    with torch.cuda.device(dev):
+        _check(lib().prism_quantize_gemm_w8a8(_ptr(x), _ptr(q), _ptr(scale), _ptr(w), _ptr(s_w), _ptr(y), _ptr(acc),
+                                              M, N, K, _stream(dev)))
+    return y, q, scale
 
 
 def gemm_w4a8(q, s_a, w4, s_w, y=None, acc=None):

@@ -41,7 +41,7 @@ extern "C" {
 #endif
 
 /* Bumped on any change of a signature or of the semantics below. */
-#define PRISM_ABI_VERSION 2
+#define PRISM_ABI_VERSION 3
 
 /* Largest accepted K.  For K <= 131040 every exact sum of K products of two
  * int8 values (|q|, |w| <= 128) lies strictly inside the int32 range. */
@@ -168,6 +168,22 @@ int prism_gemm_w8a8(const int8_t* q, const float* s_a, const int8_t* w, const fl
 int prism_gemm_w8a8_blockscale(const int8_t* q, const float* s_a, const int8_t* w,
                                const uint16_t* d, float* y, int32_t* partials,
                                int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * Quantize + W8A8 GEMM in one call (the README's "Quick start" int8
+ * activations feeding the exact int32 GEMM of "Why StartLux-Prism").
+ *   x     [M][K] fp32 activations (16-byte aligned).
+ *   q     [M][K] int8 and scale [M] fp32 outputs: what prism_quantize_rows
+ *         writes for x.
+ *   w, s_w, y, acc: as for prism_gemm_w8a8 (acc may be NULL).
+ * The results are those of prism_quantize_rows(x) followed by
+ * prism_gemm_w8a8 on its outputs, bit for bit.  With M = 1 and K <= 16384
+ * this is one kernel that quantizes the row on chip while the first weight
+ * rows stream in (decode); otherwise the two steps run as two launches on
+ * `stream`.  K must be a multiple of 16.
+ */
+int prism_quantize_gemm_w8a8(const float* x, int8_t* q, float* scale, const int8_t* w, const float* s_w,
+                             float* y, int32_t* acc, int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
  * W4A8 GEMM on packed signed 4-bit weights (README "Why StartLux-Prism":

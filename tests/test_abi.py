@@ -43,7 +43,7 @@ def test_header_declares_every_call():
     names = set(_declared_functions())
     assert {"prism_quantize_rows", "prism_quantize_rows_static", "prism_repack_q8_0", "prism_gemm_w8a8",
             "prism_gemm_w8a8_blockscale", "prism_gemm_w4a8", "prism_gemm_w8a8_variant", "prism_gemm_w4a8_variant",
-            "prism_repack_q4_k", "prism_gemm_w4a8_q4k",
+            "prism_repack_q4_k", "prism_gemm_w4a8_q4k", "prism_quantize_gemm_w8a8",
             "prism_abi_version", "prism_status_string"} <= names
 
 
@@ -82,6 +82,8 @@ lib.prism_repack_q4_k.restype = i32
 lib.prism_repack_q4_k.argtypes = [p, p, p, p, i64, i64, p]
 lib.prism_gemm_w4a8_q4k.restype = i32
 lib.prism_gemm_w4a8_q4k.argtypes = [p, p, p, p, p, p, i64, i64, i64, p]
+lib.prism_quantize_gemm_w8a8.restype = i32
+lib.prism_quantize_gemm_w8a8.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, p]
 for n in ("prism_gemm_w8a8_variant", "prism_gemm_w4a8_variant"):
     getattr(lib, n).restype = i32
     getattr(lib, n).argtypes = [p, p, p, p, p, p, i64, i64, i64, i32, p]
@@ -191,6 +193,37 @@ CASES += [
 ]
 
 
+_QG = "prism_quantize_gemm_w8a8"
+
+
+def _qg(x=A, q=A, scale=A, w=A, sw=A, y=A, acc=None, M=1, N=16, K=64):
+    return [x, q, scale, w, sw, y, acc, M, N, K, None]
+
+
+CASES += [
+    (_QG, _qg(M=0), OK),
+    (_QG, _qg(None, None, None, None, None, None, None, 0, 16, 64), OK),
+    (_QG, _qg(M=-1), INVALID),
+    (_QG, _qg(N=0), INVALID),
+    (_QG, _qg(K=0), INVALID),
+    (_QG, _qg(K=131040 + 16), INVALID),
+    (_QG, _qg(x=None), INVALID),
+    (_QG, _qg(q=None), INVALID),
+    (_QG, _qg(scale=None), INVALID),
+    (_QG, _qg(w=None), INVALID),
+    (_QG, _qg(sw=None), INVALID),
+    (_QG, _qg(y=None), INVALID),
+    (_QG, _qg(K=40), ALIGN),
+    (_QG, _qg(x=A + 4), ALIGN),
+    (_QG, _qg(q=A + 8), ALIGN),
+    (_QG, _qg(scale=A + 2), ALIGN),
+    (_QG, _qg(w=A + 8), ALIGN),
+    (_QG, _qg(sw=A + 2), ALIGN),
+    (_QG, _qg(y=A + 2), ALIGN),
+    (_QG, _qg(acc=A + 2), ALIGN),
+]
+
+
 def _v(variant, **kw):
     a = _g(**kw)
     return a[:9] + [variant, None]
@@ -277,11 +310,11 @@ def test_valid_call_without_a_device_is_unsupported(built):
                           ["prism_quantize_rows_static", [A, A, A, 0.25, 4, 64, None]],
                           ["prism_repack_q8_0", [A, A, A, 4, 64, None]],
                           ["prism_gemm_w8a8_variant", _g()[:9] + [7, None]],
-                          ["prism_gemm_w4a8_q4k", _k()]])
+                          ["prism_gemm_w4a8_q4k", _k()], [_QG, _qg()]])
     out = subprocess.run([sys.executable, "-c", _CHILD, built, payload], env=env, capture_output=True, text=True,
                          timeout=120)
     assert out.returncode == 0, out.stderr
-    assert json.loads(out.stdout.strip().splitlines()[-1])["status"] == [UNSUP, UNSUP, UNSUP, UNSUP, UNSUP, UNSUP]
+    assert json.loads(out.stdout.strip().splitlines()[-1])["status"] == [UNSUP] * 7
 
 
 def test_build_uses_result_defining_flags():

@@ -270,6 +270,67 @@ def test_single_row(w4, N, K):
     assert_same_floats(host(y), y_ref, "y")
 
 
+def _special_row(kind, K, rng):
+    x = rng.standard_normal(K).astype(np.float32)
+    if kind == "zero":
+        x[:] = 0.0
+    elif kind == "nan":
+        x[K // 3] = np.nan
+    elif kind == "inf":
+        x[K - 1] = -np.inf
+    elif kind == "tiny":          # amax / 127 underflows to a subnormal scale
+        x = (x * np.float32(1e-39)).astype(np.float32)
+    elif kind == "huge":
+        x = (x * np.float32(1e37)).astype(np.float32)
+    elif kind == "ties":          # x / s lands on k + 1/2 for s = 1: amax 127
+        x[:] = 0.5
+        x[0] = 127.0
+        x[1::7] = -2.5
+    return x
+
+
+@pytest.mark.parametrize("N,K", [(1, 16), (700, 1024), (300, 1040), (3000, 5120), (2560, 9728), (257, 16384),
+                                 (100, 16400), (70000, 32)])
+@pytest.mark.parametrize("kind", ["normal", "zero", "nan", "inf", "tiny", "huge", "ties"])
+def test_quantize_gemm_single_row(N, K, kind):
+    """One call that quantizes x and multiplies (one kernel for M = 1 up to K = 16384, two
+    launches past that): y, acc, the codes and the scale equal the oracle's quantize-then-GEMM
+    and the library's two separate calls, bit for bit, also for rows the quantizer marks."""
+    rng = np.random.default_rng(N + K + len(kind))
+    x = _special_row(kind, K, rng)[None, :]
+    w = rng.integers(-128, 128, (N, K), dtype=np.int8)
+    s_w = wl.channel_scales(rng, N)
+    q_ref, s_ref = oracle.quantize_rows(x)
+    y_ref, acc_ref = oracle.gemm_w8a8(q_ref, s_ref, w, s_w)
+    xd, wd, swd = dev(x), dev(w), dev(s_w)
+    acc = torch.empty((1, N), dtype=torch.int32, device=DEV)
+    y, q, s = prism.quantize_gemm_w8a8(xd, wd, swd, acc=acc)
+    q2, s2 = prism.quantize_rows(xd)
+    y2 = prism.gemm_w8a8(q2, s2, wd, swd)
+    torch.cuda.synchronize()
+    assert_same_ints(host(q), q_ref, "q")
+    assert_same_floats(host(s), s_ref, "scale")
+    assert_same_ints(host(acc), acc_ref, "acc")
+    assert_same_floats(host(y), y_ref, "y")
+    assert_same_floats(host(y), host(y2), "y against the two-call path")
+
+
+@pytest.mark.parametrize("M,N,K", [(2, 300, 1040), (7, 1000, 5120), (100, 257, 2064), (300, 130, 4096)])
+def test_quantize_gemm_several_rows(M, N, K):
+    c = wl.random_case(M + N + K, M, N, K, "w8a8")
+    c["x"][M // 2] = 0.0
+    c["x"][M - 1, 5] = np.nan
+    q_ref, s_ref = oracle.quantize_rows(c["x"])
+    y_ref, acc_ref = oracle.gemm_w8a8(q_ref, s_ref, c["w"], c["s_w"])
+    acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    y, q, s = prism.quantize_gemm_w8a8(dev(c["x"]), dev(c["w"]), dev(c["s_w"]), acc=acc)
+    torch.cuda.synchronize()
+    assert_same_ints(host(q), q_ref, "q")
+    assert_same_floats(host(s), s_ref, "scale")
+    assert_same_ints(host(acc), acc_ref, "acc")
+    assert_same_floats(host(y), y_ref, "y")
+
+
 def test_full_int8_range_and_largest_k():
     """-128 codes and weights (valid inputs, though the quantizer never makes -128)
     and the largest accepted K: the exact sums reach K * 16384 < 2^31."""

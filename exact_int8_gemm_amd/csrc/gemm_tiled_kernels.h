@@ -806,22 +806,31 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_block_kernel(const int
         const uint32_t hbits = *reinterpret_cast<const uint32_t*>(buf + kDOff + (ks * BN + ncol[j]) * 4);
         dv[j] = half_bits_to_float((uint16_t)hbits);
       }
+      // All MFMAs of the block first, then the folds at a raised wave
+      // priority: the workgroups sharing a SIMD then tend to alternate, one
+      // folding on the VALU while the other's MFMAs run.
+      v16i p[C::kTM][C::kTN];
+#pragma unroll
+      for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kTN; ++j) p[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], zero, 0, 0, 0);
+      __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int i = 0; i < C::kTM; ++i)
 #pragma unroll
         for (int j = 0; j < C::kTN; ++j) {
-          const v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], zero, 0, 0, 0);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) f[i][j][r] = __builtin_fmaf((float)p[r], dv[j], f[i][j][r]);
+          for (int r = 0; r < 16; ++r) f[i][j][r] = __builtin_fmaf((float)p[i][j][r], dv[j], f[i][j][r]);
           if constexpr (PARTIALS) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int m = m0 + wm * C::kWTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
               const int n = n0 + ncol[j];
-              if (m < M && n < N && b < NB) partials[((size_t)m * (size_t)N + (size_t)n) * (size_t)NB + b] = p[r];
+              if (m < M && n < N && b < NB) partials[((size_t)m * (size_t)N + (size_t)n) * (size_t)NB + b] = p[i][j][r];
             }
           }
         }
+      __builtin_amdgcn_s_setprio(0);
     }
   };
   auto step = [&](const int8_t* cur, int8_t* nxt, int stage) __attribute__((always_inline)) {

@@ -22,7 +22,8 @@ M_SWEEP = [1, 2, 3, 7, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255
 # ------------------------------------------------------------------ quantizer
 
 @pytest.mark.parametrize("M,K", [(1, 16), (5, 48), (64, 256), (3, 512), (33, 2560), (8, 9728), (4, 10240),
-                                 (4, 10256), (2, 20480), (300, 512), (2, 65536), (2, 65552), (3, 131072)])
+                                 (4, 10256), (2, 20480), (300, 512), (2, 65536), (2, 65552), (3, 131072),
+                                 (1024, 16), (1024, 5120), (1100, 2576), (1030, 20480), (1023, 9728)])
 def test_quantize_rows(M, K):
     rng = np.random.default_rng(M * 100003 + K)
     x = rng.standard_normal((M, K), dtype=np.float32)
@@ -59,7 +60,8 @@ def test_quantize_special_rows():
 STATIC_SCALES = [0.0625, 0.0170001, 0.0123, 3.0e-3, 2.0 ** -140]
 
 
-@pytest.mark.parametrize("M,K", [(1, 16), (5, 48), (33, 2560), (8, 9728), (4, 10256), (2, 65552), (3, 131072)])
+@pytest.mark.parametrize("M,K", [(1, 16), (5, 48), (33, 2560), (8, 9728), (4, 10256), (2, 65552), (3, 131072),
+                                 (1100, 2576), (1030, 20480)])
 @pytest.mark.parametrize("scale", STATIC_SCALES)
 def test_quantize_rows_static(M, K, scale):
     rng = np.random.default_rng(M * 7919 + K)

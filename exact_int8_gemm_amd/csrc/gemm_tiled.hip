@@ -2,7 +2,7 @@
 // tile shape is a function of (M, N, K) only.  Every choice computes the same
 // exact int32 sums and the same per-element epilogue, so the choice never
 // changes a result bit.
-#include "gemm_tiled_kernels.h"
+#include "gemm_pingpong.h"
 #include "../../include/prism.h"
 
 namespace prism {
@@ -29,7 +29,9 @@ int split_for(int64_t t, int K) {
 // 256 x 128 tile takes 0.60 and a 128 x 128 tile 0.45 of the time of a
 // 256 x 256 tile (measured on MI355X at M = 8192 for three (N, K) shapes);
 // the shape with the smallest estimate wins, ties to the larger tile:
-//  * 256 x 256 tiles: 8 waves of 64 x 128, 128-byte stages, 2-deep ring;
+//  * 256 x 256 tiles: 8 waves of 64 x 128 in two groups that alternate
+//    between MFMAs and LDS reads (gemm_pingpong.h), 128-byte stages, 2-deep
+//    ring;
 //  * 256 x 128 tiles: 8 waves of 64 x 64, 3-deep ring;
 //  * 128 x 128 tiles: 4 waves of 64 x 64, 4-deep ring, with K split over
 //    floor(256 / tiles) workgroups per tile (at most 4, at least 8 stages
@@ -42,7 +44,7 @@ void pick_int8(const int8_t* q, const float* s_a, const int8_t* w, const float* 
   const double c1 = (double)((t1 + 255) / 256), c2 = 0.60 * (double)((t2 + 255) / 256),
                c3 = 0.45 * (double)((t3 + 255) / 256);
   if (c1 <= c2 && c1 <= c3) {
-    tiled::dma::launch<256, 256, 128, 4, 2, 2, 1>(q, s_a, w, s_w, y, acc, M, N, K, st);
+    tiled::dma::launch_pp<128, 2>(q, s_a, w, s_w, y, acc, M, N, K, st);
   } else if (c2 <= c3) {
     tiled::dma::launch<256, 128, 128, 4, 2, 3, 1>(q, s_a, w, s_w, y, acc, M, N, K, st);
   } else {
@@ -76,7 +78,7 @@ int launch_gemm_tiled_variant(const int8_t* q, const float* s_a, const void* w, 
     return launch_status();
   }
   if (variant == 7) {
-    tiled::dma::launch<256, 256, 128, 4, 2, 2, 1>(q, s_a, wb, s_w, y, acc, M, N, K, st);
+    tiled::dma::launch_pp<128, 2>(q, s_a, wb, s_w, y, acc, M, N, K, st);
   } else if (variant == 8) {
     tiled::dma::launch<256, 128, 128, 4, 2, 3, 1>(q, s_a, wb, s_w, y, acc, M, N, K, st);
   } else if (variant >= 9 && variant <= 12) {

@@ -79,3 +79,13 @@ def test_w4a8_every_entry(M, N, K):
     for name in [n for n in TILES8 if n not in TILES4]:   # int8-only tiles
         with pytest.raises(prism.PrismError):
             prism.gemm_w4a8_variant(qd, sad, wd, swd, name)
+
+
+@pytest.mark.parametrize("M,N,K", [(600, 1300, 1040), (513, 1100, 4112), (256, 1024, 384), (1030, 2100, 2064)])
+def test_w8a8_256x256_several_column_groups(M, N, K):
+    """The 256 x 256 tiles walk each XCD's range in groups of four tile
+    columns; shapes with several groups, a short last group and ragged M, N
+    and K must give the oracle's bits, also through the plain call."""
+    q, s_a, w, s_w = _inputs(M + 7 * N + K, M, N, K)
+    y_ref, acc_ref = oracle.gemm_w8a8(q, s_a, w, s_w)
+    _run_all(prism.gemm_w8a8_variant, ["auto", "tile_256x256"], dev(q), dev(s_a), dev(w), dev(s_w), y_ref, acc_ref)

@@ -128,7 +128,7 @@ def _copies(bytes_per_set):
 
 # Sources of the GEMM kernels: a traffic figure is used only if it was
 # measured on exactly these sources.
-KERNEL_SOURCES = ["gemm_tiled_kernels.h", "gemm_tiled.hip", "gemm_small.hip", "prism_abi.cpp", "prism_internal.h",
+KERNEL_SOURCES = ["gemm_tiled_kernels.h", "gemm_pingpong.h", "gemm_tiled.hip", "gemm_small.hip", "prism_abi.cpp", "prism_internal.h",
                   "quant_math.h"]
 
 

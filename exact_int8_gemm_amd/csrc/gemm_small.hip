@@ -201,32 +201,39 @@ void launch_small(const int8_t* q, const float* s_a, const int8_t* w, const floa
   gemm_small_kernel<MB, CB, W4, WAVES, U><<<grid, 64 * WAVES, 0, st>>>(q, s_a, w, s_w, y, acc, M, N, K);
 }
 
-// Column blocks per workgroup and waves per workgroup, from a sweep of six
-// (N, K) shapes x M in {1, 16, 33, 64} x both weight formats on MI355X (the
-// README's kernels are likewise picked per GPU from measured tables).  Every
-// choice computes the same exact sums, so this only moves time.
-//  * M <= 32: column blocks chosen so that the workgroups spread evenly over
-//    the 256 CUs (fewest rounds x work per workgroup, ties to two blocks);
-//    4-bit weights take 8 waves once K >= 3072 (four 128-k units per wave),
-//    int8 weights 4 waves up to K = 5120 and 8 above.
-//  * M > 32: two column blocks of 4 waves once N >= 5120 (each activation
-//    fragment then feeds two column blocks), else one block of 16 waves
+// Column blocks per workgroup and waves per workgroup, from sweeps on MI355X
+// (the README's kernels are likewise picked per GPU from measured tables).
+// Every choice computes the same exact sums, so this only moves time.
+//  * Column blocks c in {1, 2, 3, 4}: the count that minimizes rounds x c,
+//    rounds = ceil(ceil(N / 16 / c) / 256), i.e. the workgroups spread evenly
+//    over the 256 CUs; ties go to the larger count, whose workgroups read the
+//    activations fewer times (each fragment feeds c column blocks), except
+//    at M = 1, where a fragment holds one real row and reuse gains nothing
+//    (4-bit weights, N = 12288: 7.0 us with one block, 7.1 with three).  At
+//    N = 12288 (768 blocks) three blocks give exactly 256 workgroups: 4-bit
+//    weights, K = 4096, M = 16 take 8.2 us against 10.5 us with one block,
+//    M = 64 15.0 against 23.0 us; N = 9728, K = 2560, int8, M = 16: 8.5 against
+//    11.0 us.
+//  * Waves: 8 with three or four blocks; with one or two blocks, as measured
+//    over six (N, K) shapes x M in {1, 16, 33, 64}: M <= 32: 4-bit weights 8
+//    waves once K >= 3072 (four 128-k units per wave), int8 weights 4 waves up
+//    to K = 5120 and 8 above; M > 32: 4 waves with two blocks, else 16 waves
 //    (N >= 4096) or 8.
 void choose_small(int M, int N, int K, bool w4, int& cb, int& waves) {
   const int64_t nunits = (K + kUnitK - 1) / kUnitK;
-  if (M <= 32) {
-    const int64_t g1 = (N + 15) / 16, g2 = (N + 31) / 32;
-    const int64_t c1 = (g1 + 255) / 256, c2 = 2 * ((g2 + 255) / 256);
-    cb = c2 <= c1 ? 2 : 1;
-    if (w4) waves = nunits >= 24 ? 8 : 4;
-    else waves = nunits <= 40 ? 4 : 8;
-  } else if (N >= 5120) {
-    cb = 2;
-    waves = 4;
-  } else {
-    cb = 1;
-    waves = N >= 4096 ? 16 : 8;
+  const int64_t blocks = (N + 15) / 16;
+  int64_t best = -1;
+  for (int c = 1; c <= 4; ++c) {
+    const int64_t cost = ((blocks + c - 1) / c + 255) / 256 * c;
+    if (best < 0 || cost < best || (cost == best && M > 1)) {
+      best = cost;
+      cb = c;
+    }
   }
+  if (cb >= 3) waves = 8;
+  else if (M <= 32) waves = w4 ? (nunits >= 24 ? 8 : 4) : (nunits <= 40 ? 4 : 8);
+  else if (cb == 2) waves = 4;
+  else waves = N >= 4096 ? 16 : 8;
 }
 
 template <bool W4>
@@ -239,6 +246,10 @@ bool pick_variant(const int8_t* q, const float* s_a, const int8_t* w, const floa
   else if (cb == 2 && waves == 4) launch_small<MB, 2, W4, 4>(q, s_a, w, s_w, y, acc, M, N, K, st);      \
   else if (cb == 2 && waves == 8) launch_small<MB, 2, W4, 8>(q, s_a, w, s_w, y, acc, M, N, K, st);      \
   else if (cb == 2 && waves == 16) launch_small<MB, 2, W4, 16>(q, s_a, w, s_w, y, acc, M, N, K, st);    \
+  else if (cb == 3 && waves == 4) launch_small<MB, 3, W4, 4>(q, s_a, w, s_w, y, acc, M, N, K, st);      \
+  else if (cb == 3 && waves == 8) launch_small<MB, 3, W4, 8>(q, s_a, w, s_w, y, acc, M, N, K, st);      \
+  else if (cb == 4 && waves == 4) launch_small<MB, 4, W4, 4>(q, s_a, w, s_w, y, acc, M, N, K, st);      \
+  else if (cb == 4 && waves == 8) launch_small<MB, 4, W4, 8>(q, s_a, w, s_w, y, acc, M, N, K, st);      \
   else return false;
   if (M <= 16) { PRISM_SMALL_CASE(1) }
   else if (M <= 32) { PRISM_SMALL_CASE(2) }

@@ -69,6 +69,7 @@ bool grid_fits(int64_t M, int64_t N) { return ((M + 127) / 128) * ((N + 127) / 1
 int run_variant(const int8_t* q, const float* s_a, const void* w, bool w4, const float* s_w, float* y, int32_t* acc,
                 int64_t M, int64_t N, int64_t K, int variant, hipStream_t s) {
   static const int kSmall[7][2] = {{0, 0}, {1, 4}, {1, 8}, {1, 16}, {2, 4}, {2, 8}, {2, 16}};
+  static const int kSmallWide[4][2] = {{3, 4}, {3, 8}, {4, 4}, {4, 8}};
   if (variant == PRISM_VARIANT_AUTO) {
     if (M <= prism::kSmallMMax) return prism::launch_gemm_small(q, s_a, w, w4, s_w, y, acc, (int)M, (int)N, (int)K, s);
     return prism::launch_gemm_tiled(q, s_a, w, w4, s_w, y, acc, (int)M, (int)N, (int)K, s);
@@ -78,7 +79,12 @@ int run_variant(const int8_t* q, const float* s_a, const void* w, bool w4, const
     return prism::launch_gemm_small_variant(q, s_a, w, w4, s_w, y, acc, (int)M, (int)N, (int)K, kSmall[variant][0],
                                             kSmall[variant][1], s);
   }
-  if (variant >= PRISM_VARIANT_TILE_256x256 && variant < PRISM_VARIANT_COUNT)
+  if (variant >= PRISM_VARIANT_SMALL_3x4 && variant <= PRISM_VARIANT_SMALL_4x8) {
+    if (M > prism::kSmallMMax) return PRISM_ERR_INVALID_ARG;
+    const int* e = kSmallWide[variant - PRISM_VARIANT_SMALL_3x4];
+    return prism::launch_gemm_small_variant(q, s_a, w, w4, s_w, y, acc, (int)M, (int)N, (int)K, e[0], e[1], s);
+  }
+  if (variant >= PRISM_VARIANT_TILE_256x256 && variant <= PRISM_VARIANT_TILE_128x128_SPLIT4)
     return prism::launch_gemm_tiled_variant(q, s_a, w, w4, s_w, y, acc, (int)M, (int)N, (int)K, variant, s);
   return PRISM_ERR_INVALID_ARG;
 }

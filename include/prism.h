@@ -41,7 +41,7 @@ extern "C" {
 #endif
 
 /* Bumped on any change of a signature or of the semantics below. */
-#define PRISM_ABI_VERSION 3
+#define PRISM_ABI_VERSION 4
 
 /* Largest accepted K.  For K <= 131040 every exact sum of K products of two
  * int8 values (|q|, |w| <= 128) lies strictly inside the int32 range. */
@@ -209,7 +209,8 @@ int prism_gemm_w4a8(const int8_t* q, const float* s_a, const uint8_t* w4, const 
  * Same arguments and checks as the plain calls, plus `variant`:
  *   PRISM_VARIANT_AUTO            the plain call's choice;
  *   PRISM_VARIANT_SMALL_<c>x<w>   the small-M kernel with c column blocks of
- *                                 16 and w waves per workgroup (M <= 64 only);
+ *                                 16 (c = 1..4) and w waves per workgroup
+ *                                 (M <= 64 only);
  *   PRISM_VARIANT_TILE_*          the LDS-tiled kernels: 256x256 and 256x128
  *                                 (int8 weights only), 128x128, and 128x128 with
  *                                 K split over 2, 3 or 4 workgroups whose exact
@@ -229,7 +230,11 @@ int prism_gemm_w4a8(const int8_t* q, const float* s_a, const uint8_t* w4, const 
 #define PRISM_VARIANT_TILE_128x128_SPLIT2 10
 #define PRISM_VARIANT_TILE_128x128_SPLIT3 11
 #define PRISM_VARIANT_TILE_128x128_SPLIT4 12
-#define PRISM_VARIANT_COUNT 13
+#define PRISM_VARIANT_SMALL_3x4 13
+#define PRISM_VARIANT_SMALL_3x8 14
+#define PRISM_VARIANT_SMALL_4x4 15
+#define PRISM_VARIANT_SMALL_4x8 16
+#define PRISM_VARIANT_COUNT 17
 
 int prism_gemm_w8a8_variant(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w,
                             float* y, int32_t* acc, int64_t M, int64_t N, int64_t K, int variant,

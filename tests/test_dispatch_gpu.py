@@ -17,7 +17,8 @@ from gpu_util import DEV, assert_same_floats, assert_same_ints, dev, host
 
 pytestmark = pytest.mark.gpu
 
-SMALL = ["small_1x4", "small_1x8", "small_1x16", "small_2x4", "small_2x8", "small_2x16"]
+SMALL = ["small_1x4", "small_1x8", "small_1x16", "small_2x4", "small_2x8", "small_2x16", "small_3x4", "small_3x8",
+         "small_4x4", "small_4x8"]
 TILES8 = ["tile_256x256", "tile_256x128", "tile_128x128", "tile_128x128_split2", "tile_128x128_split3",
           "tile_128x128_split4"]
 TILES4 = ["tile_128x128", "tile_128x128_split2", "tile_128x128_split3", "tile_128x128_split4"]
@@ -89,3 +90,20 @@ def test_w8a8_256x256_several_column_groups(M, N, K):
     q, s_a, w, s_w = _inputs(M + 7 * N + K, M, N, K)
     y_ref, acc_ref = oracle.gemm_w8a8(q, s_a, w, s_w)
     _run_all(prism.gemm_w8a8_variant, ["auto", "tile_256x256"], dev(q), dev(s_a), dev(w), dev(s_w), y_ref, acc_ref)
+
+
+@pytest.mark.parametrize("w4", [False, True])
+@pytest.mark.parametrize("M", [2, 16, 33, 64])
+def test_small_m_three_column_blocks(w4, M):
+    """N = 9000 has 563 column blocks of 16: the plain call takes workgroups
+    of three blocks (one round of 188), the last one ragged; the plain call
+    and every small-M entry must give the oracle's bits."""
+    N, K = 9000, 1056
+    q, s_a, w, s_w = _inputs(M * 31 + (7 if w4 else 0), M, N, K, w4=w4)
+    if w4:
+        y_ref, acc_ref = oracle.gemm_w4a8(q, s_a, w, s_w)
+        fn = prism.gemm_w4a8_variant
+    else:
+        y_ref, acc_ref = oracle.gemm_w8a8(q, s_a, w, s_w)
+        fn = prism.gemm_w8a8_variant
+    _run_all(fn, ["auto"] + SMALL, dev(q), dev(s_a), dev(w), dev(s_w), y_ref, acc_ref)

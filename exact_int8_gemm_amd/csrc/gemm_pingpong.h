@@ -61,15 +61,15 @@ __device__ inline void pp_barrier() { asm volatile("s_barrier" ::: "memory"); }
 // s_waitcnt lgkmcnt(0), no wait on vmcnt or expcnt (gfx9 encoding).
 __device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-template <int BK, int RING>
+template <int BK, int RING, int BN = 256, int KSP = 2>
 __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restrict__ q, const float* __restrict__ s_a,
                                                         const int8_t* __restrict__ w, const float* __restrict__ s_w,
                                                         float* __restrict__ y, int32_t* __restrict__ acc_out, int M,
                                                         int N, int K, int tiles_m, int tiles_n, int splits) {
-  constexpr int BM = 256, BN = 256;
+  constexpr int BM = 256;
   using C = Cfg<BM, BN, BK, 4, 2, RING>;
-  constexpr int P = BK / 64;  // read/compute phase pairs per stage
-  constexpr int TM = 2, TN = 4;
+  constexpr int P = BK / (32 * KSP);  // read/compute phase pairs per stage (KSP 32-k steps each)
+  constexpr int TM = 2, TN = BN / 64;
   static_assert(C::kNW == 8 && C::kPerWaveA * 8 == C::kCopiesA, "eight waves");
   __shared__ __attribute__((aligned(1024))) int8_t lds[RING * C::kStage];
 
@@ -86,17 +86,20 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
   // Copy sources of this wave (as in gemm_dma_kernel).
   const v4i ra = rsrc_words(q + (size_t)m0 * (size_t)K, (int64_t)(M - m0) * K);
   const v4i rb = rsrc_words(w + (size_t)n0 * (size_t)K, (int64_t)(N - n0) * K);
+  // The k offset of a lane's chunk (chunk * 16) is recomputed at each issue
+  // from the lane and the copy index instead of being kept per copy: a few
+  // VALU operations in a read phase, against one register per copy.
+  auto chunk_of = [&](int copy) __attribute__((always_inline)) {
+    return (lane % C::kChunks) ^ C::swz(copy * C::kRowsPerCopy + lane / C::kChunks);
+  };
   uint32_t off[C::kPerWave];
-  int kc[C::kPerWave];
 #pragma unroll
   for (int s = 0; s < C::kPerWave; ++s) {
     const bool isA = s < C::kPerWaveA;
     const int copy = isA ? wave * C::kPerWaveA + s : wave * C::kPerWaveB + (s - C::kPerWaveA);
     const int row = copy * C::kRowsPerCopy + lane / C::kChunks;
-    const int chunk = (lane % C::kChunks) ^ C::swz(row);
-    kc[s] = chunk * 16;
     const bool valid = isA ? (m0 + row < M) : (n0 + row < N);
-    off[s] = valid ? (uint32_t)(row * K + chunk * 16) : kOutOfRange;
+    off[s] = valid ? (uint32_t)(row * K + chunk_of(copy) * 16) : kOutOfRange;
   }
   auto issue = [&](int buf, int stage) __attribute__((always_inline)) {
     const int k0 = stage * BK;
@@ -104,7 +107,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
     for (int s = 0; s < C::kPerWave; ++s) {
       const bool isA = s < C::kPerWaveA;
       const int copy = isA ? wave * C::kPerWaveA + s : wave * C::kPerWaveB + (s - C::kPerWaveA);
-      const uint32_t o = (k0 + kc[s] < kend) ? off[s] + (uint32_t)k0 : kOutOfRange;
+      const uint32_t o = (k0 + chunk_of(copy) * 16 < kend) ? off[s] + (uint32_t)k0 : kOutOfRange;
       const int8_t* dst = lds + buf * C::kStage + (isA ? 0 : BM * BK) + copy * 1024;
       copy_to_lds(isA ? ra : rb, lds_addr(dst), o);
     }
@@ -119,15 +122,16 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
   const int rl = lane & 31;
   const int sw = C::swz(rl);
   const int arow = (wm * 64 + rl) * BK;
-  const int brow = (BM + grp * 128 + rl) * BK;
-  v4i af[TM][2], bf[TN][2];
-  // Fragments of the 64-k slice `half` of the stage in buffer `buf`: logical
-  // chunk 4 half + 2 ks + lane / 32 of row (lane % 32) of each 32-row tile.
+  const int brow = (BM + grp * (BN / 2) + rl) * BK;
+  v4i af[TM][KSP], bf[TN][KSP];
+  // Fragments of the (32 KSP)-k slice `half` of the stage in buffer `buf`:
+  // logical chunk 2 (KSP half + ks) + lane / 32 of row (lane % 32) of each
+  // 32-row tile.
   auto read = [&](int buf, int half) __attribute__((always_inline)) {
     const int8_t* base = lds + buf * C::kStage;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int c = ((4 * half + 2 * ks + (lane >> 5)) ^ sw) * 16;
+    for (int ks = 0; ks < KSP; ++ks) {
+      const int c = ((2 * (KSP * half + ks) + (lane >> 5)) ^ sw) * 16;
 #pragma unroll
       for (int i = 0; i < TM; ++i) af[i][ks] = *reinterpret_cast<const v4i*>(base + arow + i * 32 * BK + c);
 #pragma unroll
@@ -136,7 +140,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
   };
   auto mma = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < KSP; ++ks)
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -178,7 +182,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
   if (grp == 0) pp_barrier();  // matches group 1's extra barrier at the start
   wait_vmcnt<0>();             // no copy may land in LDS after the workgroup ends
 
-  const int mb = m0 + wm * 64, nb = n0 + grp * 128;
+  const int mb = m0 + wm * 64, nb = n0 + grp * (BN / 2);
   if (splits > 1) {
     int32_t* yi = reinterpret_cast<int32_t*>(y);
 #pragma unroll
@@ -219,14 +223,14 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
   }
 }
 
-template <int BK, int RING>
+template <int BK, int RING, int BN = 256, int KSP = 2>
 void launch_pp(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc, int M,
                int N, int K, hipStream_t st, int splits = 1) {
-  const int tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
+  const int tiles_m = (M + 255) / 256, tiles_n = (N + BN - 1) / BN;
   const int64_t total = (int64_t)M * N;
   if (splits > 1)
     zero_kernel<<<(unsigned)((total + 1023) / 1024), 256, 0, st>>>(reinterpret_cast<int32_t*>(y), total);
-  gemm_pp_kernel<BK, RING><<<(unsigned)(tiles_m * tiles_n * splits), 512, 0, st>>>(q, s_a, w, s_w, y, acc, M, N, K,
+  gemm_pp_kernel<BK, RING, BN, KSP><<<(unsigned)(tiles_m * tiles_n * splits), 512, 0, st>>>(q, s_a, w, s_w, y, acc, M, N, K,
                                                                                    tiles_m, tiles_n, splits);
   if (splits > 1) finalize_kernel<<<(unsigned)((total + 1023) / 1024), 256, 0, st>>>(y, acc, s_a, s_w, M, N);
 }

@@ -23,32 +23,43 @@ int split_for(int64_t t, int K) {
   return (int)splits;
 }
 
-// int8 weights: direct-to-LDS pipelines (gemm_tiled_kernels.h, namespace dma).
-// A launch runs in waves of up to 256 tiles (one per CU), so its time is
-// about ceil(tiles / 256) times the time of one wave of tiles.  Per wave, a
-// 256 x 128 tile takes 0.60 and a 128 x 128 tile 0.45 of the time of a
-// 256 x 256 tile (measured on MI355X at M = 8192 for three (N, K) shapes);
-// the shape with the smallest estimate wins, ties to the larger tile:
-//  * 256 x 256 tiles: 8 waves of 64 x 128 in two groups that alternate
-//    between MFMAs and LDS reads (gemm_pingpong.h), 128-byte stages, 2-deep
-//    ring;
+// int8 weights: direct-to-LDS pipelines (gemm_pingpong.h and
+// gemm_tiled_kernels.h, namespace dma).  A launch runs in waves of up to 256
+// tiles (one per CU), so its time is about ceil(tiles / 256) times the time
+// of one wave of tiles.  Per wave, relative to a 256 x 256 tile (measured on
+// MI355X): 256 x 192 0.83 and 256 x 320 1.23 (one-round launches at M = 2048,
+// N = K = 5120), 256 x 128 0.60 and 128 x 128 0.45 (M = 8192, three (N, K)
+// shapes).  The shape with the smallest estimate wins; ties go to the earlier
+// shape in the order 256 x 256, 256 x 320, 256 x 192, 256 x 128, 128 x 128:
+//  * 256 x 192 / 256 / 320 tiles: 8 waves of 64 x (tile width / 2) in two
+//    groups that alternate between MFMAs and LDS reads (gemm_pingpong.h),
+//    128-byte stages, 2-deep ring; the 320-wide tiles read one 32-k step of
+//    fragments per phase (their accumulators take 160 registers);
 //  * 256 x 128 tiles: 8 waves of 64 x 64, 3-deep ring;
 //  * 128 x 128 tiles: 4 waves of 64 x 64, 4-deep ring, with K split over
 //    floor(256 / tiles) workgroups per tile (at most 4, at least 8 stages
 //    each) whose exact int32 partial tiles are added atomically.
-// A sweep of M from 65 to 8192 on four projection shapes puts this choice
-// within 8% of the fastest entry of the table everywhere.
+// E.g. M = 8192, N = K = 5120: 640 tiles of 256 x 256 take three rounds for
+// 2.5 rounds of work, 512 tiles of 256 x 320 exactly two (272 -> 245 us);
+// M = 2048, N = 5120: 216 tiles of 256 x 192 fill the CUs that 160 tiles of
+// 256 x 256 leave idle (88 -> 74 us).
 void pick_int8(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc, int M,
                int N, int K, hipStream_t st) {
-  const int64_t t1 = tiles(M, N, 256, 256), t2 = tiles(M, N, 256, 128), t3 = tiles(M, N, 128, 128);
-  const double c1 = (double)((t1 + 255) / 256), c2 = 0.60 * (double)((t2 + 255) / 256),
-               c3 = 0.45 * (double)((t3 + 255) / 256);
-  if (c1 <= c2 && c1 <= c3) {
-    tiled::dma::launch_pp<128, 2>(q, s_a, w, s_w, y, acc, M, N, K, st);
-  } else if (c2 <= c3) {
-    tiled::dma::launch<256, 128, 128, 4, 2, 3, 1>(q, s_a, w, s_w, y, acc, M, N, K, st);
-  } else {
-    tiled::dma::launch<128, 128, 128, 2, 2, 4, 1>(q, s_a, w, s_w, y, acc, M, N, K, st, split_for(t3, K));
+  auto rounds = [](int64_t t) { return (double)((t + 255) / 256); };
+  const double cost[5] = {rounds(tiles(M, N, 256, 256)), 1.23 * rounds(tiles(M, N, 256, 320)),
+                          0.83 * rounds(tiles(M, N, 256, 192)), 0.60 * rounds(tiles(M, N, 256, 128)),
+                          0.45 * rounds(tiles(M, N, 128, 128))};
+  int best = 0;
+  for (int i = 1; i < 5; ++i)
+    if (cost[i] < cost[best]) best = i;
+  switch (best) {
+    case 0: tiled::dma::launch_pp<128, 2>(q, s_a, w, s_w, y, acc, M, N, K, st); break;
+    case 1: tiled::dma::launch_pp<128, 2, 320, 1>(q, s_a, w, s_w, y, acc, M, N, K, st); break;
+    case 2: tiled::dma::launch_pp<128, 2, 192>(q, s_a, w, s_w, y, acc, M, N, K, st); break;
+    case 3: tiled::dma::launch<256, 128, 128, 4, 2, 3, 1>(q, s_a, w, s_w, y, acc, M, N, K, st); break;
+    default:
+      tiled::dma::launch<128, 128, 128, 2, 2, 4, 1>(q, s_a, w, s_w, y, acc, M, N, K, st,
+                                                     split_for(tiles(M, N, 128, 128), K));
   }
 }
 
@@ -65,12 +76,13 @@ void pick_int4(const int8_t* q, const float* s_a, const int8_t* w, const float* 
 }  // namespace
 
 // One named entry of the table above (7: 256 x 256, 8: 256 x 128, 9..12:
-// 128 x 128 with K split over 1..4 workgroups; the 4-bit path has 9..12).
+// 128 x 128 with K split over 1..4 workgroups, 17: 256 x 192, 18: 256 x 320;
+// the 4-bit path has 9..12).
 int launch_gemm_tiled_variant(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
                               float* y, int32_t* acc, int M, int N, int K, int variant, hipStream_t st) {
   const int8_t* wb = static_cast<const int8_t*>(w);
   if (w_is_int4) {
-    if (variant < 9 || variant > 12) return PRISM_ERR_INVALID_ARG;
+    if (variant < 9 || variant > 12) return PRISM_ERR_INVALID_ARG;  // 128 x 128 only
     const int stages = (K + 127) / 128;
     int splits = variant - 8;
     if (splits > stages) splits = stages;
@@ -79,6 +91,10 @@ int launch_gemm_tiled_variant(const int8_t* q, const float* s_a, const void* w, 
   }
   if (variant == 7) {
     tiled::dma::launch_pp<128, 2>(q, s_a, wb, s_w, y, acc, M, N, K, st);
+  } else if (variant == 17) {
+    tiled::dma::launch_pp<128, 2, 192>(q, s_a, wb, s_w, y, acc, M, N, K, st);
+  } else if (variant == 18) {
+    tiled::dma::launch_pp<128, 2, 320, 1>(q, s_a, wb, s_w, y, acc, M, N, K, st);
   } else if (variant == 8) {
     tiled::dma::launch<256, 128, 128, 4, 2, 3, 1>(q, s_a, wb, s_w, y, acc, M, N, K, st);
   } else if (variant >= 9 && variant <= 12) {

@@ -19,8 +19,8 @@ pytestmark = pytest.mark.gpu
 
 SMALL = ["small_1x4", "small_1x8", "small_1x16", "small_2x4", "small_2x8", "small_2x16", "small_3x4", "small_3x8",
          "small_4x4", "small_4x8"]
-TILES8 = ["tile_256x256", "tile_256x128", "tile_128x128", "tile_128x128_split2", "tile_128x128_split3",
-          "tile_128x128_split4"]
+TILES8 = ["tile_256x256", "tile_256x192", "tile_256x320", "tile_256x128", "tile_128x128", "tile_128x128_split2",
+          "tile_128x128_split3", "tile_128x128_split4"]
 TILES4 = ["tile_128x128", "tile_128x128_split2", "tile_128x128_split3", "tile_128x128_split4"]
 
 
@@ -83,13 +83,15 @@ def test_w4a8_every_entry(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(600, 1300, 1040), (513, 1100, 4112), (256, 1024, 384), (1030, 2100, 2064)])
-def test_w8a8_256x256_several_column_groups(M, N, K):
-    """The 256 x 256 tiles walk each XCD's range in groups of four tile
-    columns; shapes with several groups, a short last group and ragged M, N
-    and K must give the oracle's bits, also through the plain call."""
+def test_w8a8_256_row_tiles_several_column_groups(M, N, K):
+    """The 256-row ping-pong tiles (192, 256 and 320 columns) walk each XCD's
+    range in groups of four tile columns; shapes with several groups, a short
+    last group and ragged M, N and K must give the oracle's bits, also
+    through the plain call."""
     q, s_a, w, s_w = _inputs(M + 7 * N + K, M, N, K)
     y_ref, acc_ref = oracle.gemm_w8a8(q, s_a, w, s_w)
-    _run_all(prism.gemm_w8a8_variant, ["auto", "tile_256x256"], dev(q), dev(s_a), dev(w), dev(s_w), y_ref, acc_ref)
+    _run_all(prism.gemm_w8a8_variant, ["auto", "tile_256x256", "tile_256x192", "tile_256x320"], dev(q), dev(s_a), dev(w),
+             dev(s_w), y_ref, acc_ref)
 
 
 @pytest.mark.parametrize("w4", [False, True])

@@ -331,11 +331,19 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_tiled_kernel(const int
     }
     return;
   }
+  // The tile's row and column scales, loaded once into LDS instead of per
+  // element inside the store loop (as in the direct-to-LDS kernels).
+  __shared__ float sa_l[BM], sw_l[BN];
+  for (int t = threadIdx.x; t < BM + BN; t += G::kNT) {
+    if (t < BM) sa_l[t] = m0 + t < M ? s_a[m0 + t] : 0.0f;
+    else sw_l[t - BM] = n0 + t - BM < N ? s_w[n0 + t - BM] : 0.0f;
+  }
+  __syncthreads();
 #pragma unroll
   for (int j = 0; j < G::kTN; ++j) {
     const int n = n0 + wn * G::kWTN + j * 32 + rl;
     if (n >= N) continue;
-    const float sw = s_w[n];
+    const float sw = sw_l[n - n0];
 #pragma unroll
     for (int i = 0; i < G::kTM; ++i) {
 #pragma unroll
@@ -346,7 +354,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_tiled_kernel(const int
           if (W4) a >>= 4;  // exact: the sum is a multiple of 16
           const size_t o = (size_t)m * (size_t)N + (size_t)n;
           if (acc_out) acc_out[o] = a;
-          const float t = (float)a * s_a[m];
+          const float t = (float)a * sa_l[m - m0];
           y[o] = t * sw;
         }
       }
@@ -605,11 +613,22 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(const int8_
     return;
   }
 
+  // The tile's row and column scales, loaded once into LDS (as in
+  // gemm_pp_kernel) instead of per element inside the store loop.  Every
+  // wave has waited for its own copies above; the barrier orders these
+  // writes after all of them and after every wave's last fragment read.
+  __shared__ float sa_l[BM], sw_l[BN];
+  __syncthreads();
+  for (int t = threadIdx.x; t < BM + BN; t += C::kNT) {
+    if (t < BM) sa_l[t] = m0 + t < M ? s_a[m0 + t] : 0.0f;
+    else sw_l[t - BM] = n0 + t - BM < N ? s_w[n0 + t - BM] : 0.0f;
+  }
+  __syncthreads();
 #pragma unroll
   for (int j = 0; j < C::kTN; ++j) {
     const int n = n0 + wn * C::kWTN + j * 32 + rl;
     if (n >= N) continue;
-    const float swn = s_w[n];
+    const float swn = sw_l[n - n0];
 #pragma unroll
     for (int i = 0; i < C::kTM; ++i) {
 #pragma unroll
@@ -619,7 +638,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(const int8_
           const int a = acc[i][j][r];
           const size_t o = (size_t)m * (size_t)N + (size_t)n;
           if (acc_out) acc_out[o] = a;
-          const float t = (float)a * s_a[m];
+          const float t = (float)a * sa_l[m - m0];
           y[o] = t * swn;
         }
       }

@@ -1,16 +1,17 @@
-// Ping-pong schedule of the int8 tiled GEMM (256 x 256 output tiles, eight
-// waves, direct-to-LDS copies as in gemm_dma_kernel).
+// Ping-pong schedule of the int8 tiled GEMM (output tiles of 256 rows by BN =
+// 192, 256 or 320 columns, eight waves, direct-to-LDS copies as in
+// gemm_dma_kernel).
 //
 // The exact int32 sums of the StartLux-Prism README ("How it works") need a
 // dense int8 contraction at large M; this kernel keeps the matrix cores of a
 // CU busy while its own operand traffic is in flight.  The eight waves form
 // two groups of four; wave w and wave w + 4 share a SIMD.  Group 0 owns the
-// left 128 columns of the tile and group 1 the right 128, each wave a 64 x
-// 128 block of 2 x 4 MFMA tiles of 32 x 32.
+// left BN / 2 columns of the tile and group 1 the right BN / 2, each wave a
+// 64 x BN / 2 block of 2 x BN / 64 MFMA tiles of 32 x 32.
 //
 // Time is cut into phases by workgroup barriers.  In every phase one group
-// runs the 16 MFMAs of one 64-k slice from registers while the other group
-// reads its fragments of the next slice from LDS (and, once per stage,
+// runs the MFMAs of KSP 32-k steps from registers while the other group
+// reads its fragments of the next KSP steps from LDS (and, once per stage,
 // issues its share of the global -> LDS copies of a later stage); in the
 // next phase the roles swap.  Group 1 starts one barrier late, so the two
 // waves of a SIMD alternate and the MFMA unit always has queued work.

@@ -109,3 +109,22 @@ def test_small_m_three_column_blocks(w4, M):
         y_ref, acc_ref = oracle.gemm_w8a8(q, s_a, w, s_w)
         fn = prism.gemm_w8a8_variant
     _run_all(fn, ["auto"] + SMALL, dev(q), dev(s_a), dev(w), dev(s_w), y_ref, acc_ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(2048, 5120, 5120), (4096, 9728, 2560), (2048, 17408, 5120), (8192, 2560, 9728)])
+def test_256_row_tiles_full_size_sampled_rows(M, N, K):
+    """The shapes where the plain call picks 256 x 192 or 256 x 320 tiles,
+    at full size: the plain call and every 256-row tile width, compared with
+    the oracle on sampled rows (rows are independent in the definition, so
+    the oracle on a subset of rows gives exactly those rows)."""
+    q, s_a, w, s_w = _inputs(M + N + K, M, N, K)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, M // 2, M - 257, M - 256, M - 1],
+                                     np.random.default_rng(M + N).choice(M, 16, replace=False)]))
+    y_ref, acc_ref = oracle.gemm_w8a8(q[rows], s_a[rows], w, s_w)
+    qd, sad, wd, swd = dev(q), dev(s_a), dev(w), dev(s_w)
+    for name in ["auto", "tile_256x256", "tile_256x192", "tile_256x320"]:
+        acc = torch.full((M, N), 7, dtype=torch.int32, device=DEV)
+        y = prism.gemm_w8a8_variant(qd, sad, wd, swd, name, acc=acc)
+        torch.cuda.synchronize()
+        assert_same_ints(host(acc)[rows], acc_ref, "acc (%s)" % name)
+        assert_same_floats(host(y)[rows], y_ref, "y (%s)" % name)

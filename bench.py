@@ -45,7 +45,7 @@ def _args():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy three times (scale for HBM byte counters)")
     ap.add_argument("--only", default=None, help="run only one kernel measurement (for profiling): "
-                    "step | w4a8 | block | repack | q4k | decode | vendor | stress")
+                    "step | w4a8 | block | repack | q4k | decode | vendor | stress | sweep (M sweep, not in the default run)")
     return ap.parse_args()
 
 
@@ -421,6 +421,36 @@ def kernels(torch, prism, wl, only=None):
             except RuntimeError as e:   # not every torch build exposes an int8 GEMM
                 out["vendor_int_mm_" + name] = dict(error=str(e)[:120])
             del wts
+    if only == "sweep":
+        # Not in the default run: the per-channel W8A8 GEMM across M at
+        # N = K = 5120 (the plain call's own kernel choice at each M), next to
+        # the vendor int8 GEMM on the same inputs (int32 output only); weights
+        # rotated as above.  Inputs are seeded int8 codes (values do not change
+        # the kernels' timing much; the stress workload covers real activations).
+        g = torch.Generator(device=dev)
+        g.manual_seed(12)
+        N = K = 5120
+        R = _copies(N * K)
+        wts = [torch.randint(-127, 128, (N, K), dtype=torch.int8, device=dev, generator=g) for _ in range(R)]
+        sw = torch.rand((N,), device=dev, generator=g) * 0.01
+        for M in (1, 4, 16, 64, 128, 256, 512, 1024, 2048, 4096, 8192):
+            q = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev, generator=g)
+            sa = torch.rand((M,), device=dev, generator=g) * 0.01
+            y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            reps = 100 if M <= 256 else 20
+            t1, t = _time_launches(torch, [L.w8a8(q, sa, wt, sw, y) for wt in wts], reps)
+            nbytes = N * K + 4 * N + M * K + 4 * M + 4 * M * N
+            rec = dict(us=t * 1e6, tops=2 * M * N * K / t / 1e12, mfma_frac=2 * M * N * K / t / 1e12 / PEAK_INT8_TOPS,
+                       gbs=nbytes / t / 1e9, hbm_frac=nbytes / t / 1e9 / PEAK_HBM_GBS, copies=R)
+            try:
+                def mm(wt):
+                    return lambda: (torch._int_mm(q, wt.t()), 0)[1]
+                _, tv = _time_launches(torch, [mm(wt) for wt in wts], reps)
+                rec.update(vendor_int_mm_us=tv * 1e6, vendor_over_prism=tv / t)
+            except RuntimeError as e:   # the vendor GEMM takes M > 16 only on some builds
+                rec.update(vendor_int_mm_error=str(e)[:80])
+            out["sweep_w8a8_5120x5120_m%d" % M] = rec
+        del wts
     if only in (None, "stress"):
         st = wl.stress()
         R = _copies(st["w"].nbytes)

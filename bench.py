@@ -514,7 +514,7 @@ def cpu_baseline(np, oracle, up, dn, gpu_outputs, budget_s=10.0):
 def main():
     args = _args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
     import numpy as np

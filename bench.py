@@ -508,7 +508,19 @@ def cpu_baseline(np, oracle, up, dn, gpu_outputs, budget_s=10.0):
     sample = ("%d full step(s) (quantize + GEMM, up and down, M=%d)" % (reps, M) if rows == M else
               "rows 0..%d of one step (quantize + GEMM, up and down)" % (rows - 1))
     return dict(value=ops / dt / 1e12, unit="TOPS", cores=oracle.max_threads(), kind="oracle", sample=sample,
-                seconds=dt, cpu=platform.processor() or platform.machine(), nproc=os.cpu_count()), exact
+                seconds=dt, cpu=_cpu_model(), nproc=os.cpu_count(), compiler="gcc " + " ".join(oracle.CFLAGS)), exact
+
+
+def _cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo where there is one)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def main():

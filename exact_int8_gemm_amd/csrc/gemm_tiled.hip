@@ -12,15 +12,40 @@ using tiled::launch_tiled;
 
 inline int64_t tiles(int64_t M, int64_t N, int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
 
-// K split of a 128 x 128 launch with t tiles: floor(256 / t) workgroups per
-// tile, at most 4, each with at least 8 stages of 128 k.
-int split_for(int64_t t, int K) {
+// 4-bit weights (unpacked on the way into LDS, so a stage costs more and the
+// int8 fit below does not carry over): floor(256 / t) workgroups per tile, at
+// most 4, each with at least 8 stages of 128 k.
+int split_int4(int64_t t, int K) {
   const int64_t stages = (K + 127) / 128;
   int64_t splits = 256 / t;
   if (splits > 4) splits = 4;
   if (splits > stages / 8) splits = stages / 8;
   if (splits < 1) splits = 1;
   return (int)splits;
+}
+
+// K split s in 1..4 of an int8 128 x 128 launch with t tiles, from a cost model
+// fitted to 27 shapes on MI355X (M in {128, 256, 512}, N and K in {2560, 5120,
+// 9728}): about 0.95 us per stage of 128 k per round of up to 256
+// workgroups, ceil(t s / 256) x ceil(stages / s), plus for s > 1 the fill and
+// in-place epilogue (about 2.3 us) and the atomic partial tiles (about 4 us
+// per split and million outputs).  Ties go to the smaller split.  E.g. M =
+// 512, N = K = 2560: no split, 19 us (a 2-way split took 22); M = 512, N =
+// 2560, K = 9728: 3 ways, 35.5 us.
+int split_for(int64_t t, int64_t M, int64_t N, int K) {
+  const int64_t stages = (K + 127) / 128;
+  int best = 1;
+  double best_cost = 0.0;
+  for (int s = 1; s <= 4 && s <= stages; ++s) {
+    const double rounds = (double)((t * s + 255) / 256);
+    double cost = 0.95 * rounds * (double)((stages + s - 1) / s);
+    if (s > 1) cost += 2.3 + 4.0 * (double)s * (double)(M * N) * 1e-6;
+    if (s == 1 || cost < best_cost) {
+      best = s;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 // int8 weights: direct-to-LDS pipelines (gemm_pingpong.h and
@@ -37,8 +62,8 @@ int split_for(int64_t t, int K) {
 //    fragments per phase (their accumulators take 160 registers);
 //  * 256 x 128 tiles: 8 waves of 64 x 64, 3-deep ring;
 //  * 128 x 128 tiles: 4 waves of 64 x 64, 4-deep ring, with K split over
-//    floor(256 / tiles) workgroups per tile (at most 4, at least 8 stages
-//    each) whose exact int32 partial tiles are added atomically.
+//    up to 4 workgroups per tile (split_for) whose exact int32 partial
+//    tiles are added atomically.
 // E.g. M = 8192, N = K = 5120: 640 tiles of 256 x 256 take three rounds for
 // 2.5 rounds of work, 512 tiles of 256 x 320 exactly two (272 -> 245 us);
 // M = 2048, N = 5120: 216 tiles of 256 x 192 fill the CUs that 160 tiles of
@@ -59,18 +84,18 @@ void pick_int8(const int8_t* q, const float* s_a, const int8_t* w, const float* 
     case 3: tiled::dma::launch<256, 128, 128, 4, 2, 3, 1>(q, s_a, w, s_w, y, acc, M, N, K, st); break;
     default:
       tiled::dma::launch<128, 128, 128, 2, 2, 4, 1>(q, s_a, w, s_w, y, acc, M, N, K, st,
-                                                     split_for(tiles(M, N, 128, 128), K));
+                                                     split_for(tiles(M, N, 128, 128), M, N, K));
   }
 }
 
 // 4-bit weights: register-staged pipeline that unpacks the nibbles on their
-// way into LDS; 128 x 128 tiles, with K split as for the int8 128 x 128 tiles
-// when there are fewer tiles than CUs.
+// way into LDS; 128 x 128 tiles, with K split (split_int4) when there are
+// fewer tiles than CUs.
 
 void pick_int4(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc, int M,
                int N, int K, hipStream_t st) {
   launch_tiled<128, 128, 128, 2, 2, true, 2>(q, s_a, w, s_w, y, acc, M, N, K, st,
-                                              split_for(tiles(M, N, 128, 128), K));
+                                              split_int4(tiles(M, N, 128, 128), K));
 }
 
 }  // namespace

@@ -242,7 +242,7 @@ void launch_pp(const int8_t* q, const float* s_a, const int8_t* w, const float* 
     zero_kernel<<<(unsigned)((total + 1023) / 1024), 256, 0, st>>>(reinterpret_cast<int32_t*>(y), total);
   gemm_pp_kernel<BK, RING, BN, KSP><<<(unsigned)(tiles_m * tiles_n * splits), 512, 0, st>>>(q, s_a, w, s_w, y, acc, M, N, K,
                                                                                    tiles_m, tiles_n, splits);
-  if (splits > 1) finalize_kernel<<<(unsigned)((total + 1023) / 1024), 256, 0, st>>>(y, acc, s_a, s_w, M, N);
+  if (splits > 1) launch_finalize(y, acc, s_a, s_w, M, N, st);
 }
 
 }  // namespace dma

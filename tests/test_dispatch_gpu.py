@@ -82,6 +82,23 @@ def test_w4a8_every_entry(M, N, K):
             prism.gemm_w4a8_variant(qd, sad, wd, swd, name)
 
 
+@pytest.mark.parametrize("M,N,K", [(70, 2052, 2080), (129, 1028, 1056), (3, 2560, 4096), (200, 1030, 1056),
+                                   (33, 4098, 544)])
+def test_k_split_epilogue_rows(M, N, K):
+    """A K-split launch finishes in place with its own epilogue kernel: one
+    workgroup per 1024 columns of a row when N % 4 == 0 (here 2052, 1028 and
+    2560: two or three pieces per row, the last one ragged), a flat walk
+    over y otherwise (1030, 4098: runs of four that cross row ends).  Every
+    split entry, 4-bit included, must give the oracle's bits and int32 sums."""
+    q, s_a, w, s_w = _inputs(M * 3 + N + K, M, N, K)
+    y_ref, acc_ref = oracle.gemm_w8a8(q, s_a, w, s_w)
+    names = ["auto"] + [n for n in TILES4 if "split" in n]
+    _run_all(prism.gemm_w8a8_variant, names, dev(q), dev(s_a), dev(w), dev(s_w), y_ref, acc_ref)
+    q, s_a, w4, s_w = _inputs(M * 5 + N + K, M, N, K, w4=True)
+    y_ref, acc_ref = oracle.gemm_w4a8(q, s_a, w4, s_w)
+    _run_all(prism.gemm_w4a8_variant, names, dev(q), dev(s_a), dev(w4), dev(s_w), y_ref, acc_ref)
+
+
 @pytest.mark.parametrize("M,N,K", [(600, 1300, 1040), (513, 1100, 4112), (256, 1024, 384), (1030, 2100, 2064)])
 def test_w8a8_256_row_tiles_several_column_groups(M, N, K):
     """The 256-row ping-pong tiles (192, 256 and 320 columns) walk each XCD's

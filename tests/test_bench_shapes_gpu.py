@@ -1,0 +1,94 @@
+"""GPU parity at the full sizes of the extra workloads that bench.py times
+(W4A8 prefill, block-scale decode, Q4_K), on the same inputs, against the
+CPU oracle.
+
+Rows are independent in the definition, so the oracle run on a subset of
+rows gives exactly those rows' outputs; at M > 16 the checks use sampled
+rows (the first and last rows of tiles among them).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_int8_gemm_amd import prism
+from exact_int8_gemm_amd import workloads as wl
+from gpu_util import DEV, assert_same_floats, assert_same_ints, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows(M, seed):
+    fixed = [r for r in (0, 1, 127, 128, 255, 256, M - 1) if r < M]
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([fixed, rng.choice(M, min(M, 17), replace=False)])).astype(np.int64)
+
+
+def _quantize_both(x):
+    q_ref, s_ref = oracle.quantize_rows(x)
+    q, s = prism.quantize_rows(dev(x))
+    torch.cuda.synchronize()
+    assert_same_floats(host(s), s_ref, "scale")
+    assert_same_ints(host(q), q_ref, "codes")
+    return q, s, q_ref, s_ref
+
+
+@pytest.mark.parametrize("M", [512, 2048])
+def test_w4a8_prefill_full_size_sampled_rows(M):
+    """N = 12288, K = 4096 (the W4A8 weights), M > 64: the 4-bit tiled path,
+    with the 64 seeded rows repeated as in the benchmark."""
+    c = wl.w4()
+    x = c["x"][[i % 64 for i in range(M)]]
+    q, s, q_ref, s_ref = _quantize_both(x)
+    N = c["w4"].shape[0]
+    acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    y = host(prism.gemm_w4a8(q, s, dev(c["w4"]), dev(c["s_w"]), acc=acc))
+    rows = _rows(M, M)
+    y_ref, acc_ref = oracle.gemm_w4a8(q_ref[rows], s_ref[rows], c["w4"], c["s_w"])
+    assert_same_ints(host(acc)[rows], acc_ref, "acc sampled rows")
+    assert_same_floats(y[rows], y_ref, "y sampled rows")
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_block_scale_decode_full_size(M):
+    """N = 17408, K = 5120 with fp16 block scales, M <= 16: the small-M block
+    kernel, every row against the oracle."""
+    c = wl.block()
+    q, s, q_ref, s_ref = _quantize_both(c["x"][:M].copy())
+    y = host(prism.gemm_w8a8_blockscale(q, s, dev(c["w"]), dev(c["d"])))
+    y_ref, _ = oracle.gemm_w8a8_blockscale(q_ref, s_ref, c["w"], c["d"])
+    assert_same_floats(y, y_ref, "y")
+
+
+def _q4k_blocks(seed, N, K):
+    """Random Q4_K super-block bytes (144 per 256 weights) whose d and dmin are
+    finite binary16 values in [2^-14, 2^-5): every scale, min and code pattern
+    occurs, and no output is NaN or infinite."""
+    rng = np.random.default_rng(seed)
+    nsb = N * (K // 256)
+    blocks = rng.integers(0, 256, (nsb, 144), dtype=np.uint8)
+    dd = (rng.uniform(0.5, 1.0, (nsb, 2)) * 2.0 ** rng.integers(-13, -5, (nsb, 2))).astype("<f2")
+    blocks[:, 0:4] = dd.view(np.uint8).reshape(nsb, 4)
+    return blocks.reshape(-1)
+
+
+@pytest.mark.parametrize("M", [1, 2048])
+def test_q4k_full_size(M):
+    """Q4_K weights of the block-scale shape (17408 x 5120): the repacked
+    planes in full, and the GEMM (M = 1: small-M block kernel, every output;
+    M = 2048: tiled kernel, sampled rows)."""
+    N, K = 17408, 5120
+    blocks = _q4k_blocks(12, N, K)
+    w, D, Mn = prism.repack_q4_k(dev(blocks), N, K)
+    if M == 1:
+        w_ref, D_ref, M_ref = oracle.repack_q4_k(blocks, N, K)
+        torch.cuda.synchronize()
+        assert_same_ints(host(w), w_ref, "codes")
+        assert_same_floats(host(D), D_ref, "d * sc")
+        assert_same_floats(host(Mn), M_ref, "dmin * m")
+    q, s, q_ref, s_ref = _quantize_both(wl.block()["x"][:M].copy())
+    y = host(prism.gemm_w4a8_q4k(q, s, w, D, Mn))
+    rows = _rows(M, 7) if M > 16 else np.arange(M)
+    y_ref = oracle.gemm_w4a8_q4k(q_ref[rows], s_ref[rows], blocks, N)
+    assert np.isfinite(y_ref).all()
+    assert_same_floats(y[rows], y_ref, "y")

@@ -62,8 +62,19 @@ int check_gemm(const void* q, const void* s_a, const void* w, const void* scale_
   return PRISM_OK;
 }
 
-// Grid limits of the tiled kernels (128 x 128 tiles at the smallest).
-bool grid_fits(int64_t M, int64_t N) { return ((M + 127) / 128) * ((N + 127) / 128) <= INT_MAX; }
+// Grid limits of the tiled kernels (64 x 128 tiles with a 4-way K split at the most).
+bool grid_fits(int64_t M, int64_t N) { return ((M + 63) / 64) * ((N + 127) / 128) * 4 <= INT_MAX; }
+
+// The small-M kernel re-reads the whole M x K activation block in every
+// workgroup.  With int8 weights, from 32 rows and 240 KiB of activations
+// (M K >= 245760) the 64 x 128 tiles of the tiled path are faster (M = 32,
+// 48, 64 and N, K in {2560, 5120, 9728} on MI355X: e.g. M = 64, N = 5120,
+// K = 9728: 19.9 us against 30.7; M = 64, N = K = 2560 stays small-M: 8.5 us
+// against 10.7).  4-bit weights always take the small-M kernel up to 64 rows.
+bool use_small(int64_t M, int64_t K, bool w4) {
+  if (M > prism::kSmallMMax) return false;
+  return w4 || M < 32 || M * K < 245760;
+}
 
 // Variant dispatch shared by the two _variant calls (arguments already checked).
 int run_variant(const int8_t* q, const float* s_a, const void* w, bool w4, const float* s_w, float* y, int32_t* acc,
@@ -71,7 +82,7 @@ int run_variant(const int8_t* q, const float* s_a, const void* w, bool w4, const
   static const int kSmall[7][2] = {{0, 0}, {1, 4}, {1, 8}, {1, 16}, {2, 4}, {2, 8}, {2, 16}};
   static const int kSmallWide[4][2] = {{3, 4}, {3, 8}, {4, 4}, {4, 8}};
   if (variant == PRISM_VARIANT_AUTO) {
-    if (M <= prism::kSmallMMax) return prism::launch_gemm_small(q, s_a, w, w4, s_w, y, acc, (int)M, (int)N, (int)K, s);
+    if (use_small(M, K, w4)) return prism::launch_gemm_small(q, s_a, w, w4, s_w, y, acc, (int)M, (int)N, (int)K, s);
     return prism::launch_gemm_tiled(q, s_a, w, w4, s_w, y, acc, (int)M, (int)N, (int)K, s);
   }
   if (variant >= PRISM_VARIANT_SMALL_1x4 && variant <= PRISM_VARIANT_SMALL_2x16) {
@@ -85,7 +96,7 @@ int run_variant(const int8_t* q, const float* s_a, const void* w, bool w4, const
     return prism::launch_gemm_small_variant(q, s_a, w, w4, s_w, y, acc, (int)M, (int)N, (int)K, e[0], e[1], s);
   }
   if ((variant >= PRISM_VARIANT_TILE_256x256 && variant <= PRISM_VARIANT_TILE_128x128_SPLIT4) ||
-      variant == PRISM_VARIANT_TILE_256x192 || variant == PRISM_VARIANT_TILE_256x320)
+      (variant >= PRISM_VARIANT_TILE_256x192 && variant <= PRISM_VARIANT_TILE_64x128_SPLIT4))
     return prism::launch_gemm_tiled_variant(q, s_a, w, w4, s_w, y, acc, (int)M, (int)N, (int)K, variant, s);
   return PRISM_ERR_INVALID_ARG;
 }
@@ -178,7 +189,8 @@ int prism_gemm_w8a8(const int8_t* q, const float* s_a, const int8_t* w, const fl
   if (!grid_fits(M, N)) return PRISM_ERR_INVALID_ARG;
   if ((st = check_device()) != PRISM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (M <= prism::kSmallMMax) return prism::launch_gemm_small(q, s_a, w, false, s_w, y, acc, (int)M, (int)N, (int)K, s);
+  if (use_small(M, K, false))
+    return prism::launch_gemm_small(q, s_a, w, false, s_w, y, acc, (int)M, (int)N, (int)K, s);
   return prism::launch_gemm_tiled(q, s_a, w, false, s_w, y, acc, (int)M, (int)N, (int)K, s);
 }
 
@@ -195,7 +207,7 @@ int prism_quantize_gemm_w8a8(const float* x, int8_t* q, float* scale, const int8
   if (M == 1 && prism::launch_quantize_gemv(x, q, scale, w, s_w, y, acc, (int)N, (int)K, s))
     return prism::launch_status();
   if ((st = prism::launch_quantize_rows(x, q, scale, M, K, s)) != PRISM_OK) return st;
-  if (M <= prism::kSmallMMax)
+  if (use_small(M, K, false))
     return prism::launch_gemm_small(q, scale, w, false, s_w, y, acc, (int)M, (int)N, (int)K, s);
   return prism::launch_gemm_tiled(q, scale, w, false, s_w, y, acc, (int)M, (int)N, (int)K, s);
 }
@@ -209,7 +221,7 @@ int prism_gemm_w4a8(const int8_t* q, const float* s_a, const uint8_t* w4, const 
   if (!grid_fits(M, N)) return PRISM_ERR_INVALID_ARG;
   if ((st = check_device()) != PRISM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (M <= prism::kSmallMMax) return prism::launch_gemm_small(q, s_a, w4, true, s_w, y, acc, (int)M, (int)N, (int)K, s);
+  if (use_small(M, K, true)) return prism::launch_gemm_small(q, s_a, w4, true, s_w, y, acc, (int)M, (int)N, (int)K, s);
   return prism::launch_gemm_tiled(q, s_a, w4, true, s_w, y, acc, (int)M, (int)N, (int)K, s);
 }
 

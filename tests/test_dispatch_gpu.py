@@ -20,7 +20,8 @@ pytestmark = pytest.mark.gpu
 SMALL = ["small_1x4", "small_1x8", "small_1x16", "small_2x4", "small_2x8", "small_2x16", "small_3x4", "small_3x8",
          "small_4x4", "small_4x8"]
 TILES8 = ["tile_256x256", "tile_256x192", "tile_256x320", "tile_256x128", "tile_128x128", "tile_128x128_split2",
-          "tile_128x128_split3", "tile_128x128_split4"]
+          "tile_128x128_split3", "tile_128x128_split4", "tile_64x128", "tile_64x128_split2", "tile_64x128_split3",
+          "tile_64x128_split4"]
 TILES4 = ["tile_128x128", "tile_128x128_split2", "tile_128x128_split3", "tile_128x128_split4"]
 
 
@@ -80,6 +81,23 @@ def test_w4a8_every_entry(M, N, K):
     for name in [n for n in TILES8 if n not in TILES4]:   # int8-only tiles
         with pytest.raises(prism.PrismError):
             prism.gemm_w4a8_variant(qd, sad, wd, swd, name)
+
+
+@pytest.mark.parametrize("M,K", [(31, 9728), (32, 7664), (32, 7680), (48, 5104), (48, 5120), (64, 3824), (64, 3840),
+                                 (64, 9728)])
+def test_w8a8_small_m_or_tiled(M, K):
+    """With int8 weights, 32 <= M <= 64 rows take the tiled path (64 x 128 or
+    128 x 128 tiles, K split by the cost model) once M K >= 245760, the
+    small-M kernel below that; the plain call must give the oracle's bits on
+    both sides of the boundary, and so must every small-M and tiled entry."""
+    N = 300
+    q, s_a, w, s_w = _inputs(M * 11 + K, M, N, K)
+    y_ref, acc_ref = oracle.gemm_w8a8(q, s_a, w, s_w)
+    names = ["auto"] + SMALL + [n for n in TILES8 if "128" in n]
+    _run_all(prism.gemm_w8a8_variant, names, dev(q), dev(s_a), dev(w), dev(s_w), y_ref, acc_ref)
+    y = prism.gemm_w8a8(dev(q), dev(s_a), dev(w), dev(s_w))
+    torch.cuda.synchronize()
+    assert_same_floats(host(y), y_ref, "y (plain call)")
 
 
 @pytest.mark.parametrize("M,N,K", [(70, 2052, 2080), (129, 1028, 1056), (3, 2560, 4096), (200, 1030, 1056),

@@ -24,36 +24,43 @@ int split_int4(int64_t t, int K) {
   return (int)splits;
 }
 
-// Tile height (128 or 64 rows, 128 columns) and K split s in 1..4 of the
-// int8 launches with few tiles, from a cost model fitted on MI355X (M in 32
-// ... 512, N and K in {2560, 5120, 9728}): per stage of 128 k, about 0.95 us
-// for 128 x 128 tiles and 0.71 us for 64 x 128 (24 instead of 32 KiB of
-// copies), times the stages per workgroup and the rounds of up to 256
-// workgroups, ceil(tiles s / 256) x ceil(stages / s); plus for s > 1 the
-// fill and in-place epilogue (about 2.3 us) and the atomic partial tiles
-// (about 4 us per split and million outputs).  Ties go to the taller tile and
+// Tile (128 x 128, 64 x 128 or 128 x 96) and K split s in 1..4 of the int8
+// launches with few tiles, from a cost model fitted on MI355X (M from 32 to
+// 1024, N in {2560, 5120, 9728, 17408}, K in {2560, 5120, 9728}): per stage
+// of 128 k, about 0.95 us for 128 x 128 tiles, 0.71 us for 64 x 128 and
+// 0.83 us for 128 x 96 (their copies are 32, 24 and 28 KiB), times the stages
+// per workgroup and the rounds of up to 256 workgroups, ceil(tiles s / 256)
+// x ceil(stages / s); plus for s > 1 the fill and in-place epilogue (about
+// 2.3 us) and the atomic partial tiles (about 4 us per split and million
+// outputs).  128 x 96 tiles pay only up to a 2-way split (with 3 or 4 they
+// were 1-4% slower than the other choices).  Ties go to the earlier tile and
 // the smaller split.  E.g. M = 512, N = K = 2560: 64 x 128, no split, 13 us
-// (128 x 128: 19 us, with a 2-way split 22); M = 512, N = 2560, K = 9728:
-// 128 x 128, 3 ways, 36 us.
+// (128 x 128: 19 us); M = 512, N = K = 5120: 128 x 96, no split, 32 us
+// (128 x 128: 35 us); M = 512, N = 2560, K = 9728: 128 x 128, 3 ways, 36 us.
 struct SplitChoice {
-  int bm;      // 128 or 64
+  int tile;    // 0: 128 x 128, 1: 64 x 128, 2: 128 x 96
   int splits;  // 1..4
 };
 
 SplitChoice split_for(int64_t M, int64_t N, int K) {
+  struct Shape {
+    int bm, bn, max_splits;
+    double per_stage;
+  };
+  static constexpr Shape kShapes[3] = {{128, 128, 4, 0.95}, {64, 128, 4, 0.71}, {128, 96, 2, 0.83}};
   const int64_t stages = (K + 127) / 128;
-  SplitChoice best{128, 1};
+  SplitChoice best{0, 1};
   double best_cost = 0.0;
   bool first = true;
-  for (int bm : {128, 64}) {
-    const int64_t t = tiles(M, N, bm, 128);
-    const double per_stage = bm == 128 ? 0.95 : 0.71;
-    for (int s = 1; s <= 4 && s <= stages; ++s) {
+  for (int i = 0; i < 3; ++i) {
+    const Shape& sh = kShapes[i];
+    const int64_t t = tiles(M, N, sh.bm, sh.bn);
+    for (int s = 1; s <= sh.max_splits && s <= stages; ++s) {
       const double rounds = (double)((t * s + 255) / 256);
-      double cost = per_stage * rounds * (double)((stages + s - 1) / s);
+      double cost = sh.per_stage * rounds * (double)((stages + s - 1) / s);
       if (s > 1) cost += 2.3 + 4.0 * (double)s * (double)(M * N) * 1e-6;
       if (first || cost < best_cost) {
-        best = SplitChoice{bm, s};
+        best = SplitChoice{i, s};
         best_cost = cost;
         first = false;
       }
@@ -76,9 +83,9 @@ SplitChoice split_for(int64_t M, int64_t N, int K) {
 //    fragments per phase (their accumulators take 160 registers);
 //  * 256 x 128 tiles: 8 waves of 64 x 64, 3-deep ring;
 //  * 128 x 128 tiles: 4 waves of 64 x 64, 4-deep ring, or, where split_for
-//    finds them faster, 64 x 128 tiles of 4 waves of 32 x 64; either with K
-//    split over up to 4 workgroups per tile (split_for) whose exact int32
-//    partial tiles are added atomically.
+//    finds them faster, 64 x 128 tiles of 4 waves of 32 x 64 or 128 x 96
+//    tiles of 4 waves of 32 x 96; with K split over up to 4 workgroups per
+//    tile (split_for) whose exact int32 partial tiles are added atomically.
 // E.g. M = 8192, N = K = 5120: 640 tiles of 256 x 256 take three rounds for
 // 2.5 rounds of work, 512 tiles of 256 x 320 exactly two (272 -> 245 us);
 // M = 2048, N = 5120: 216 tiles of 256 x 192 fill the CUs that 160 tiles of
@@ -99,7 +106,8 @@ void pick_int8(const int8_t* q, const float* s_a, const int8_t* w, const float* 
     case 3: tiled::dma::launch<256, 128, 128, 4, 2, 3, 1>(q, s_a, w, s_w, y, acc, M, N, K, st); break;
     default: {
       const SplitChoice c = split_for(M, N, K);
-      if (c.bm == 64) tiled::dma::launch<64, 128, 128, 2, 2, 4, 1>(q, s_a, w, s_w, y, acc, M, N, K, st, c.splits);
+      if (c.tile == 1) tiled::dma::launch<64, 128, 128, 2, 2, 4, 1>(q, s_a, w, s_w, y, acc, M, N, K, st, c.splits);
+      else if (c.tile == 2) tiled::dma::launch<128, 96, 128, 4, 1, 4, 1>(q, s_a, w, s_w, y, acc, M, N, K, st, c.splits);
       else tiled::dma::launch<128, 128, 128, 2, 2, 4, 1>(q, s_a, w, s_w, y, acc, M, N, K, st, c.splits);
     }
   }
@@ -119,8 +127,8 @@ void pick_int4(const int8_t* q, const float* s_a, const int8_t* w, const float* 
 
 // One named entry of the table above (7: 256 x 256, 8: 256 x 128, 9..12:
 // 128 x 128 with K split over 1..4 workgroups, 17: 256 x 192, 18: 256 x 320,
-// 19..22: 64 x 128 with K split over 1..4 workgroups; the 4-bit path has
-// 9..12).
+// 19..22: 64 x 128 with K split over 1..4 workgroups, 23, 24: 128 x 96 with
+// K split over 1, 2 workgroups; the 4-bit path has 9..12).
 int launch_gemm_tiled_variant(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
                               float* y, int32_t* acc, int M, int N, int K, int variant, hipStream_t st) {
   const int8_t* wb = static_cast<const int8_t*>(w);
@@ -150,6 +158,11 @@ int launch_gemm_tiled_variant(const int8_t* q, const float* s_a, const void* w, 
     int splits = variant - 18;
     if (splits > stages) splits = stages;
     tiled::dma::launch<64, 128, 128, 2, 2, 4, 1>(q, s_a, wb, s_w, y, acc, M, N, K, st, splits);
+  } else if (variant == 23 || variant == 24) {
+    const int stages = (K + 127) / 128;
+    int splits = variant - 22;
+    if (splits > stages) splits = stages;
+    tiled::dma::launch<128, 96, 128, 4, 1, 4, 1>(q, s_a, wb, s_w, y, acc, M, N, K, st, splits);
   } else {
     return PRISM_ERR_INVALID_ARG;
   }

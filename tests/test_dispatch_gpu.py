@@ -21,7 +21,7 @@ SMALL = ["small_1x4", "small_1x8", "small_1x16", "small_2x4", "small_2x8", "smal
          "small_4x4", "small_4x8"]
 TILES8 = ["tile_256x256", "tile_256x192", "tile_256x320", "tile_256x128", "tile_128x128", "tile_128x128_split2",
           "tile_128x128_split3", "tile_128x128_split4", "tile_64x128", "tile_64x128_split2", "tile_64x128_split3",
-          "tile_64x128_split4"]
+          "tile_64x128_split4", "tile_128x96", "tile_128x96_split2"]
 TILES4 = ["tile_128x128", "tile_128x128_split2", "tile_128x128_split3", "tile_128x128_split4"]
 
 
@@ -158,6 +158,27 @@ def test_256_row_tiles_full_size_sampled_rows(M, N, K):
     y_ref, acc_ref = oracle.gemm_w8a8(q[rows], s_a[rows], w, s_w)
     qd, sad, wd, swd = dev(q), dev(s_a), dev(w), dev(s_w)
     for name in ["auto", "tile_256x256", "tile_256x192", "tile_256x320"]:
+        acc = torch.full((M, N), 7, dtype=torch.int32, device=DEV)
+        y = prism.gemm_w8a8_variant(qd, sad, wd, swd, name, acc=acc)
+        torch.cuda.synchronize()
+        assert_same_ints(host(acc)[rows], acc_ref, "acc (%s)" % name)
+        assert_same_floats(host(y)[rows], y_ref, "y (%s)" % name)
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 5120, 5120), (1024, 2560, 9728), (96, 17408, 2560), (128, 9728, 2560),
+                                   (256, 2560, 9728), (64, 5120, 9728), (512, 2560, 2560)])
+def test_few_tile_shapes_full_size_sampled_rows(M, N, K):
+    """Shapes where the plain call picks 128 x 96 tiles (no split), 64 x 128
+    tiles (with and without a K split) or 128 x 128 tiles with a split, at full
+    size: the plain call and those entries, against the oracle on sampled rows
+    (the first and last rows of 64- and 128-row tiles among them)."""
+    q, s_a, w, s_w = _inputs(3 * M + N + K, M, N, K)
+    fixed = [r for r in (0, 1, 63, 64, 127, 128, M // 2, M - 65, M - 64, M - 1) if 0 <= r < M]
+    rows = np.unique(np.concatenate([fixed, np.random.default_rng(M * N).choice(M, min(M, 16), replace=False)]))
+    y_ref, acc_ref = oracle.gemm_w8a8(q[rows], s_a[rows], w, s_w)
+    qd, sad, wd, swd = dev(q), dev(s_a), dev(w), dev(s_w)
+    for name in ["auto", "tile_128x96", "tile_128x96_split2", "tile_64x128", "tile_64x128_split3",
+                 "tile_128x128_split3"]:
         acc = torch.full((M, N), 7, dtype=torch.int32, device=DEV)
         y = prism.gemm_w8a8_variant(qd, sad, wd, swd, name, acc=acc)
         torch.cuda.synchronize()

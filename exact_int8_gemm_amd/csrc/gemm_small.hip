@@ -68,14 +68,18 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(const int8_t* __
                                                                 const float* __restrict__ s_w,
                                                                 float* __restrict__ y,
                                                                 int32_t* __restrict__ acc_out, int M, int N,
-                                                                int K) {
+                                                                int K, int G) {
   __shared__ int red[WAVES][CB * MB * 4][64];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15;
   const int g = lane >> 4;
-  const int n0 = blockIdx.x * 16 * CB;
+  // Columns [n0, n1) of this workgroup: blocks of 16 CB (G == 0), or the
+  // b-th of G even shares of N (G > 0; the host makes every share fit in
+  // 16 CB columns), so that every CU streams the same number of weight rows.
+  const int n0 = G > 0 ? (int)((int64_t)blockIdx.x * N / G) : blockIdx.x * 16 * CB;
+  const int n1 = G > 0 ? (int)((int64_t)(blockIdx.x + 1) * N / G) : min(n0 + 16 * CB, N);
 
   const int nunits = (K + kUnitK - 1) / kUnitK;
   const int ub = (int)((int64_t)wave * nunits / WAVES);
@@ -88,7 +92,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(const int8_t* __
   uint32_t wbase[CB], qbase[MB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb)
-    wbase[cb] = (n0 + cb * 16 + col < N) ? (uint32_t)((cb * 16 + col) * wrow) : kOutOfRange;
+    wbase[cb] = (n0 + cb * 16 + col < n1) ? (uint32_t)((cb * 16 + col) * wrow) : kOutOfRange;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) qbase[mb] = (mb * 16 + col < M) ? (uint32_t)((mb * 16 + col) * K) : kOutOfRange;
 
@@ -103,7 +107,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(const int8_t* __
     const int idx = e >> 6, l = e & 63;
     const int m = ((idx / 4) % MB) * 16 + (l >> 4) * 4 + idx % 4;
     const int n = n0 + (idx / (MB * 4)) * 16 + (l & 15);
-    const bool ok = e < kOut && m < M && n < N;
+    const bool ok = e < kOut && m < M && n < n1;
     ea[t] = ok ? s_a[m] : 0.0f;
     ew[t] = ok ? s_w[n] : 0.0f;
   }
@@ -184,7 +188,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(const int8_t* __
     const int cb = idx / (MB * 4), mb = (idx / 4) % MB, i = idx % 4;
     const int m = mb * 16 + (l >> 4) * 4 + i;
     const int n = n0 + cb * 16 + (l & 15);
-    if (m < M && n < N) {
+    if (m < M && n < n1) {
       const size_t o = (size_t)m * (size_t)N + (size_t)n;
       if (acc_out) acc_out[o] = s;
       const float v = (float)s * ea[t];
@@ -193,12 +197,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(const int8_t* __
   }
 }
 
+// G > 0: G workgroups with even shares of the N columns (each share at most
+// 16 CB columns); G == 0: one workgroup per 16 CB columns.
 template <int MB, int CB, bool W4, int WAVES>
 void launch_small(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc,
-                  int M, int N, int K, hipStream_t st) {
+                  int M, int N, int K, int G, hipStream_t st) {
   constexpr int U = MB >= 4 ? 2 : 4;  // units per batch: keeps the batch's registers under ~100 VGPRs
-  const unsigned grid = (unsigned)((N + 16 * CB - 1) / (16 * CB));
-  gemm_small_kernel<MB, CB, W4, WAVES, U><<<grid, 64 * WAVES, 0, st>>>(q, s_a, w, s_w, y, acc, M, N, K);
+  const unsigned grid = G > 0 ? (unsigned)G : (unsigned)((N + 16 * CB - 1) / (16 * CB));
+  gemm_small_kernel<MB, CB, W4, WAVES, U><<<grid, 64 * WAVES, 0, st>>>(q, s_a, w, s_w, y, acc, M, N, K, G);
 }
 
 // Column blocks per workgroup and waves per workgroup, from sweeps on MI355X
@@ -219,8 +225,15 @@ void launch_small(const int8_t* q, const float* s_a, const int8_t* w, const floa
 //    waves once K >= 3072 (four 128-k units per wave), int8 weights 4 waves up
 //    to K = 5120 and 8 above; M > 32: 4 waves with two blocks, else 16 waves
 //    (N >= 4096) or 8.
-void choose_small(int M, int N, int K, bool w4, int& cb, int& waves) {
+int waves_for(int M, int N, int K, bool w4, int cb) {
   const int64_t nunits = (K + kUnitK - 1) / kUnitK;
+  if (cb >= 3) return 8;
+  if (M <= 32) return w4 ? (nunits >= 24 ? 8 : 4) : (nunits <= 40 ? 4 : 8);
+  if (cb == 2) return 4;
+  return N >= 4096 ? 16 : 8;
+}
+
+void choose_small(int M, int N, int K, bool w4, int& cb, int& waves) {
   const int64_t blocks = (N + 15) / 16;
   int64_t best = -1;
   for (int c = 1; c <= 4; ++c) {
@@ -230,26 +243,23 @@ void choose_small(int M, int N, int K, bool w4, int& cb, int& waves) {
       cb = c;
     }
   }
-  if (cb >= 3) waves = 8;
-  else if (M <= 32) waves = w4 ? (nunits >= 24 ? 8 : 4) : (nunits <= 40 ? 4 : 8);
-  else if (cb == 2) waves = 4;
-  else waves = N >= 4096 ? 16 : 8;
+  waves = waves_for(M, N, K, w4, cb);
 }
 
 template <bool W4>
 bool pick_variant(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc,
-                  int M, int N, int K, int cb, int waves, hipStream_t st) {
+                  int M, int N, int K, int cb, int waves, int G, hipStream_t st) {
 #define PRISM_SMALL_CASE(MB)                                                                              \
-  if (cb == 1 && waves == 4) launch_small<MB, 1, W4, 4>(q, s_a, w, s_w, y, acc, M, N, K, st);           \
-  else if (cb == 1 && waves == 8) launch_small<MB, 1, W4, 8>(q, s_a, w, s_w, y, acc, M, N, K, st);      \
-  else if (cb == 1 && waves == 16) launch_small<MB, 1, W4, 16>(q, s_a, w, s_w, y, acc, M, N, K, st);    \
-  else if (cb == 2 && waves == 4) launch_small<MB, 2, W4, 4>(q, s_a, w, s_w, y, acc, M, N, K, st);      \
-  else if (cb == 2 && waves == 8) launch_small<MB, 2, W4, 8>(q, s_a, w, s_w, y, acc, M, N, K, st);      \
-  else if (cb == 2 && waves == 16) launch_small<MB, 2, W4, 16>(q, s_a, w, s_w, y, acc, M, N, K, st);    \
-  else if (cb == 3 && waves == 4) launch_small<MB, 3, W4, 4>(q, s_a, w, s_w, y, acc, M, N, K, st);      \
-  else if (cb == 3 && waves == 8) launch_small<MB, 3, W4, 8>(q, s_a, w, s_w, y, acc, M, N, K, st);      \
-  else if (cb == 4 && waves == 4) launch_small<MB, 4, W4, 4>(q, s_a, w, s_w, y, acc, M, N, K, st);      \
-  else if (cb == 4 && waves == 8) launch_small<MB, 4, W4, 8>(q, s_a, w, s_w, y, acc, M, N, K, st);      \
+  if (cb == 1 && waves == 4) launch_small<MB, 1, W4, 4>(q, s_a, w, s_w, y, acc, M, N, K, G, st);           \
+  else if (cb == 1 && waves == 8) launch_small<MB, 1, W4, 8>(q, s_a, w, s_w, y, acc, M, N, K, G, st);      \
+  else if (cb == 1 && waves == 16) launch_small<MB, 1, W4, 16>(q, s_a, w, s_w, y, acc, M, N, K, G, st);    \
+  else if (cb == 2 && waves == 4) launch_small<MB, 2, W4, 4>(q, s_a, w, s_w, y, acc, M, N, K, G, st);      \
+  else if (cb == 2 && waves == 8) launch_small<MB, 2, W4, 8>(q, s_a, w, s_w, y, acc, M, N, K, G, st);      \
+  else if (cb == 2 && waves == 16) launch_small<MB, 2, W4, 16>(q, s_a, w, s_w, y, acc, M, N, K, G, st);    \
+  else if (cb == 3 && waves == 4) launch_small<MB, 3, W4, 4>(q, s_a, w, s_w, y, acc, M, N, K, G, st);      \
+  else if (cb == 3 && waves == 8) launch_small<MB, 3, W4, 8>(q, s_a, w, s_w, y, acc, M, N, K, G, st);      \
+  else if (cb == 4 && waves == 4) launch_small<MB, 4, W4, 4>(q, s_a, w, s_w, y, acc, M, N, K, G, st);      \
+  else if (cb == 4 && waves == 8) launch_small<MB, 4, W4, 8>(q, s_a, w, s_w, y, acc, M, N, K, G, st);      \
   else return false;
   if (M <= 16) { PRISM_SMALL_CASE(1) }
   else if (M <= 32) { PRISM_SMALL_CASE(2) }
@@ -609,11 +619,23 @@ int launch_gemm_block_small(const int8_t* q, const float* s_a, const int8_t* w, 
 }
 
 int launch_gemm_small_variant(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
-                              float* y, int32_t* acc, int M, int N, int K, int cb, int waves, hipStream_t st) {
+                              float* y, int32_t* acc, int M, int N, int K, int cb, int waves, hipStream_t st, int G) {
   const int8_t* wb = static_cast<const int8_t*>(w);
-  const bool ok = w_is_int4 ? pick_variant<true>(q, s_a, wb, s_w, y, acc, M, N, K, cb, waves, st)
-                            : pick_variant<false>(q, s_a, wb, s_w, y, acc, M, N, K, cb, waves, st);
+  const bool ok = w_is_int4 ? pick_variant<true>(q, s_a, wb, s_w, y, acc, M, N, K, cb, waves, G, st)
+                            : pick_variant<false>(q, s_a, wb, s_w, y, acc, M, N, K, cb, waves, G, st);
   return ok ? launch_status() : PRISM_ERR_INVALID_ARG;
+}
+
+// Even column shares: min(256, N) workgroups (one per CU), each with at most
+// 16 cb columns, cb = ceil(ceil(N / 256) / 16) <= 4.
+int launch_gemm_small_balanced(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
+                               float* y, int32_t* acc, int M, int N, int K, hipStream_t st) {
+  const int G = N < 256 ? N : 256;
+  const int share = (N + G - 1) / G;
+  const int cb = (share + 15) / 16;
+  if (cb > 4) return PRISM_ERR_INVALID_ARG;
+  return launch_gemm_small_variant(q, s_a, w, w_is_int4, s_w, y, acc, M, N, K, cb,
+                                   waves_for(M, N, K, w_is_int4, cb), st, G);
 }
 
 int launch_gemm_small(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
@@ -623,6 +645,15 @@ int launch_gemm_small(const int8_t* q, const float* s_a, const void* w, bool w_i
     return launch_status();
   int cb, waves;
   choose_small(M, N, K, w_is_int4, cb, waves);
+  // Blocks of 16 cb columns that do not fill whole rounds of 256 CUs leave
+  // some CUs reading more weight rows than others: then one even share of
+  // the columns per CU instead (M <= 16 on MI355X, same bits: int8 2560 x
+  // 9728, M = 2: 9.8 -> 8.4 us; 5120 x 5120, M = 4: 9.5 -> 8.6 us; 4-bit
+  // 5120 x 5120, M = 1: 7.4 -> 6.2 us; N = 12288, whose 768 blocks already
+  // fill the CUs evenly, keeps its blocks).
+  const int64_t groups = (N + 16 * cb - 1) / (16 * cb);
+  if (groups % 256 != 0 && N <= 16384)
+    return launch_gemm_small_balanced(q, s_a, w, w_is_int4, s_w, y, acc, M, N, K, st);
   return launch_gemm_small_variant(q, s_a, w, w_is_int4, s_w, y, acc, M, N, K, cb, waves, st);
 }
 

@@ -95,6 +95,10 @@ int run_variant(const int8_t* q, const float* s_a, const void* w, bool w4, const
     const int* e = kSmallWide[variant - PRISM_VARIANT_SMALL_3x4];
     return prism::launch_gemm_small_variant(q, s_a, w, w4, s_w, y, acc, (int)M, (int)N, (int)K, e[0], e[1], s);
   }
+  if (variant == PRISM_VARIANT_SMALL_BALANCED) {
+    if (M > prism::kSmallMMax) return PRISM_ERR_INVALID_ARG;
+    return prism::launch_gemm_small_balanced(q, s_a, w, w4, s_w, y, acc, (int)M, (int)N, (int)K, s);
+  }
   if ((variant >= PRISM_VARIANT_TILE_256x256 && variant <= PRISM_VARIANT_TILE_128x128_SPLIT4) ||
       (variant >= PRISM_VARIANT_TILE_256x192 && variant <= PRISM_VARIANT_TILE_128x96_SPLIT2))
     return prism::launch_gemm_tiled_variant(q, s_a, w, w4, s_w, y, acc, (int)M, (int)N, (int)K, variant, s);

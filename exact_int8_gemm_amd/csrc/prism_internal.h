@@ -41,8 +41,14 @@ bool launch_quantize_gemv(const float* x, int8_t* q, float* s_a, const int8_t* w
 int launch_gemm_tiled(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
                       float* y, int32_t* acc, int M, int N, int K, hipStream_t st);
 
+// G > 0: G workgroups with even shares of the N columns, each at most 16 cb.
 int launch_gemm_small_variant(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
-                              float* y, int32_t* acc, int M, int N, int K, int cb, int waves, hipStream_t st);
+                              float* y, int32_t* acc, int M, int N, int K, int cb, int waves, hipStream_t st,
+                              int G = 0);
+// The small-M kernel with one even column share per CU (PRISM_ERR_INVALID_ARG
+// when a share would exceed 64 columns, i.e. N > 16384).
+int launch_gemm_small_balanced(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
+                               float* y, int32_t* acc, int M, int N, int K, hipStream_t st);
 int launch_gemm_tiled_variant(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
                               float* y, int32_t* acc, int M, int N, int K, int variant, hipStream_t st);
 int launch_gemm_blockscale(const int8_t* q, const float* s_a, const int8_t* w, const uint16_t* d, float* y,

@@ -41,7 +41,7 @@ extern "C" {
 #endif
 
 /* Bumped on any change of a signature or of the semantics below. */
-#define PRISM_ABI_VERSION 7
+#define PRISM_ABI_VERSION 8
 
 /* Largest accepted K.  For K <= 131040 every exact sum of K products of two
  * int8 values (|q|, |w| <= 128) lies strictly inside the int32 range. */
@@ -211,6 +211,8 @@ int prism_gemm_w4a8(const int8_t* q, const float* s_a, const uint8_t* w4, const 
  *   PRISM_VARIANT_SMALL_<c>x<w>   the small-M kernel with c column blocks of
  *                                 16 (c = 1..4) and w waves per workgroup
  *                                 (M <= 64 only);
+ *   PRISM_VARIANT_SMALL_BALANCED  the small-M kernel with one even share of
+ *                                 the N columns per CU (M <= 64, N <= 16384);
  *   PRISM_VARIANT_TILE_*          the LDS-tiled kernels: 256x192, 256x256,
  *                                 256x320, 256x128, 64x128 and 128x96 (int8
  *                                 weights only), 128x128, and 128x128 or
@@ -244,7 +246,8 @@ int prism_gemm_w4a8(const int8_t* q, const float* s_a, const uint8_t* w4, const 
 #define PRISM_VARIANT_TILE_64x128_SPLIT4 22
 #define PRISM_VARIANT_TILE_128x96 23
 #define PRISM_VARIANT_TILE_128x96_SPLIT2 24
-#define PRISM_VARIANT_COUNT 25
+#define PRISM_VARIANT_SMALL_BALANCED 25
+#define PRISM_VARIANT_COUNT 26
 
 int prism_gemm_w8a8_variant(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w,
                             float* y, int32_t* acc, int64_t M, int64_t N, int64_t K, int variant,

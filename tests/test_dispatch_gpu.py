@@ -18,7 +18,7 @@ from gpu_util import DEV, assert_same_floats, assert_same_ints, dev, host
 pytestmark = pytest.mark.gpu
 
 SMALL = ["small_1x4", "small_1x8", "small_1x16", "small_2x4", "small_2x8", "small_2x16", "small_3x4", "small_3x8",
-         "small_4x4", "small_4x8"]
+         "small_4x4", "small_4x8", "small_balanced"]
 TILES8 = ["tile_256x256", "tile_256x192", "tile_256x320", "tile_256x128", "tile_128x128", "tile_128x128_split2",
           "tile_128x128_split3", "tile_128x128_split4", "tile_64x128", "tile_64x128_split2", "tile_64x128_split3",
           "tile_64x128_split4", "tile_128x96", "tile_128x96_split2"]

@@ -27,16 +27,17 @@ int split_int4(int64_t t, int K) {
 // Tile (128 x 128, 64 x 128 or 128 x 96) and K split s in 1..4 of the int8
 // launches with few tiles, from a cost model fitted on MI355X (M from 32 to
 // 1024, N in {2560, 5120, 9728, 17408}, K in {2560, 5120, 9728}): per stage
-// of 128 k, about 0.95 us for 128 x 128 tiles, 0.71 us for 64 x 128 and
-// 0.83 us for 128 x 96 (their copies are 32, 24 and 28 KiB), times the stages
+// of 128 k, about 0.86 us for 128 x 128 tiles, 0.65 us for 64 x 128 (both
+// with 8 waves) and 0.83 us for 128 x 96 (4 waves; copies of 32, 24 and 28
+// KiB), times the stages
 // per workgroup and the rounds of up to 256 workgroups, ceil(tiles s / 256)
 // x ceil(stages / s); plus for s > 1 the fill and in-place epilogue (about
 // 2.3 us) and the atomic partial tiles (about 4 us per split and million
 // outputs).  128 x 96 tiles pay only up to a 2-way split (with 3 or 4 they
 // were 1-4% slower than the other choices).  Ties go to the earlier tile and
-// the smaller split.  E.g. M = 512, N = K = 2560: 64 x 128, no split, 13 us
-// (128 x 128: 19 us); M = 512, N = K = 5120: 128 x 96, no split, 32 us
-// (128 x 128: 35 us); M = 512, N = 2560, K = 9728: 128 x 128, 3 ways, 36 us.
+// the smaller split.  E.g. M = 512, N = K = 2560: 64 x 128, no split, 11 us
+// (128 x 128: 16 us); M = 512, N = K = 5120: 128 x 96, no split, 31 us;
+// M = 512, N = 2560, K = 9728: 128 x 128, 3 ways, 36 us.
 struct SplitChoice {
   int tile;    // 0: 128 x 128, 1: 64 x 128, 2: 128 x 96
   int splits;  // 1..4
@@ -47,7 +48,7 @@ SplitChoice split_for(int64_t M, int64_t N, int K) {
     int bm, bn, max_splits;
     double per_stage;
   };
-  static constexpr Shape kShapes[3] = {{128, 128, 4, 0.95}, {64, 128, 4, 0.71}, {128, 96, 2, 0.83}};
+  static constexpr Shape kShapes[3] = {{128, 128, 4, 0.86}, {64, 128, 4, 0.65}, {128, 96, 2, 0.83}};
   const int64_t stages = (K + 127) / 128;
   SplitChoice best{0, 1};
   double best_cost = 0.0;
@@ -82,10 +83,12 @@ SplitChoice split_for(int64_t M, int64_t N, int K) {
 //    128-byte stages, 2-deep ring; the 320-wide tiles read one 32-k step of
 //    fragments per phase (their accumulators take 160 registers);
 //  * 256 x 128 tiles: 8 waves of 64 x 64, 3-deep ring;
-//  * 128 x 128 tiles: 4 waves of 64 x 64, 4-deep ring, or, where split_for
-//    finds them faster, 64 x 128 tiles of 4 waves of 32 x 64 or 128 x 96
+//  * 128 x 128 tiles: 8 waves of 32 x 64, 4-deep ring, or, where split_for
+//    finds them faster, 64 x 128 tiles of 8 waves of 32 x 32 or 128 x 96
 //    tiles of 4 waves of 32 x 96; with K split over up to 4 workgroups per
 //    tile (split_for) whose exact int32 partial tiles are added atomically.
+//    (8 waves instead of 4 took 2-20% off the 128 x 128 and 64 x 128
+//    launches, e.g. M = 512, N = K = 2560 unsplit: 20.4 -> 16.4 us.)
 // E.g. M = 8192, N = K = 5120: 640 tiles of 256 x 256 take three rounds for
 // 2.5 rounds of work, 512 tiles of 256 x 320 exactly two (272 -> 245 us);
 // M = 2048, N = 5120: 216 tiles of 256 x 192 fill the CUs that 160 tiles of
@@ -106,9 +109,9 @@ void pick_int8(const int8_t* q, const float* s_a, const int8_t* w, const float* 
     case 3: tiled::dma::launch<256, 128, 128, 4, 2, 3, 1>(q, s_a, w, s_w, y, acc, M, N, K, st); break;
     default: {
       const SplitChoice c = split_for(M, N, K);
-      if (c.tile == 1) tiled::dma::launch<64, 128, 128, 2, 2, 4, 1>(q, s_a, w, s_w, y, acc, M, N, K, st, c.splits);
+      if (c.tile == 1) tiled::dma::launch<64, 128, 128, 2, 4, 4, 1>(q, s_a, w, s_w, y, acc, M, N, K, st, c.splits);
       else if (c.tile == 2) tiled::dma::launch<128, 96, 128, 4, 1, 4, 1>(q, s_a, w, s_w, y, acc, M, N, K, st, c.splits);
-      else tiled::dma::launch<128, 128, 128, 2, 2, 4, 1>(q, s_a, w, s_w, y, acc, M, N, K, st, c.splits);
+      else tiled::dma::launch<128, 128, 128, 4, 2, 4, 1>(q, s_a, w, s_w, y, acc, M, N, K, st, c.splits);
     }
   }
 }
@@ -152,12 +155,12 @@ int launch_gemm_tiled_variant(const int8_t* q, const float* s_a, const void* w, 
     const int stages = (K + 127) / 128;
     int splits = variant - 8;
     if (splits > stages) splits = stages;
-    tiled::dma::launch<128, 128, 128, 2, 2, 4, 1>(q, s_a, wb, s_w, y, acc, M, N, K, st, splits);
+    tiled::dma::launch<128, 128, 128, 4, 2, 4, 1>(q, s_a, wb, s_w, y, acc, M, N, K, st, splits);
   } else if (variant >= 19 && variant <= 22) {
     const int stages = (K + 127) / 128;
     int splits = variant - 18;
     if (splits > stages) splits = stages;
-    tiled::dma::launch<64, 128, 128, 2, 2, 4, 1>(q, s_a, wb, s_w, y, acc, M, N, K, st, splits);
+    tiled::dma::launch<64, 128, 128, 2, 4, 4, 1>(q, s_a, wb, s_w, y, acc, M, N, K, st, splits);
   } else if (variant == 23 || variant == 24) {
     const int stages = (K + 127) / 128;
     int splits = variant - 22;

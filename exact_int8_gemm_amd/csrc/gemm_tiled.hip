@@ -118,12 +118,13 @@ void pick_int8(const int8_t* q, const float* s_a, const int8_t* w, const float* 
 }
 
 // 4-bit weights: register-staged pipeline that unpacks the nibbles on their
-// way into LDS; 128 x 128 tiles, with K split (split_int4) when there are
-// fewer tiles than CUs.
+// way into LDS; 128 x 128 tiles of 8 waves (32 x 64 each; 4-20% faster than
+// 4 waves of 64 x 64, e.g. M = 256, N = K = 5120: 38.5 -> 30.3 us), with K
+// split (split_int4) when there are fewer tiles than CUs.
 
 void pick_int4(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc, int M,
                int N, int K, hipStream_t st) {
-  launch_tiled<128, 128, 128, 2, 2, true, 2>(q, s_a, w, s_w, y, acc, M, N, K, st,
+  launch_tiled<128, 128, 128, 4, 2, true, 2>(q, s_a, w, s_w, y, acc, M, N, K, st,
                                               split_int4(tiles(M, N, 128, 128), K));
 }
 
@@ -141,7 +142,7 @@ int launch_gemm_tiled_variant(const int8_t* q, const float* s_a, const void* w, 
     const int stages = (K + 127) / 128;
     int splits = variant - 8;
     if (splits > stages) splits = stages;
-    launch_tiled<128, 128, 128, 2, 2, true, 2>(q, s_a, wb, s_w, y, acc, M, N, K, st, splits);
+    launch_tiled<128, 128, 128, 4, 2, true, 2>(q, s_a, wb, s_w, y, acc, M, N, K, st, splits);
     return launch_status();
   }
   if (variant == 7) {

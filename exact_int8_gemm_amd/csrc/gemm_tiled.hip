@@ -25,19 +25,20 @@ int split_int4(int64_t t, int K) {
 }
 
 // Tile (128 x 128, 64 x 128 or 128 x 96) and K split s in 1..4 of the int8
-// launches with few tiles, from a cost model fitted on MI355X (M from 32 to
-// 1024, N in {2560, 5120, 9728, 17408}, K in {2560, 5120, 9728}): per stage
-// of 128 k, about 0.86 us for 128 x 128 tiles, 0.65 us for 64 x 128 (both
-// with 8 waves) and 0.83 us for 128 x 96 (4 waves; copies of 32, 24 and 28
-// KiB), times the stages
-// per workgroup and the rounds of up to 256 workgroups, ceil(tiles s / 256)
-// x ceil(stages / s); plus for s > 1 the fill and in-place epilogue (about
-// 2.3 us) and the atomic partial tiles (about 4 us per split and million
-// outputs).  128 x 96 tiles pay only up to a 2-way split (with 3 or 4 they
-// were 1-4% slower than the other choices).  Ties go to the earlier tile and
-// the smaller split.  E.g. M = 512, N = K = 2560: 64 x 128, no split, 11 us
-// (128 x 128: 16 us); M = 512, N = K = 5120: 128 x 96, no split, 31 us;
-// M = 512, N = 2560, K = 9728: 128 x 128, 3 ways, 36 us.
+// launches with few tiles, from a cost model fitted on MI355X (51 shapes, M
+// from 64 to 1024, N and K in {2560, 5120, 9728}, every candidate timed): per
+// stage of 128 k, about 0.80 us for 128 x 128 tiles, 0.60 us for 64 x 128
+// (both with 8 waves) and 0.78 us for 128 x 96 (4 waves; copies of 32, 24 and
+// 28 KiB), times the stages per workgroup and the rounds of up to 256
+// workgroups, ceil(tiles s / 256) x ceil(stages / s); plus for s > 1 the fill,
+// the in-place epilogue and the atomic partial tiles, about 5 us and 5 us
+// per split and million outputs.  128 x 96 tiles pay only up to a 2-way
+// split (with 3 or 4 they were 1-4% slower than the other choices).  Ties
+// go to the earlier tile and the smaller split.  On the 51 shapes the pick
+// was on average 0.2% and at most 5% slower than the best candidate.  E.g.
+// M = 512, N = K = 2560: 64 x 128, no split, 11 us (128 x 128: 16 us);
+// M = 512, N = K = 5120: 128 x 96, no split, 31 us; M = 512, N = 2560,
+// K = 9728: 128 x 128, 3 ways, 36 us.
 struct SplitChoice {
   int tile;    // 0: 128 x 128, 1: 64 x 128, 2: 128 x 96
   int splits;  // 1..4
@@ -48,7 +49,7 @@ SplitChoice split_for(int64_t M, int64_t N, int K) {
     int bm, bn, max_splits;
     double per_stage;
   };
-  static constexpr Shape kShapes[3] = {{128, 128, 4, 0.86}, {64, 128, 4, 0.65}, {128, 96, 2, 0.83}};
+  static constexpr Shape kShapes[3] = {{128, 128, 4, 0.80}, {64, 128, 4, 0.60}, {128, 96, 2, 0.78}};
   const int64_t stages = (K + 127) / 128;
   SplitChoice best{0, 1};
   double best_cost = 0.0;
@@ -59,7 +60,7 @@ SplitChoice split_for(int64_t M, int64_t N, int K) {
     for (int s = 1; s <= sh.max_splits && s <= stages; ++s) {
       const double rounds = (double)((t * s + 255) / 256);
       double cost = sh.per_stage * rounds * (double)((stages + s - 1) / s);
-      if (s > 1) cost += 2.3 + 4.0 * (double)s * (double)(M * N) * 1e-6;
+      if (s > 1) cost += 5.0 + 5.0 * (double)s * (double)(M * N) * 1e-6;
       if (first || cost < best_cost) {
         best = SplitChoice{i, s};
         best_cost = cost;

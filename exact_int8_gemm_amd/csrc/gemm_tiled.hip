@@ -78,11 +78,14 @@ SplitChoice split_for(int64_t M, int64_t N, int K) {
 // MI355X): 256 x 192 0.83 and 256 x 320 1.23 (one-round launches at M = 2048,
 // N = K = 5120), 256 x 128 0.60 and 128 x 128 0.45 (M = 8192, three (N, K)
 // shapes).  The shape with the smallest estimate wins; ties go to the earlier
-// shape in the order 256 x 256, 256 x 320, 256 x 192, 256 x 128, 128 x 128:
+// shape in the order 256 x 256, 256 x 320, 256 x 192, 256 x 128, 128 x 128,
+// 192 x 128 (0.55: 9-13% faster than 256 x 128 where its tiles fit in one
+// round or save one, e.g. M = 512, N = 9728, K = 2560: 28.2 -> 25.6 us):
 //  * 256 x 192 / 256 / 320 tiles: 8 waves of 64 x (tile width / 2) in two
 //    groups that alternate between MFMAs and LDS reads (gemm_pingpong.h),
 //    128-byte stages, 2-deep ring; the 320-wide tiles read one 32-k step of
 //    fragments per phase (their accumulators take 160 registers);
+//  * 192 x 128 tiles: 8 waves of 96 x 32, 3-deep ring;
 //  * 256 x 128 tiles: 16 waves of 64 x 32, 3-deep ring (16 waves instead of
 //    8: 5-15% faster, e.g. M = 512, N = 9728, K = 2560: 30.6 -> 27.9 us);
 //  * 128 x 128 tiles: 8 waves of 32 x 64, 4-deep ring, or, where split_for
@@ -98,17 +101,18 @@ SplitChoice split_for(int64_t M, int64_t N, int K) {
 void pick_int8(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc, int M,
                int N, int K, hipStream_t st) {
   auto rounds = [](int64_t t) { return (double)((t + 255) / 256); };
-  const double cost[5] = {rounds(tiles(M, N, 256, 256)), 1.23 * rounds(tiles(M, N, 256, 320)),
+  const double cost[6] = {rounds(tiles(M, N, 256, 256)),        1.23 * rounds(tiles(M, N, 256, 320)),
                           0.83 * rounds(tiles(M, N, 256, 192)), 0.60 * rounds(tiles(M, N, 256, 128)),
-                          0.45 * rounds(tiles(M, N, 128, 128))};
+                          0.45 * rounds(tiles(M, N, 128, 128)), 0.55 * rounds(tiles(M, N, 192, 128))};
   int best = 0;
-  for (int i = 1; i < 5; ++i)
+  for (int i = 1; i < 6; ++i)
     if (cost[i] < cost[best]) best = i;
   switch (best) {
     case 0: tiled::dma::launch_pp<128, 2>(q, s_a, w, s_w, y, acc, M, N, K, st); break;
     case 1: tiled::dma::launch_pp<128, 2, 320, 1>(q, s_a, w, s_w, y, acc, M, N, K, st); break;
     case 2: tiled::dma::launch_pp<128, 2, 192>(q, s_a, w, s_w, y, acc, M, N, K, st); break;
     case 3: tiled::dma::launch<256, 128, 128, 4, 4, 3, 1>(q, s_a, w, s_w, y, acc, M, N, K, st); break;
+    case 5: tiled::dma::launch<192, 128, 128, 2, 4, 3, 1>(q, s_a, w, s_w, y, acc, M, N, K, st); break;
     default: {
       const SplitChoice c = split_for(M, N, K);
       if (c.tile == 1) tiled::dma::launch<64, 128, 128, 2, 4, 4, 1>(q, s_a, w, s_w, y, acc, M, N, K, st, c.splits);
@@ -134,7 +138,7 @@ void pick_int4(const int8_t* q, const float* s_a, const int8_t* w, const float* 
 // One named entry of the table above (7: 256 x 256, 8: 256 x 128, 9..12:
 // 128 x 128 with K split over 1..4 workgroups, 17: 256 x 192, 18: 256 x 320,
 // 19..22: 64 x 128 with K split over 1..4 workgroups, 23, 24: 128 x 96 with
-// K split over 1, 2 workgroups; the 4-bit path has 9..12).
+// K split over 1, 2 workgroups, 26: 192 x 128; the 4-bit path has 9..12).
 int launch_gemm_tiled_variant(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
                               float* y, int32_t* acc, int M, int N, int K, int variant, hipStream_t st) {
   const int8_t* wb = static_cast<const int8_t*>(w);
@@ -164,6 +168,8 @@ int launch_gemm_tiled_variant(const int8_t* q, const float* s_a, const void* w, 
     int splits = variant - 18;
     if (splits > stages) splits = stages;
     tiled::dma::launch<64, 128, 128, 2, 4, 4, 1>(q, s_a, wb, s_w, y, acc, M, N, K, st, splits);
+  } else if (variant == 26) {
+    tiled::dma::launch<192, 128, 128, 2, 4, 3, 1>(q, s_a, wb, s_w, y, acc, M, N, K, st);
   } else if (variant == 23 || variant == 24) {
     const int stages = (K + 127) / 128;
     int splits = variant - 22;

@@ -100,7 +100,8 @@ int run_variant(const int8_t* q, const float* s_a, const void* w, bool w4, const
     return prism::launch_gemm_small_balanced(q, s_a, w, w4, s_w, y, acc, (int)M, (int)N, (int)K, s);
   }
   if ((variant >= PRISM_VARIANT_TILE_256x256 && variant <= PRISM_VARIANT_TILE_128x128_SPLIT4) ||
-      (variant >= PRISM_VARIANT_TILE_256x192 && variant <= PRISM_VARIANT_TILE_128x96_SPLIT2))
+      (variant >= PRISM_VARIANT_TILE_256x192 && variant <= PRISM_VARIANT_TILE_128x96_SPLIT2) ||
+      variant == PRISM_VARIANT_TILE_192x128)
     return prism::launch_gemm_tiled_variant(q, s_a, w, w4, s_w, y, acc, (int)M, (int)N, (int)K, variant, s);
   return PRISM_ERR_INVALID_ARG;
 }

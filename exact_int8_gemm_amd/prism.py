@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libprism.so")
 
 PRISM_OK = 0
-ABI_VERSION = 8
+ABI_VERSION = 9
 K_MAX = 131040
 
 # Dispatch-table entries of the W8A8 / W4A8 calls (PRISM_VARIANT_* in include/prism.h).
@@ -27,7 +27,8 @@ VARIANTS = {"auto": 0, "small_1x4": 1, "small_1x8": 2, "small_1x16": 3, "small_2
             "tile_128x128_split3": 11, "tile_128x128_split4": 12, "small_3x4": 13, "small_3x8": 14,
             "small_4x4": 15, "small_4x8": 16, "tile_256x192": 17, "tile_256x320": 18, "tile_64x128": 19,
             "tile_64x128_split2": 20, "tile_64x128_split3": 21, "tile_64x128_split4": 22, "tile_128x96": 23,
-            "tile_128x96_split2": 24, "small_balanced": 25}
+            "tile_128x96_split2": 24, "small_balanced": 25,
+            "tile_192x128": 26}
 
 
 class PrismError(RuntimeError):

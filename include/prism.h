@@ -41,7 +41,7 @@ extern "C" {
 #endif
 
 /* Bumped on any change of a signature or of the semantics below. */
-#define PRISM_ABI_VERSION 8
+#define PRISM_ABI_VERSION 9
 
 /* Largest accepted K.  For K <= 131040 every exact sum of K products of two
  * int8 values (|q|, |w| <= 128) lies strictly inside the int32 range. */
@@ -214,8 +214,8 @@ int prism_gemm_w4a8(const int8_t* q, const float* s_a, const uint8_t* w4, const 
  *   PRISM_VARIANT_SMALL_BALANCED  the small-M kernel with one even share of
  *                                 the N columns per CU (M <= 64, N <= 16384);
  *   PRISM_VARIANT_TILE_*          the LDS-tiled kernels: 256x192, 256x256,
- *                                 256x320, 256x128, 64x128 and 128x96 (int8
- *                                 weights only), 128x128, and 128x128 or
+ *                                 256x320, 256x128, 192x128, 64x128 and 128x96
+ *                                 (int8 weights only), 128x128, and 128x128 or
  *                                 64x128 with K split over 2, 3 or 4
  *                                 workgroups, 128x96 over 2, whose exact int32
  *                                 partials are added atomically into y.
@@ -247,7 +247,8 @@ int prism_gemm_w4a8(const int8_t* q, const float* s_a, const uint8_t* w4, const 
 #define PRISM_VARIANT_TILE_128x96 23
 #define PRISM_VARIANT_TILE_128x96_SPLIT2 24
 #define PRISM_VARIANT_SMALL_BALANCED 25
-#define PRISM_VARIANT_COUNT 26
+#define PRISM_VARIANT_TILE_192x128 26
+#define PRISM_VARIANT_COUNT 27
 
 int prism_gemm_w8a8_variant(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w,
                             float* y, int32_t* acc, int64_t M, int64_t N, int64_t K, int variant,

@@ -232,8 +232,8 @@ def _v(variant, **kw):
 for fn in ("prism_gemm_w8a8_variant", "prism_gemm_w4a8_variant"):
     CASES += [
         (fn, _v(-1), INVALID),                 # unknown variant: refused before anything else
-        (fn, _v(26), INVALID),
-        (fn, _v(26, M=0), INVALID),
+        (fn, _v(27), INVALID),
+        (fn, _v(27, M=0), INVALID),
         (fn, _v(0, M=0), OK),
         (fn, _v(3, M=0), OK),
         (fn, _v(0, q=None), INVALID),

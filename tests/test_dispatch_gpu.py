@@ -21,7 +21,7 @@ SMALL = ["small_1x4", "small_1x8", "small_1x16", "small_2x4", "small_2x8", "smal
          "small_4x4", "small_4x8", "small_balanced"]
 TILES8 = ["tile_256x256", "tile_256x192", "tile_256x320", "tile_256x128", "tile_128x128", "tile_128x128_split2",
           "tile_128x128_split3", "tile_128x128_split4", "tile_64x128", "tile_64x128_split2", "tile_64x128_split3",
-          "tile_64x128_split4", "tile_128x96", "tile_128x96_split2"]
+          "tile_64x128_split4", "tile_128x96", "tile_128x96_split2", "tile_192x128"]
 TILES4 = ["tile_128x128", "tile_128x128_split2", "tile_128x128_split3", "tile_128x128_split4"]
 
 
@@ -157,7 +157,7 @@ def test_256_row_tiles_full_size_sampled_rows(M, N, K):
                                      np.random.default_rng(M + N).choice(M, 16, replace=False)]))
     y_ref, acc_ref = oracle.gemm_w8a8(q[rows], s_a[rows], w, s_w)
     qd, sad, wd, swd = dev(q), dev(s_a), dev(w), dev(s_w)
-    for name in ["auto", "tile_256x256", "tile_256x192", "tile_256x320"]:
+    for name in ["auto", "tile_256x256", "tile_256x192", "tile_256x320", "tile_192x128"]:
         acc = torch.full((M, N), 7, dtype=torch.int32, device=DEV)
         y = prism.gemm_w8a8_variant(qd, sad, wd, swd, name, acc=acc)
         torch.cuda.synchronize()

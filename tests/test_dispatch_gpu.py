@@ -184,3 +184,32 @@ def test_few_tile_shapes_full_size_sampled_rows(M, N, K):
         torch.cuda.synchronize()
         assert_same_ints(host(acc)[rows], acc_ref, "acc (%s)" % name)
         assert_same_floats(host(y)[rows], y_ref, "y (%s)" % name)
+
+
+def _random_shapes(seed, count):
+    """Seeded (M, N, K) shapes that reach every branch of the plain call's
+    dispatch: single rows, the small-M kernel (blocked and even shares), its
+    boundary with the tiled path, the few-tile cost model (128 x 128,
+    64 x 128, 128 x 96, K splits) and the tile-shape estimate (192, 256 and
+    320 columns), with ragged M, N and K."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        M = int(rng.choice([1, 2, 5, 16, 17, 31, 32, 33, 48, 64, 65, 96, 129, 200, 257, 383, 512, 700, 1100]))
+        N = int(rng.integers(1, 3200))
+        K = 16 * int(rng.integers(1, 400))
+        out.append((M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", _random_shapes(2024, 24))
+def test_plain_call_random_shapes(M, N, K):
+    """The plain call on seeded random shapes: the oracle's int32 sums and
+    output bits, whatever kernel, tile and split the dispatch picks."""
+    q, s_a, w, s_w = _inputs(M * 7919 + N * 31 + K, M, N, K)
+    y_ref, acc_ref = oracle.gemm_w8a8(q, s_a, w, s_w)
+    acc = torch.full((M, N), 7, dtype=torch.int32, device=DEV)
+    y = prism.gemm_w8a8(dev(q), dev(s_a), dev(w), dev(s_w), acc=acc)
+    torch.cuda.synchronize()
+    assert_same_ints(host(acc), acc_ref, "acc")
+    assert_same_floats(host(y), y_ref, "y")

@@ -213,3 +213,32 @@ def test_plain_call_random_shapes(M, N, K):
     torch.cuda.synchronize()
     assert_same_ints(host(acc), acc_ref, "acc")
     assert_same_floats(host(y), y_ref, "y")
+
+
+@pytest.mark.parametrize("M,N,K", [(M, N, 32 * (K // 32 + 1)) for (M, N, K) in _random_shapes(77, 12)])
+def test_plain_call_random_shapes_w4a8(M, N, K):
+    """The plain W4A8 call on seeded random shapes (small-M kernel with
+    blocked columns or even shares, 4-bit tiled kernel with its K split)."""
+    q, s_a, w4, s_w = _inputs(M * 131 + N * 7 + K, M, N, K, w4=True)
+    y_ref, acc_ref = oracle.gemm_w4a8(q, s_a, w4, s_w)
+    acc = torch.full((M, N), 7, dtype=torch.int32, device=DEV)
+    y = prism.gemm_w4a8(dev(q), dev(s_a), dev(w4), dev(s_w), acc=acc)
+    torch.cuda.synchronize()
+    assert_same_ints(host(acc), acc_ref, "acc")
+    assert_same_floats(host(y), y_ref, "y")
+
+
+@pytest.mark.parametrize("M,N,K", [(M, N, 32 * (K // 32 + 1)) for (M, N, K) in _random_shapes(78, 12)])
+def test_plain_call_random_shapes_blockscale(M, N, K):
+    """The plain block-scale call on seeded random shapes (small-M block
+    kernel up to 16 rows, tiled block kernel above), fp16 scales drawn as
+    in the block-scale workload."""
+    rng = np.random.default_rng(M * 17 + N + K)
+    q = rng.integers(-128, 128, (M, K), dtype=np.int8)
+    s_a = rng.uniform(1e-3, 1e-2, M).astype(np.float32)
+    w = wl.int8_weights(rng, N, K)
+    d = wl.block_scale_bits(rng, N, K // 32)
+    y_ref, _ = oracle.gemm_w8a8_blockscale(q, s_a, w, d)
+    y = prism.gemm_w8a8_blockscale(dev(q), dev(s_a), dev(w), dev(d))
+    torch.cuda.synchronize()
+    assert_same_floats(host(y), y_ref, "y")

@@ -650,7 +650,9 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(const int8_
 // turn the exact int32 sums into the per-channel fp32 epilogue afterwards,
 // in place, one element per thread.
 __global__ __launch_bounds__(256) void zero_kernel(int32_t* __restrict__ p, int64_t n) {
-  // One 16-byte chunk per thread (p is 16-byte aligned); the last chunk may be partial.
+  // One 16-byte chunk per thread; the last chunk may be partial.  p need only
+  // be 4-byte aligned (the C ABI's rule for y): the 16-byte stores are then
+  // dword aligned, which gfx950 global memory accesses allow.
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i + 4 <= n) {
     *reinterpret_cast<v4i*>(p + i) = v4i{0, 0, 0, 0};
@@ -662,8 +664,8 @@ __global__ __launch_bounds__(256) void zero_kernel(int32_t* __restrict__ p, int6
 __global__ __launch_bounds__(256) void finalize_kernel(float* __restrict__ y, int32_t* __restrict__ acc_out,
                                                        const float* __restrict__ s_a, const float* __restrict__ s_w,
                                                        int M, int N) {
-  // Four consecutive elements per thread (16-byte aligned), which may run
-  // across the end of a row.
+  // Four consecutive elements per thread (16-byte accesses, dword aligned at
+  // least), which may run across the end of a row.
   const int64_t total = (int64_t)M * N;
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= total) return;
@@ -694,7 +696,8 @@ __global__ __launch_bounds__(256) void finalize_kernel(float* __restrict__ y, in
   }
 }
 
-// The same epilogue when N % 4 == 0 (every row then starts 16-byte aligned):
+// The same epilogue when N % 4 == 0 (every row then starts at a multiple of
+// 16 bytes from y; y, acc and s_w need only be 4-byte aligned):
 // one workgroup per 1024 columns of one row, so the row index and its scale
 // are uniform over the workgroup and the column scales are one 16-byte load.
 // (At M = 512, N = 2560 on MI355X: 3.5 us against 5.0 for the flat form.)

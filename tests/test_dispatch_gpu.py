@@ -242,3 +242,31 @@ def test_plain_call_random_shapes_blockscale(M, N, K):
     y = prism.gemm_w8a8_blockscale(dev(q), dev(s_a), dev(w), dev(d))
     torch.cuda.synchronize()
     assert_same_floats(host(y), y_ref, "y")
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 2560, 9728), (100, 2052, 9728), (70, 1030, 8192), (512, 2560, 9728),
+                                   (33, 5120, 5120), (300, 1000, 2048)])
+def test_outputs_only_4_byte_aligned(M, N, K):
+    """The C ABI asks y, acc and s_w to be 4-byte aligned only.  Called
+    through the ABI directly with all three one element past a 16-byte
+    boundary, the K-split launches (whose fill and epilogue kernels move 16
+    bytes per access) and the other paths must still give the oracle's
+    bits."""
+    import ctypes
+    q, s_a, w, s_w = _inputs(M + 3 * N + K, M, N, K)
+    y_ref, acc_ref = oracle.gemm_w8a8(q, s_a, w, s_w)
+    qd, sad, wd = dev(q), dev(s_a), dev(w)
+    swb = torch.zeros(N + 1, dtype=torch.float32, device=DEV)
+    swb[1:] = dev(s_w)
+    yb = torch.full((M * N + 1,), 3.0, dtype=torch.float32, device=DEV)
+    ab = torch.full((M * N + 1,), 7, dtype=torch.int32, device=DEV)
+    P = lambda t, off=0: ctypes.c_void_p(t.data_ptr() + 4 * off)
+    assert (swb.data_ptr() + 4) % 16 == 4 and (yb.data_ptr() + 4) % 16 == 4
+    lib = prism.lib()
+    st = ctypes.c_void_p(torch.cuda.current_stream(DEV).cuda_stream)
+    status = lib.prism_gemm_w8a8(P(qd), P(sad), P(wd), P(swb, 1), P(yb, 1), P(ab, 1), M, N, K, st)
+    torch.cuda.synchronize()
+    assert status == 0
+    assert_same_ints(host(ab[1:]).reshape(M, N), acc_ref, "acc")
+    assert_same_floats(host(yb[1:]).reshape(M, N), y_ref, "y")
+    assert host(yb[:1])[0] == 3.0 and host(ab[:1])[0] == 7   # nothing written before y / acc

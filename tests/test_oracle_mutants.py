@@ -61,6 +61,9 @@ MUTANTS = [
      "return (i % 2 == 0) ? (qs[i / 2] & 15) : (qs[i / 2] >> 4);", 1),
     ("q4k: min added", "f = fmaf(-(float)sa, Mn, f);", "f = fmaf((float)sa, Mn, f);", 1),
     ("q4k: min term dropped", "f = fmaf(-(float)sa, Mn, f);", "", 1),
+    ("q4k: min term before the scale term", "f = fmaf((float)p, D, f);\n                    f = fmaf(-(float)sa, Mn, f);",
+     "f = fmaf(-(float)sa, Mn, f);\n                    f = fmaf((float)p, D, f);", 1),
+    ("q4k: min term unfused", "f = fmaf(-(float)sa, Mn, f);", "{ float t = -(float)sa * Mn; f = f + t; }", 1),
     ("q4k: d and dmin swapped", "const float d = oracle_f16_to_f32((uint16_t)(sb[0] | (sb[1] << 8)));",
      "const float d = oracle_f16_to_f32((uint16_t)(sb[2] | (sb[3] << 8)));", 0),
     ("no int32 range check", "if (sum >= INT32_LIMIT || sum < -INT32_LIMIT) {", "if (0) {", 0),
@@ -90,6 +93,8 @@ def _checks():
         pins.test_q4_k_round_trip_with_independent_packer,
         pins.test_q4_k_gemm_within_bound_of_exact_dot_product,
         pins.test_q4_k_gemm_without_mins_is_the_block_scale_gemm,
+        lambda: pins.test_q4_k_gemm_exact_rationals(0),
+        pins.test_q4_k_fold_order_where_orders_differ,
         pins.test_channel_epilogue_exact_rationals,
         pins.test_w4a8_epilogue_exact_rationals,
         pins.test_f16_to_f32_exhaustive_vs_numpy,

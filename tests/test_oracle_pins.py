@@ -444,6 +444,87 @@ def test_q4_k_gemm_within_bound_of_exact_dot_product():
         assert (np.abs(y[m] / s_a[m].astype(np.float64) - exact) <= bound + 1e-30).all(), m
 
 
+def _q4k_replay(codes, d16, dmin16, sc, mn, q, s_a, m, n, order="scale_then_min"):
+    """The fixed fp32 chain of one output, replayed in exact rationals with binary32 rounding
+    after every fused step: per 32-weight sub-block b in ascending k, P = sum code * a and
+    S = sum a (Python integers), D = d * sc and Mn = dmin * m (exact), then
+    f = rn(P D + f) and f = rn(-S Mn + f); finally y = rn(f s_a)."""
+    K = codes.shape[1]
+    f = np.float32(0.0)
+    for b in range(K // 32):
+        t = b // 8
+        P = sum(int(codes[n, k]) * int(q[m, k]) for k in range(32 * b, 32 * b + 32))
+        S = sum(int(q[m, k]) for k in range(32 * b, 32 * b + 32))
+        D = Fraction(float(d16[n, t])) * int(sc[n, b])
+        Mn = Fraction(float(dmin16[n, t])) * int(mn[n, b])
+        if order == "scale_then_min":
+            f = round_f32(Fraction(P) * D + frac(f))
+            f = round_f32(Fraction(-S) * Mn + frac(f))
+        else:   # the other order, used only to find inputs where the two differ
+            f = round_f32(Fraction(-S) * Mn + frac(f))
+            f = round_f32(Fraction(P) * D + frac(f))
+    return round_f32(frac(f) * frac(s_a[m]))
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_q4_k_gemm_exact_rationals(seed):
+    """Every output of the Q4_K GEMM equals the exact-rational replay of its fp32 chain
+    (scale term, then min term, per sub-block, ascending; one rounding per fused step)."""
+    N, K, M = 3, 512, 3
+    codes, d16, dmin16, sc, mn = _q4k_case(150 + seed, N, K)
+    blocks = _pack_q4_k(codes, d16, dmin16, sc, mn)
+    r = _rng(152 + seed)
+    q = r.integers(-127, 128, (M, K), dtype=np.int8)
+    s_a = r.uniform(1e-3, 1.0, M).astype(np.float32)
+    y = oracle.gemm_w4a8_q4k(q, s_a, blocks, N)
+    for m in range(M):
+        for n in range(N):
+            assert bits(y[m, n]) == bits(_q4k_replay(codes, d16, dmin16, sc, mn, q, s_a, m, n)), (m, n)
+
+
+def test_q4_k_fold_order_where_orders_differ():
+    """Hand-built two-sub-block rows where 'scale term, then min term' and the reverse order
+    (or an unfused min term) round to different floats: the oracle must give the first."""
+    r = _rng(160)
+    found = 0
+    for _ in range(4000):
+        codes = np.zeros((1, 256), np.int8)
+        q = np.zeros((1, 256), np.int8)
+        # sub-blocks 0 and 1 carry one nonzero code/activation pair each, plus a few
+        # activations on zero codes so that S differs from the code-weighted sum
+        for b in (0, 1):
+            codes[0, 32 * b] = r.integers(1, 16)
+            q[0, 32 * b] = r.integers(-127, 128)
+            q[0, 32 * b + 1:32 * b + 4] = r.integers(-127, 128, 3)
+        d16 = np.array([[np.float16(r.uniform(0.5, 1.0) * 2.0 ** int(r.integers(-12, -6)))]])
+        dmin16 = np.array([[np.float16(r.uniform(0.5, 1.0) * 2.0 ** int(r.integers(-12, -6)))]])
+        sc = np.zeros((1, 8), np.int64)
+        mn = np.zeros((1, 8), np.int64)
+        sc[0, :2] = r.integers(1, 64, 2)
+        mn[0, :2] = r.integers(1, 64, 2)
+        s_a = np.ones(1, np.float32)
+        want = _q4k_replay(codes, d16, dmin16, sc, mn, q, s_a, 0, 0)
+        other = _q4k_replay(codes, d16, dmin16, sc, mn, q, s_a, 0, 0, order="min_then_scale")
+        # the min term as a rounded product followed by a rounded add
+        f = np.float32(0.0)
+        for b in (0, 1):
+            P = int(codes[0, 32 * b]) * int(q[0, 32 * b])
+            S = sum(int(v) for v in q[0, 32 * b:32 * b + 32])
+            D = Fraction(float(d16[0, 0])) * int(sc[0, b])
+            Mn = Fraction(float(dmin16[0, 0])) * int(mn[0, b])
+            f = round_f32(Fraction(P) * D + frac(f))
+            f = round_f32(frac(round_f32(Fraction(-S) * Mn)) + frac(f))
+        unfused = round_f32(frac(f))
+        if bits(want) == bits(other) and bits(want) == bits(unfused):
+            continue
+        y = oracle.gemm_w4a8_q4k(q, s_a, _pack_q4_k(codes, d16, dmin16, sc, mn), 1)
+        assert bits(y[0, 0]) == bits(want)
+        found += 1
+        if found == 20:
+            break
+    assert found == 20
+
+
 def test_q4_k_gemm_without_mins_is_the_block_scale_gemm():
     """Zero mins and d * sc exact in binary16: the Q4_K path is the pinned block-scale path, bit for bit."""
     N, K, M = 5, 512, 3

@@ -1,20 +1,20 @@
 #!/usr/bin/env python3
 """Benchmark of the exact int8 linear layer on one MI355X.
 
-A step is one pass of the hot path over one batch of the 4B-class projection
-prefill workload (M = 512 tokens, W8A8 with per-channel scales):
-    quantize rows of X_up [512 x 2560]  -> GEMM with W_up   [9728 x 2560]
-    quantize rows of X_dn [512 x 9728]  -> GEMM with W_down [2560 x 9728]
+A step is one pass of the hot path over the largest single-GPU workload, the
+batch-invariance stress batch (W8A8 with per-channel scales):
+    quantize rows of X [8192 x 5120]  -> GEMM with W [5120 x 5120]
+(X holds the 64 seeded probe rows at seeded positions among N(0,1) rows).
 Inputs are synthetic and seeded (exact_int8_gemm_amd.workloads) and resident
 in HBM before timing starts.  R copies of every input set are rotated so that
 the working set exceeds the 256 MB MALL plus L2, so operands come from HBM.
 
 Printed: one JSON line with the whole-step int8 throughput (TOPS), the
-roofline of the dominant kernel (measured with HIP events around its
-launches, in a second pass of the same steps right after the timed one: the
-timed steps carry no events), the CPU oracle's throughput on a bounded
-sample, and per-kernel measurements of the other workloads (W4A8 decode,
-block-scale, batch-invariance stress) under "kernels".
+roofline of the GEMM (measured with HIP events around its launches, in a
+second pass of the same steps right after the timed one: the timed steps
+carry no events), the CPU oracle's throughput on a bounded sample, and
+per-kernel measurements of the other workloads (the M = 512 projection step,
+W4A8 decode and prefill, block-scale, Q4_K, repacks, decode) under "kernels".
 """
 from __future__ import annotations
 
@@ -46,7 +46,7 @@ def _args():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy three times (scale for HBM byte counters)")
     ap.add_argument("--only", default=None, help="run only one kernel measurement (for profiling): "
-                    "step | w4a8 | block | repack | q4k | decode | vendor | stress | sweep (M sweep, not in the default run)")
+                    "step | proj | w4a8 | block | repack | q4k | decode | vendor | stress | sweep (M sweep, not in the default run)")
     return ap.parse_args()
 
 
@@ -156,25 +156,48 @@ def _traffic(kernel_key, src_hash):
     return None
 
 
-# --------------------------------------------------------------------- headline
+# --------------------------------------------------------------------- steps
 
-def headline(torch, prism, wl, args):
+def _gemm_roofline(name, M, N, K, us, traffic_key, src):
+    """Roofline record of one W8A8 per-channel GEMM launch taking `us` microseconds."""
+    ops = 2 * M * N * K
+    nbytes = N * K + 4 * N + M * K + 4 * M + 4 * M * N  # W, s_w, q, s_a, y
+    t = us / 1e6
+    if ops / (PEAK_INT8_TOPS * 1e12) >= nbytes / (PEAK_HBM_GBS * 1e9):
+        rec = dict(bound="mfma", achieved=ops / t / 1e12, peak=PEAK_INT8_TOPS, unit="TOPS")
+    else:
+        rec = dict(bound="hbm", achieved=nbytes / t / 1e9, peak=PEAK_HBM_GBS, unit="GB/s")
+    rec["frac"] = rec["achieved"] / rec["peak"]
+    rec["traffic"] = _traffic(traffic_key, src)
+    rec.update(launch="%s, prism_gemm_w8a8 (M=%d, K=%d, N=%d)" % (name, M, K, N), avg_launch_us=us,
+               ops_per_launch=ops, algorithmic_bytes_per_launch=nbytes, mfma_frac=ops / t / 1e12 / PEAK_INT8_TOPS,
+               hbm_frac=nbytes / t / 1e9 / PEAK_HBM_GBS)
+    return rec
+
+
+def run_steps(torch, prism, cases, steps, warmup):
+    """Times `steps` steps; a step runs, for each case (x, w, s_w), the row quantizer
+    on x and then the W8A8 GEMM of its codes with w.  R copies of every case's
+    buffers are rotated so that the working set exceeds the MALL and L2.
+
+    The timed steps carry no events (a timing event between two kernels costs a
+    few microseconds of its own on this GPU); the per-launch durations come from
+    a second pass of the same steps with HIP events recorded on the launch
+    stream around each quantizer and each GEMM call."""
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     L = Launcher(prism, stream.cuda_stream)
-    up, dn = wl.proj_up(), wl.proj_down()
-    M = up["x"].shape[0]
 
     def T(a):
         return torch.from_numpy(a).to(dev)
 
-    per_set = sum(c["x"].nbytes + c["w"].nbytes + c["x"].shape[0] * (c["x"].shape[1] + 4 * c["w"].shape[0])
-                  for c in (up, dn))
+    per_set = sum(c["x"].nbytes + c["w"].nbytes + c["x"].shape[0] * (c["x"].shape[1] + 4 + 4 * c["w"].shape[0])
+                  for c in cases)
     R = _copies(per_set)
     sets = []
     for _ in range(R):
         s = []
-        for c in (up, dn):
+        for c in cases:
             Mx, K = c["x"].shape
             N = c["w"].shape[0]
             x, w, sw = T(c["x"]), T(c["w"]), T(c["s_w"])
@@ -188,64 +211,75 @@ def headline(torch, prism, wl, args):
     torch.cuda.synchronize()
 
     E = torch.cuda.Event
-    ev = [[(E(enable_timing=True), E(enable_timing=True)) for _ in range(2)] for _ in range(args.steps)]
+    nc = len(cases)
+    ev = [[[E(enable_timing=True) for _ in range(3)] for _ in range(nc)] for _ in range(steps)]
 
     def step(i, record):
         for j, p in enumerate(sets[i % R]):
-            _check(p["quant"]())
             if record is not None:
                 record[j][0].record(stream)
-            _check(p["gemm"]())
+            _check(p["quant"]())
             if record is not None:
                 record[j][1].record(stream)
+            _check(p["gemm"]())
+            if record is not None:
+                record[j][2].record(stream)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i, None)
-    # The timed steps carry no events: a timing event between two kernels
-    # costs a few microseconds of its own on this GPU (about 14 us per step
-    # with four of them).  The per-GEMM durations come from a second pass of
-    # the same steps, with the events.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i, None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    for i in range(args.steps):
+    for i in range(steps):
         step(i, ev[i])
     torch.cuda.synchronize()
+    quant_us = [sum(ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps)) / steps * 1e3 for j in range(nc)]
+    gemm_us = [sum(ev[i][j][1].elapsed_time(ev[i][j][2]) for i in range(steps)) / steps * 1e3 for j in range(nc)]
+    last = sets[(steps - 1) % R]
+    return dict(ms_per_step=wall * 1e3 / steps, R=R, quant_us=quant_us, gemm_us=gemm_us,
+                outputs=[(p["q"], p["sa"], p["y"]) for p in last])
 
-    gemm_us = [sum(ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(args.steps)) / args.steps * 1e3
-               for j in range(2)]
-    ms_step = wall * 1e3 / args.steps
-    ops_per_gemm = 2 * M * 2560 * 9728
+
+def headline(torch, prism, wl, args):
+    """The largest single-GPU workload: the batch-invariance stress batch (M = 8192
+    rows of K = 5120, the 64 probe rows placed among them) quantized per row and
+    multiplied with the 5120 x 5120 int8 weights (per-channel scales)."""
+    st = wl.stress()
+    x, _ = wl.stress_overwrite(st)
+    case = dict(x=x, w=st["w"], s_w=st["s_w"])
+    M, K = x.shape
+    N = st["w"].shape[0]
+    r = run_steps(torch, prism, [case], args.steps, args.warmup)
     src = _src_hash(KERNEL_SOURCES)
-    gemms = []
-    for j, (c, name, key) in enumerate(((up, "up-projection", "proj_up"), (dn, "down-projection", "proj_down"))):
-        K = c["x"].shape[1]
-        N = c["w"].shape[0]
-        nbytes = N * K + 4 * N + M * K + 4 * M + 4 * M * N  # W, s_w, q, s_a, y
-        t = gemm_us[j] / 1e6
-        t_mfma = ops_per_gemm / (PEAK_INT8_TOPS * 1e12)
-        t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
-        if t_mfma >= t_hbm:
-            rec = dict(bound="mfma", achieved=ops_per_gemm / t / 1e12, peak=PEAK_INT8_TOPS, unit="TOPS")
-        else:
-            rec = dict(bound="hbm", achieved=nbytes / t / 1e9, peak=PEAK_HBM_GBS, unit="GB/s")
-        rec["frac"] = rec["achieved"] / rec["peak"]
-        rec["traffic"] = _traffic("gemm_w8a8_" + key, src)
-        rec.update(launch="%s GEMM, prism_gemm_w8a8 (M=%d, K=%d, N=%d)" % (name, M, K, N),
-                   avg_launch_us=gemm_us[j], ops_per_launch=ops_per_gemm, algorithmic_bytes_per_launch=nbytes,
-                   mfma_frac=ops_per_gemm / t / 1e12 / PEAK_INT8_TOPS, hbm_frac=nbytes / t / 1e9 / PEAK_HBM_GBS)
-        gemms.append(rec)
-    dominant = max(range(2), key=lambda j: gemm_us[j])
-    roof = dict(gemms[dominant])
+    roof = _gemm_roofline("stress GEMM", M, N, K, r["gemm_us"][0], "gemm_w8a8_stress_m8192", src)
     roof["timing"] = "HIP events on the launch stream around each GEMM call, over a second pass of the timed steps"
-    roof["other_gemm"] = gemms[1 - dominant]
-    last = sets[(args.steps - 1) % R]
-    return dict(
-        value=2 * ops_per_gemm / (ms_step / 1e3) / 1e12, ms_per_step=ms_step, R=R, M=M, roofline=roof,
-        outputs=[(p["q"], p["sa"], p["y"]) for p in last], inputs=(up, dn))
+    qus = r["quant_us"][0]
+    qbytes = 5 * M * K + 4 * M
+    roof["quantizer"] = dict(launch="prism_quantize_rows (M=%d, K=%d)" % (M, K), avg_launch_us=qus,
+                             bound="hbm", achieved=qbytes / qus / 1e3, peak=PEAK_HBM_GBS, unit="GB/s",
+                             frac=qbytes / qus / 1e3 / PEAK_HBM_GBS, algorithmic_bytes_per_launch=qbytes)
+    ops = 2 * M * N * K
+    return dict(value=ops / (r["ms_per_step"] / 1e3) / 1e12, ms_per_step=r["ms_per_step"], R=r["R"], M=M, N=N, K=K,
+                roofline=roof, outputs=r["outputs"], case=case)
+
+
+def proj_step(torch, prism, wl, steps=100, warmup=10):
+    """The 4B-class projection prefill step (M = 512): quantize + GEMM for the
+    up-projection (K = 2560, N = 9728) and the down-projection (K = 9728, N = 2560)."""
+    up, dn = wl.proj_up(), wl.proj_down()
+    M = up["x"].shape[0]
+    r = run_steps(torch, prism, [up, dn], steps, warmup)
+    src = _src_hash(KERNEL_SOURCES)
+    gemms = [_gemm_roofline("%s GEMM" % name, M, c["w"].shape[0], c["x"].shape[1], r["gemm_us"][j], "gemm_w8a8_" + key,
+                            src)
+             for j, (c, name, key) in enumerate(((up, "up-projection", "proj_up"), (dn, "down-projection",
+                                                                                     "proj_down")))]
+    ops = 2 * (2 * M * 2560 * 9728)
+    return dict(tops=ops / (r["ms_per_step"] / 1e3) / 1e12, ms_per_step=r["ms_per_step"], us=r["ms_per_step"] * 1e3,
+                quantize_us=r["quant_us"], copies=r["R"], gemms=gemms)
 
 
 # --------------------------------------------------------------- other kernels
@@ -460,6 +494,8 @@ def kernels(torch, prism, wl, only=None):
                 rec.update(vendor_int_mm_error=str(e)[:80])
             out["sweep_w8a8_5120x5120_m%d" % M] = rec
         del wts
+    if only in (None, "proj"):
+        out["step_proj_m512"] = proj_step(torch, prism, wl)
     if only in (None, "stress"):
         st = wl.stress()
         R = _copies(st["w"].nbytes)
@@ -467,6 +503,8 @@ def kernels(torch, prism, wl, only=None):
         sw = T(st["s_w"])
         K = N = 5120
         x_over, _ = wl.stress_overwrite(st)
+        # M = 8192 is also the headline step; here its GEMM is timed on its own
+        # (launches back to back, weights rotated), next to the static quantizer
         for M, xa in ((8192, x_over), (1, st["x_probe"][:1].copy())):
             x = T(xa)
             q = torch.empty((M, K), dtype=torch.int8, device=dev)
@@ -489,33 +527,33 @@ def kernels(torch, prism, wl, only=None):
 
 # ------------------------------------------------------------------ CPU oracle
 
-def cpu_baseline(np, oracle, up, dn, gpu_outputs, budget_s=10.0):
-    """The oracle, as it stands, on the host cores: the same step (quantize + GEMM,
-    up and down); full steps repeated until the budget is spent, or a row subset
-    if one full step would take far longer than the budget."""
-    M = up["x"].shape[0]
+def cpu_baseline(np, oracle, case, gpu_out, budget_s=12.0):
+    """The oracle, as it stands, on the host cores, on the headline step's work
+    (quantize rows + W8A8 GEMM): full steps repeated until the budget is spent,
+    or the first rows of one step if a full step would take far longer.  The
+    sampled rows are compared bit for bit with the GPU's outputs."""
+    x, w, s_w = case["x"], case["w"], case["s_w"]
+    M, K = x.shape
+    N = w.shape[0]
     t0 = time.perf_counter()
-    oracle.gemm_w8a8(*oracle.quantize_rows(up["x"][:8]), up["w"], up["s_w"])
-    oracle.gemm_w8a8(*oracle.quantize_rows(dn["x"][:8]), dn["w"], dn["s_w"])
-    est_full = (time.perf_counter() - t0) * M / 8
-    rows = M if est_full <= 3 * budget_s else max(8, int(M * budget_s / est_full) // 8 * 8)
-    done, reps, outs = 0.0, 0, None
+    oracle.gemm_w8a8(*oracle.quantize_rows(x[:64]), w, s_w)
+    est_full = (time.perf_counter() - t0) * M / 64
+    rows = M if est_full <= 2 * budget_s else max(64, int(M * budget_s / est_full) // 64 * 64)
+    reps, out = 0, None
     t0 = time.perf_counter()
     while reps == 0 or (time.perf_counter() - t0 < budget_s and rows == M):
-        outs = []
-        for c in (up, dn):
-            q, s = oracle.quantize_rows(c["x"][:rows])
-            y, _ = oracle.gemm_w8a8(q, s, c["w"], c["s_w"])
-            outs.append((q, s, y))
+        q, s = oracle.quantize_rows(x[:rows])
+        y, _ = oracle.gemm_w8a8(q, s, w, s_w)
+        out = (q, s, y)
         reps += 1
     dt = time.perf_counter() - t0
-    ops = reps * 2 * (2 * rows * 2560 * 9728)
-    exact = True
-    for (q, s, y), (gq, gs, gy) in zip(outs, gpu_outputs):
-        exact &= bool(np.array_equal(gq[:rows], q) and np.array_equal(gs[:rows].view(np.uint32), s.view(np.uint32))
-                      and np.array_equal(gy[:rows].view(np.uint32), y.view(np.uint32)))
-    sample = ("%d full step(s) (quantize + GEMM, up and down, M=%d)" % (reps, M) if rows == M else
-              "rows 0..%d of one step (quantize + GEMM, up and down)" % (rows - 1))
+    ops = reps * 2 * rows * N * K
+    gq, gs, gy = gpu_out
+    q, s, y = out
+    exact = bool(np.array_equal(gq[:rows], q) and np.array_equal(gs[:rows].view(np.uint32), s.view(np.uint32))
+                 and np.array_equal(gy[:rows].view(np.uint32), y.view(np.uint32)))
+    sample = ("%d full step(s) (quantize + GEMM, M=%d, K=%d, N=%d)" % (reps, M, K, N) if rows == M else
+              "rows 0..%d of one step (quantize + GEMM, K=%d, N=%d)" % (rows - 1, K, N))
     return dict(value=ops / dt / 1e12, unit="TOPS", cores=oracle.max_threads(), kind="oracle", sample=sample,
                 seconds=dt, cpu=_cpu_model(), nproc=os.cpu_count(), compiler="gcc " + " ".join(oracle.CFLAGS)), exact
 
@@ -555,23 +593,35 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     h = headline(torch, prism, wl, args)
+    print("headline step done: %.1f us per step" % (h["ms_per_step"] * 1e3), file=sys.stderr, flush=True)
     rec = {
         "metric": METRIC, "value": h["value"], "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": h["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int8", "data": "synthetic",
-        "config": {"workload": "4B-class projection prefill, W8A8 per-channel: quantize rows + GEMM for "
-                               "up (M=512, K=2560, N=9728) and down (M=512, K=9728, N=2560)",
-                   "M": h["M"], "rotated_input_copies": h["R"], "parallelism": "single GPU"},
+        "config": {"workload": "batch-invariance stress batch, W8A8 per-channel: quantize rows of X [8192 x 5120] "
+                               "(64 probe rows among N(0,1) rows) + GEMM with W [5120 x 5120]",
+                   "M": h["M"], "K": h["K"], "N": h["N"], "rotated_input_copies": h["R"],
+                   "parallelism": "single GPU"},
         "roofline": h["roofline"],
     }
     if args.only is None and not args.no_cpu:
         import oracle
-        outs = [(o[0].cpu().numpy(), o[1].cpu().numpy(), o[2].cpu().numpy()) for o in h["outputs"]]
-        cb, exact = cpu_baseline(np, oracle, h["inputs"][0], h["inputs"][1], outs)
+        o = h["outputs"][0]
+        cb, exact = cpu_baseline(np, oracle, h["case"], (o[0].cpu().numpy(), o[1].cpu().numpy(), o[2].cpu().numpy()))
         rec["cpu_baseline"] = cb
         rec["bit_exact_vs_oracle"] = exact
+        print("cpu baseline done", file=sys.stderr, flush=True)
     if args.only is None and not args.no_kernels:
-        rec["kernels"] = kernels(torch, prism, wl)
+        k = kernels(torch, prism, wl)
+        rec["kernels"] = k
+        # the two regimes of the measurement targets, side by side
+        small = {n: k[n]["hbm_frac"] for n in ("w4a8_m1", "w4a8_m4", "w4a8_m16", "stress_m1", "decode_m1_proj_up",
+                                               "decode_m1_proj_down", "block_scale_m1", "q4k_m1") if n in k}
+        rec["targets"] = {"m_ge_2048_mfma_frac": {"stress_m8192 (headline GEMM)": h["roofline"]["frac"],
+                                                  "block_scale_m2048": k.get("block_scale_m2048", {}).get("mfma_frac"),
+                                                  "w4a8_m2048": k.get("w4a8_m2048", {}).get("mfma_frac"),
+                                                  "q4k_m2048": k.get("q4k_m2048", {}).get("mfma_frac")},
+                          "m_le_16_hbm_frac": small}
     print(json.dumps(rec))
 
 

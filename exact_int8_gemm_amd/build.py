@@ -13,6 +13,7 @@ Flags that define results, not only speed:
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -43,20 +44,40 @@ def sources():
     return [os.path.join(CSRC, s) for s in SOURCES]
 
 
-def _compile_cmd(src, obj):
+def source_hash() -> str:
+    """sha256 (hex, 32 digits) of every file under csrc/, of include/prism.h and of
+    the compile flags.  It is compiled into the library (prism_build_id), so a
+    binary can be matched against the sources it is meant to come from."""
+    h = hashlib.sha256()
+    files = sorted(os.listdir(CSRC))
+    for name in files:
+        path = os.path.join(CSRC, name)
+        if os.path.isfile(path):
+            h.update(name.encode() + b"\0")
+            with open(path, "rb") as f:
+                h.update(f.read())
+    with open(os.path.join(ROOT, "include", "prism.h"), "rb") as f:
+        h.update(b"prism.h\0" + f.read())
+    h.update(" ".join(COMMON + DEVICE).encode())
+    return h.hexdigest()[:32]
+
+
+def _compile_cmd(src, obj, build_id="0" * 32):
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    return [HIPCC, *lang, *COMMON, *DEVICE, "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
+    return [HIPCC, *lang, *COMMON, *DEVICE, "-I", os.path.join(ROOT, "include"),
+            '-DPRISM_BUILD_ID="%s"' % build_id, "-c", src, "-o", obj]
 
 
 def build_library(verbose: bool = False) -> str:
     """Compile every HIP source for gfx950 and link libprism.so; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
+    build_id = source_hash()
     procs = []
     objs = []
     for src in sources():
         obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
         objs.append(obj)
-        cmd = _compile_cmd(src, obj)
+        cmd = _compile_cmd(src, obj, build_id)
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

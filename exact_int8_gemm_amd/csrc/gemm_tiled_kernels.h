@@ -398,7 +398,8 @@ __device__ inline v4i rsrc_words(const void* base, int64_t bytes) {
 // 16 * lane.  Written as inline assembly so that the compiler does not add
 // its own (conservative) waits for it: every copy is awaited explicitly with
 // wait_vmcnt before its data is read, and all are drained before the kernel
-// leaves the main loop.  No compiler-generated code in these kernels uses M0.
+// leaves the main loop.  M0 is listed as clobbered, so the compiler keeps no
+// value of its own in M0 across a copy.
 __device__ inline void copy_to_lds(const v4i rsrc, uint32_t lds_addr, uint32_t voff) {
   // lds_addr and rsrc are wave-uniform; readfirstlane puts them in SGPRs.
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
@@ -407,7 +408,7 @@ __device__ inline void copy_to_lds(const v4i rsrc, uint32_t lds_addr, uint32_t v
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(m0v), "v"(voff), "s"(r)
-               : "memory");
+               : "memory", "m0");
 }
 
 // The same for 2-byte elements: lane i's value lands zero-extended in the
@@ -419,7 +420,7 @@ __device__ inline void copy2_to_lds(const v4i rsrc, uint32_t lds_addr, uint32_t 
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ushort %1, %2, 0 offen lds"
                :
                : "s"(m0v), "v"(voff), "s"(r)
-               : "memory");
+               : "memory", "m0");
 }
 
 // The same for 4-byte elements: lane i's dword lands at lds_addr + 4 * lane.
@@ -430,7 +431,7 @@ __device__ inline void copy4_to_lds(const v4i rsrc, uint32_t lds_addr, uint32_t 
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :
                : "s"(m0v), "v"(voff), "s"(r)
-               : "memory");
+               : "memory", "m0");
 }
 
 // s_waitcnt with vmcnt <= n and no wait on the other counters (gfx9 encoding).

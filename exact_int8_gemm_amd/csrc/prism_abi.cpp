@@ -15,6 +15,10 @@
 #include "../../include/prism.h"
 #include "prism_internal.h"
 
+#ifndef PRISM_BUILD_ID
+#error "PRISM_BUILD_ID (the source hash written by build.py) must be defined"
+#endif
+
 namespace prism {
 
 int launch_status() { return hipGetLastError() == hipSuccess ? PRISM_OK : PRISM_ERR_LAUNCH; }
@@ -26,7 +30,10 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
+// Also clears an error that an earlier, unrelated HIP call left on this thread,
+// so that launch_status() after this call's launches reports those launches only.
 int check_device() {
+  (void)hipGetLastError();
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return PRISM_ERR_UNSUPPORTED;
   if (dev < kMaxDevices) {
@@ -112,6 +119,8 @@ int run_variant(const int8_t* q, const float* s_a, const void* w, bool w4, const
 extern "C" {
 
 int prism_abi_version(void) { return PRISM_ABI_VERSION; }
+
+const char* prism_build_id(void) { return PRISM_BUILD_ID; }
 
 const char* prism_status_string(int status) {
   switch (status) {

@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libprism.so")
 
 PRISM_OK = 0
-ABI_VERSION = 9
+ABI_VERSION = 10
 K_MAX = 131040
 
 # Dispatch-table entries of the W8A8 / W4A8 calls (PRISM_VARIANT_* in include/prism.h).
@@ -44,6 +44,8 @@ def _declare(lib):
     p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.prism_abi_version.restype = i32
     lib.prism_abi_version.argtypes = []
+    lib.prism_build_id.restype = ctypes.c_char_p
+    lib.prism_build_id.argtypes = []
     lib.prism_status_string.restype = ctypes.c_char_p
     lib.prism_status_string.argtypes = [i32]
     lib.prism_quantize_rows.restype = i32
@@ -70,16 +72,25 @@ def _declare(lib):
 
 
 def lib():
-    """The loaded ``libprism.so`` (built with hipcc first if it does not exist yet)."""
+    """The loaded ``libprism.so`` (built with hipcc first if it does not exist yet).
+
+    Raises if the library was built from other sources than the ones next to
+    this binding (its build id is the hash of the HIP sources, the header and
+    the compile flags), so that a stale binary is never the one under test."""
     global _lib
     if _lib is None:
+        from . import build
         if not os.path.exists(LIB_PATH):
-            from . import build
             build.build_library()
-        _lib = _declare(ctypes.CDLL(LIB_PATH))
-        v = _lib.prism_abi_version()
+        loaded = _declare(ctypes.CDLL(LIB_PATH))
+        v = loaded.prism_abi_version()
         if v != ABI_VERSION:
             raise RuntimeError("libprism ABI version %d, binding expects %d: rebuild" % (v, ABI_VERSION))
+        got, want = loaded.prism_build_id().decode(), build.source_hash()
+        if got != want:
+            raise RuntimeError("%s was built from other sources (build id %s, sources hash to %s): rebuild it "
+                               "with exact_int8_gemm_amd.build.build_library()" % (LIB_PATH, got, want))
+        _lib = loaded
     return _lib
 
 

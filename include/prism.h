@@ -41,7 +41,7 @@ extern "C" {
 #endif
 
 /* Bumped on any change of a signature or of the semantics below. */
-#define PRISM_ABI_VERSION 9
+#define PRISM_ABI_VERSION 10
 
 /* Largest accepted K.  For K <= 131040 every exact sum of K products of two
  * int8 values (|q|, |w| <= 128) lies strictly inside the int32 range. */
@@ -56,6 +56,12 @@ extern "C" {
 
 /* Returns PRISM_ABI_VERSION of the built library. */
 int prism_abi_version(void);
+
+/* Identity of the sources the library was built from: 32 hex digits of the
+ * sha256 of its HIP/C++ sources, this header and its compile flags (static
+ * string, never NULL).  A binding can compare it with the sources it ships
+ * with and refuse a library built from others. */
+const char* prism_build_id(void);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* prism_status_string(int status);

@@ -3,7 +3,8 @@ invalid calls before any HIP call (runs without a GPU).
 
 The validation calls pass fake pointers, so they run in a child process in
 which no HIP device is visible: even a validation bug could then never reach
-a kernel launch.
+a kernel launch.  The child asks the HIP runtime for its device count first
+and makes no call at all if it sees a device.
 """
 import json
 import os
@@ -44,7 +45,7 @@ def test_header_declares_every_call():
     assert {"prism_quantize_rows", "prism_quantize_rows_static", "prism_repack_q8_0", "prism_gemm_w8a8",
             "prism_gemm_w8a8_blockscale", "prism_gemm_w4a8", "prism_gemm_w8a8_variant", "prism_gemm_w4a8_variant",
             "prism_repack_q4_k", "prism_gemm_w4a8_q4k", "prism_quantize_gemm_w8a8",
-            "prism_abi_version", "prism_status_string"} <= names
+            "prism_abi_version", "prism_build_id", "prism_status_string"} <= names
 
 
 def test_library_exports_every_declared_symbol(built):
@@ -68,6 +69,14 @@ def test_binding_constants_match_header():
 _CHILD = r"""
 import ctypes, json, sys
 lib = ctypes.CDLL(sys.argv[1])
+# The calls below pass fake device addresses.  Refuse to make any of them if the
+# HIP runtime that libprism loaded can see a device (the parent hides devices
+# through the environment; this checks that the hiding took effect).
+hip = ctypes.CDLL("libamdhip64.so.7")
+count = ctypes.c_int(0)
+if hip.hipGetDeviceCount(ctypes.byref(count)) == 0 and count.value > 0:
+    print(json.dumps({"device_visible": count.value}))
+    sys.exit(0)
 p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 lib.prism_abi_version.restype = i32
 lib.prism_status_string.restype = ctypes.c_char_p
@@ -282,7 +291,10 @@ def child_results(built):
     out = subprocess.run([sys.executable, "-c", _CHILD, built, payload], env=env, capture_output=True, text=True,
                          timeout=120)
     assert out.returncode == 0, out.stderr
-    return json.loads(out.stdout.strip().splitlines()[-1])
+    res = json.loads(out.stdout.strip().splitlines()[-1])
+    if "device_visible" in res:
+        pytest.skip("a HIP device is visible despite HIP_VISIBLE_DEVICES=-1: fake-pointer calls not made")
+    return res
 
 
 def test_abi_version(child_results):
@@ -314,7 +326,28 @@ def test_valid_call_without_a_device_is_unsupported(built):
     out = subprocess.run([sys.executable, "-c", _CHILD, built, payload], env=env, capture_output=True, text=True,
                          timeout=120)
     assert out.returncode == 0, out.stderr
-    assert json.loads(out.stdout.strip().splitlines()[-1])["status"] == [UNSUP] * 7
+    res = json.loads(out.stdout.strip().splitlines()[-1])
+    if "device_visible" in res:
+        pytest.skip("a HIP device is visible despite HIP_VISIBLE_DEVICES=-1: fake-pointer calls not made")
+    assert res["status"] == [UNSUP] * 7
+
+
+def test_library_build_id_matches_sources(built):
+    sys.path.insert(0, ROOT)
+    from exact_int8_gemm_amd import build, prism
+    prism._lib = None
+    assert prism.lib().prism_build_id().decode() == build.source_hash()
+
+
+def test_library_from_other_sources_is_refused(built, monkeypatch):
+    """A library whose build id differs from the hash of the sources beside it is not loaded."""
+    sys.path.insert(0, ROOT)
+    from exact_int8_gemm_amd import build, prism
+    monkeypatch.setattr(build, "source_hash", lambda: "f" * 32)
+    monkeypatch.setattr(prism, "_lib", None)
+    with pytest.raises(RuntimeError, match="built from other sources"):
+        prism.lib()
+    assert prism._lib is None
 
 
 def test_build_uses_result_defining_flags():

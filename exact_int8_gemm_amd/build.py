@@ -29,7 +29,7 @@ SOURCES = ["quantize.hip", "gemm_small.hip", "gemm_tiled.hip", "repack.hip", "pr
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = [
-    "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", "-Werror=inline-asm",
     "-ffp-contract=off", "-fno-fast-math",
 ]
 DEVICE = [

@@ -2,10 +2,34 @@
 // tile shape is a function of (M, N, K) only.  Every choice computes the same
 // exact int32 sums and the same per-element epilogue, so the choice never
 // changes a result bit.
+#include <atomic>
+
 #include "gemm_pingpong.h"
 #include "../../include/prism.h"
 
 namespace prism {
+namespace tiled {
+namespace dma {
+
+int device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (dev < 0 || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;  // MI355X
+  if (dev >= 0 && dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+}  // namespace dma
+}  // namespace tiled
+
 namespace {
 
 using tiled::launch_tiled;
@@ -83,8 +107,9 @@ SplitChoice split_for(int64_t M, int64_t N, int K) {
 // round or save one, e.g. M = 512, N = 9728, K = 2560: 28.2 -> 25.6 us):
 //  * 256 x 192 / 256 / 320 tiles: 8 waves of 64 x (tile width / 2) in two
 //    groups that alternate between MFMAs and LDS reads (gemm_pingpong.h),
-//    128-byte stages, 2-deep ring; the 320-wide tiles read one 32-k step of
-//    fragments per phase (their accumulators take 160 registers);
+//    128-byte stages, 2-deep ring, one persistent workgroup per CU; the
+//    320-wide tiles read one 32-k step of fragments per phase (their
+//    accumulators take 160 registers);
 //  * 192 x 128 tiles: 8 waves of 96 x 32, 3-deep ring;
 //  * 256 x 128 tiles: 16 waves of 64 x 32, 3-deep ring (16 waves instead of
 //    8: 5-15% faster, e.g. M = 512, N = 9728, K = 2560: 30.6 -> 27.9 us);
@@ -108,9 +133,9 @@ void pick_int8(const int8_t* q, const float* s_a, const int8_t* w, const float* 
   for (int i = 1; i < 6; ++i)
     if (cost[i] < cost[best]) best = i;
   switch (best) {
-    case 0: tiled::dma::launch_pp<128, 2>(q, s_a, w, s_w, y, acc, M, N, K, st); break;
-    case 1: tiled::dma::launch_pp<128, 2, 320, 1>(q, s_a, w, s_w, y, acc, M, N, K, st); break;
-    case 2: tiled::dma::launch_pp<128, 2, 192>(q, s_a, w, s_w, y, acc, M, N, K, st); break;
+    case 0: tiled::dma::launch_pp<128>(q, s_a, w, s_w, y, acc, M, N, K, st); break;
+    case 1: tiled::dma::launch_pp<128, 320, 1>(q, s_a, w, s_w, y, acc, M, N, K, st); break;
+    case 2: tiled::dma::launch_pp<128, 192>(q, s_a, w, s_w, y, acc, M, N, K, st); break;
     case 3: tiled::dma::launch<256, 128, 128, 4, 4, 3, 1>(q, s_a, w, s_w, y, acc, M, N, K, st); break;
     case 5: tiled::dma::launch<192, 128, 128, 2, 4, 3, 1>(q, s_a, w, s_w, y, acc, M, N, K, st); break;
     default: {
@@ -151,11 +176,11 @@ int launch_gemm_tiled_variant(const int8_t* q, const float* s_a, const void* w, 
     return launch_status();
   }
   if (variant == 7) {
-    tiled::dma::launch_pp<128, 2>(q, s_a, wb, s_w, y, acc, M, N, K, st);
+    tiled::dma::launch_pp<128>(q, s_a, wb, s_w, y, acc, M, N, K, st);
   } else if (variant == 17) {
-    tiled::dma::launch_pp<128, 2, 192>(q, s_a, wb, s_w, y, acc, M, N, K, st);
+    tiled::dma::launch_pp<128, 192>(q, s_a, wb, s_w, y, acc, M, N, K, st);
   } else if (variant == 18) {
-    tiled::dma::launch_pp<128, 2, 320, 1>(q, s_a, wb, s_w, y, acc, M, N, K, st);
+    tiled::dma::launch_pp<128, 320, 1>(q, s_a, wb, s_w, y, acc, M, N, K, st);
   } else if (variant == 8) {
     tiled::dma::launch<256, 128, 128, 4, 4, 3, 1>(q, s_a, wb, s_w, y, acc, M, N, K, st);
   } else if (variant >= 9 && variant <= 12) {

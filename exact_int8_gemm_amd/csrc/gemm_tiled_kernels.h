@@ -398,17 +398,20 @@ __device__ inline v4i rsrc_words(const void* base, int64_t bytes) {
 // 16 * lane.  Written as inline assembly so that the compiler does not add
 // its own (conservative) waits for it: every copy is awaited explicitly with
 // wait_vmcnt before its data is read, and all are drained before the kernel
-// leaves the main loop.  M0 is listed as clobbered, so the compiler keeps no
-// value of its own in M0 across a copy.
+// leaves the main loop.  M0 (the LDS address of the copy) is written inside
+// the same statement, right before the copy, and is declared as an output of
+// the statement, so the compiler knows M0 is overwritten.  The compiler does
+// not see that the statement holds an LDS DMA, so it must not be the one to
+// place the M0 write: with M0 given as an input operand it put the next
+// copy's M0 write directly behind a copy in flight, and the GPU faulted.
 __device__ inline void copy_to_lds(const v4i rsrc, uint32_t lds_addr, uint32_t voff) {
   // lds_addr and rsrc are wave-uniform; readfirstlane puts them in SGPRs.
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
   const v4i r = v4i{__builtin_amdgcn_readfirstlane(rsrc[0]), __builtin_amdgcn_readfirstlane(rsrc[1]),
                     __builtin_amdgcn_readfirstlane(rsrc[2]), __builtin_amdgcn_readfirstlane(rsrc[3])};
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(m0v), "v"(voff), "s"(r)
-               : "memory", "m0");
+  uint32_t m0_out;
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds" : "={m0}"(m0_out) : "s"(m0v), "v"(voff), "s"(r) : "memory");
+  (void)m0_out;
 }
 
 // The same for 2-byte elements: lane i's value lands zero-extended in the
@@ -417,10 +420,9 @@ __device__ inline void copy2_to_lds(const v4i rsrc, uint32_t lds_addr, uint32_t 
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
   const v4i r = v4i{__builtin_amdgcn_readfirstlane(rsrc[0]), __builtin_amdgcn_readfirstlane(rsrc[1]),
                     __builtin_amdgcn_readfirstlane(rsrc[2]), __builtin_amdgcn_readfirstlane(rsrc[3])};
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_ushort %1, %2, 0 offen lds"
-               :
-               : "s"(m0v), "v"(voff), "s"(r)
-               : "memory", "m0");
+  uint32_t m0_out;
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_ushort %2, %3, 0 offen lds" : "={m0}"(m0_out) : "s"(m0v), "v"(voff), "s"(r) : "memory");
+  (void)m0_out;
 }
 
 // The same for 4-byte elements: lane i's dword lands at lds_addr + 4 * lane.
@@ -428,10 +430,9 @@ __device__ inline void copy4_to_lds(const v4i rsrc, uint32_t lds_addr, uint32_t 
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
   const v4i r = v4i{__builtin_amdgcn_readfirstlane(rsrc[0]), __builtin_amdgcn_readfirstlane(rsrc[1]),
                     __builtin_amdgcn_readfirstlane(rsrc[2]), __builtin_amdgcn_readfirstlane(rsrc[3])};
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :
-               : "s"(m0v), "v"(voff), "s"(r)
-               : "memory", "m0");
+  uint32_t m0_out;
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dword %2, %3, 0 offen lds" : "={m0}"(m0_out) : "s"(m0v), "v"(voff), "s"(r) : "memory");
+  (void)m0_out;
 }
 
 // s_waitcnt with vmcnt <= n and no wait on the other counters (gfx9 encoding).

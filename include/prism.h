@@ -28,8 +28,9 @@
  *     negative status, enqueues nothing and writes nothing.
  *   - Results are a pure function of the inputs: they do not depend on M,
  *     on a row's position in the batch, on the stream or on concurrency.
- *     Calls hold no global state except a per-device cache of the device's
- *     architecture, and may be made from several threads at once.
+ *     Calls hold no global state except per-device caches of the device's
+ *     architecture and compute-unit count, and may be made from several
+ *     threads at once.
  */
 #ifndef PRISM_H
 #define PRISM_H

@@ -526,11 +526,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(const float* __restrict__ x, 
     finite = (red_fin[0] & red_fin[1] & red_fin[2] & red_fin[3]) != 0;
     sa = quant::row_scale(amax, finite);
     const bool zero = !finite || sa == 0.0f;
+    const float rc = zero ? 0.0f : quant::fast_recip(sa);
 #pragma unroll
     for (int j = 0; j < PL; ++j) {
       const int f = threadIdx.x + 256 * j;
       if (f < nf4) {
-        const uint32_t c = zero ? 0u : quant::pack4(v[j], sa);
+        const uint32_t c = zero ? 0u : quant::pack4(v[j], sa, rc);
         codes[f] = c;
         if (blockIdx.x == 0) reinterpret_cast<uint32_t*>(q_out)[f] = c;
       }

@@ -1,6 +1,9 @@
 // Element arithmetic of the per-row int8 quantizer, shared by the quantizer
 // kernels and the fused single-row GEMM (both must give the same codes).
 //   s = amax / 127;  q = clamp(rint(x / s), -127, 127)
+// where x / s is the correctly rounded quotient (code_of); code_fast gets the
+// same code from a multiplication by 1/s in all but the rare elements next to
+// a rounding tie.
 // IEEE fp32, round to nearest even, no flushing; the division is the
 // correctly rounded one (the library is built with correctly rounded fp32
 // division).
@@ -23,13 +26,44 @@ __device__ inline int code_of(float x, float s) {
   return (int)r;
 }
 
-// Four codes packed little-endian into one dword.
-__device__ inline uint32_t pack4(const float4 v, float s) {
-  uint32_t b0 = (uint32_t)(code_of(v.x, s) & 0xff);
-  uint32_t b1 = (uint32_t)(code_of(v.y, s) & 0xff);
-  uint32_t b2 = (uint32_t)(code_of(v.z, s) & 0xff);
-  uint32_t b3 = (uint32_t)(code_of(v.w, s) & 0xff);
-  return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+// The same code from r = 1/s (correctly rounded) without the division, for
+// a scale s in [2^-126, 2^126] (r is then a normal float).  t = x * r differs
+// from x / s by at most 2^-16 when |x / s| <= 128, and the correctly rounded
+// quotient q = fl(x / s) differs from x / s by at most 2^-17, so |t - q| <
+// 2^-15.  If t is farther than that from every half-integer, t and q lie
+// strictly on the same side of each one and rint(t) == rint(q); the distance
+// |t - rint(t)| is computed exactly (t and rint(t) are multiples of t's ulp).
+// Otherwise (a rounding tie may be near) the quotient is computed exactly.
+// For |x / s| > 128 both t and q exceed 127.5 in magnitude and clamp to the
+// same code.  An infinite x (static scales only) gives a NaN distance and
+// takes the exact path.
+__device__ inline int code_fast(float x, float s, float r) {
+  const float t = x * r;
+  const float n = rintf(t);
+  if (!(fabsf(t - n) < 0.5f - 0x1p-15f)) return code_of(x, s);
+  return (int)fminf(fmaxf(n, -127.0f), 127.0f);
+}
+
+// 1/s for code_fast, or 0 when s is outside [2^-126, 2^126] (then every
+// code takes the division).
+__device__ inline float fast_recip(float s) { return (s >= 0x1p-126f && s <= 0x1p126f) ? 1.0f / s : 0.0f; }
+
+// Four codes packed little-endian into one dword; r = fast_recip(s).
+__device__ inline uint32_t pack4(const float4 v, float s, float r) {
+  int c0, c1, c2, c3;
+  if (r != 0.0f) {
+    c0 = code_fast(v.x, s, r);
+    c1 = code_fast(v.y, s, r);
+    c2 = code_fast(v.z, s, r);
+    c3 = code_fast(v.w, s, r);
+  } else {
+    c0 = code_of(v.x, s);
+    c1 = code_of(v.y, s);
+    c2 = code_of(v.z, s);
+    c3 = code_of(v.w, s);
+  }
+  return (uint32_t)(c0 & 0xff) | ((uint32_t)(c1 & 0xff) << 8) | ((uint32_t)(c2 & 0xff) << 16) |
+         ((uint32_t)(c3 & 0xff) << 24);
 }
 
 __device__ inline bool finite4(const float4 v) {

@@ -12,8 +12,8 @@
 // Arithmetic per row (IEEE fp32, round to nearest even, no flushing):
 //   s = amax / 127;  q = clamp(rint(x / s), -127, 127)
 // with a NaN scale and zero codes for a row holding a non-finite value, and
-// zero codes when s == 0.  The division is the correctly rounded one (the
-// library is built with correctly rounded fp32 division).
+// zero codes when s == 0.  x / s is the correctly rounded quotient; the codes
+// come from a multiplication by 1/s except next to rounding ties (quant_math.h).
 //
 // Static form (the README's ranges measured once, ahead of time): one
 // caller-given s > 0 for the whole tensor replaces amax / 127; the clamp then
@@ -89,10 +89,11 @@ __global__ __launch_bounds__(kMaxThreads) void quantize_rows_reg(const float* __
   const float sc = STATIC ? (finite ? fixed : __builtin_nanf("")) : row_scale(amax, finite);
   if (threadIdx.x == 0) s[row] = sc;
   const bool zero = !finite || sc == 0.0f;
+  const float rc = zero ? 0.0f : fast_recip(sc);
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int64_t c = threadIdx.x + (int64_t)T * i;
-    if (c < nchunk) qr[c] = zero ? 0u : pack4(v[i], sc);
+    if (c < nchunk) qr[c] = zero ? 0u : pack4(v[i], sc, rc);
   }
 }
 
@@ -122,7 +123,8 @@ __global__ __launch_bounds__(kMaxThreads) void quantize_rows_2pass(const float* 
   const float sc = STATIC ? (finite ? fixed : __builtin_nanf("")) : row_scale(amax, finite);
   if (threadIdx.x == 0) s[row] = sc;
   const bool zero = !finite || sc == 0.0f;
-  for (int64_t c = threadIdx.x; c < nchunk; c += blockDim.x) qr[c] = zero ? 0u : pack4(xr[c], sc);
+  const float rc = zero ? 0.0f : fast_recip(sc);
+  for (int64_t c = threadIdx.x; c < nchunk; c += blockDim.x) qr[c] = zero ? 0u : pack4(xr[c], sc, rc);
 }
 
 template <int CPT, bool STATIC>

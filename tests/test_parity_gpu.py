@@ -57,6 +57,44 @@ def test_quantize_special_rows():
     assert_same_ints(host(q), q_ref, "codes")
 
 
+def _near_tie_rows(rng, rows, K, scale_of_row):
+    """Rows whose values sit on and within 4 ulps of the rounding ties (k + 1/2) s of
+    their own scale s (the row's absmax, 127 s, is in every row)."""
+    x = np.empty((rows, K), np.float32)
+    for i in range(rows):
+        s = np.float32(scale_of_row(i))
+        k = rng.integers(-127, 127, K)
+        t = ((k + 0.5) * s.astype(np.float64)).astype(np.float32)
+        steps = rng.integers(-4, 5, K)
+        for j in range(K):
+            v = t[j]
+            d = np.float32(np.inf) if steps[j] > 0 else np.float32(-np.inf)
+            for _ in range(abs(int(steps[j]))):
+                v = np.nextafter(v, d)
+            x[i, j] = v
+        x[i, 0] = np.float32(127.0) * s
+    return x
+
+
+def test_quantize_near_rounding_ties():
+    """Codes next to rounding ties, where multiplying by 1/s and dividing by s can
+    round differently: the codes must be those of the correctly rounded quotient."""
+    rng = np.random.default_rng(77)
+    x = _near_tie_rows(rng, 24, 512, lambda i: rng.uniform(0.5, 1.0) * 2.0 ** int(rng.integers(-20, 20)))
+    q_ref, s_ref = oracle.quantize_rows(x)
+    q, s = prism.quantize_rows(dev(x))
+    torch.cuda.synchronize()
+    assert_same_floats(host(s), s_ref, "scale")
+    assert_same_ints(host(q), q_ref, "codes")
+    for scale in (np.float32(0.0170001), np.float32(3.1e-3)):
+        xs = _near_tie_rows(rng, 8, 512, lambda i: scale)
+        xs[:, 0] *= np.float32(1.5)   # beyond the range: saturates
+        q_ref, s_ref = oracle.quantize_rows_static(xs, float(scale))
+        q, s = prism.quantize_rows_static(dev(xs), float(scale))
+        torch.cuda.synchronize()
+        assert_same_ints(host(q), q_ref, "static codes")
+
+
 STATIC_SCALES = [0.0625, 0.0170001, 0.0123, 3.0e-3, 2.0 ** -140]
 
 

@@ -77,15 +77,15 @@ class Launcher:
         f, a = self.lib.prism_repack_q8_0, (self.p(blocks), self.p(w), self.p(d), N, K, self.stream)
         return lambda: f(*a)
 
-    def repack_q4k(self, blocks, w, D, Mn):
-        N, K = w.shape
-        f, a = self.lib.prism_repack_q4_k, (self.p(blocks), self.p(w), self.p(D), self.p(Mn), N, K, self.stream)
+    def repack_q4k(self, blocks, w4, hdr):
+        N, K = w4.shape[0], 2 * w4.shape[1]
+        f, a = self.lib.prism_repack_q4_k, (self.p(blocks), self.p(w4), self.p(hdr), N, K, self.stream)
         return lambda: f(*a)
 
-    def q4k(self, q, sa, w, D, Mn, y):
+    def q4k(self, q, sa, w4, hdr, y):
         M, K = q.shape
-        N = w.shape[0]
-        f, a = self.lib.prism_gemm_w4a8_q4k, (self.p(q), self.p(sa), self.p(w), self.p(D), self.p(Mn), self.p(y),
+        N = w4.shape[0]
+        f, a = self.lib.prism_gemm_w4a8_q4k, (self.p(q), self.p(sa), self.p(w4), self.p(hdr), self.p(y),
                                               M, N, K, self.stream)
         return lambda: f(*a)
 
@@ -380,28 +380,26 @@ def kernels(torch, prism, wl, only=None):
                                              us_single_launch=t1 * 1e6, algorithmic_bytes=nbytes, copies=R)
         del srcs
     if only in (None, "q4k"):
-        # Q4_K weights for the block-scale shape (17408 x 5120): random super-block bytes
-        # (timing only), repacked once per copy, then the GEMM at M = 2048 and M = 1
+        # Q4_K weights of the block-scale shape (17408 x 5120): seeded super-block bytes
+        # whose d and dmin are finite binary16 values (timing only), R copies, each
+        # repacked once into its planes; then the GEMM at M = 2048 and M = 1
+        import numpy as np
         N, K = 17408, 5120
         nsb = N * (K // 256)
-        g = torch.Generator(device=dev).manual_seed(12)
-        R = _copies(N * K + 8 * N * (K // 32))
-        planes = []
-        srcs = [torch.randint(0, 256, (nsb * 144,), dtype=torch.uint8, device=dev, generator=g) for _ in range(2)]
-        for i in range(R):
-            w = torch.empty((N, K), dtype=torch.int8, device=dev)
-            D = torch.empty((N, K // 32), dtype=torch.float32, device=dev)
-            Mn = torch.empty((N, K // 32), dtype=torch.float32, device=dev)
-            D.fill_(1e-3)
-            Mn.fill_(1e-4)
-            planes.append((w, D, Mn))
-        t1, t = _time_launches(torch, [L.repack_q4k(srcs[i % 2], *planes[i]) for i in range(2)], 20)
-        nbytes = nsb * 144 + N * K + 8 * N * (K // 32)
+        rng = np.random.default_rng(12)
+        host_blocks = rng.integers(0, 256, (nsb, 144), dtype=np.uint8)
+        dd = (rng.uniform(0.5, 1.0, (nsb, 2)) * 2.0 ** rng.integers(-13, -5, (nsb, 2))).astype("<f2")
+        host_blocks[:, 0:4] = dd.view(np.uint8).reshape(nsb, 4)
+        blocks = torch.from_numpy(host_blocks.reshape(-1)).to(dev)
+        R = _copies(N * K // 2 + nsb * 16)
+        planes = [(torch.empty((N, K // 2), dtype=torch.uint8, device=dev),
+                   torch.empty((N, K // 256, 16), dtype=torch.uint8, device=dev)) for _ in range(R)]
+        t1, t = _time_launches(torch, [L.repack_q4k(blocks, *p) for p in planes], 20)
+        nbytes = 2 * nsb * 144
         out["repack_q4_k_17408x5120"] = dict(us=t * 1e6, gbs=nbytes / t / 1e9, hbm_frac=nbytes / t / 1e9 / PEAK_HBM_GBS,
                                              us_single_launch=t1 * 1e6, algorithmic_bytes=nbytes)
-        for _, D, Mn in planes:          # sane scales for the GEMM timing (random bytes may hold NaN)
-            D.fill_(1e-3)
-            Mn.fill_(1e-4)
+        torch.cuda.synchronize()
+        del blocks
         xb = wl.block()["x"]
         for M in (2048, 1):
             x = torch.from_numpy(xb[:M].copy()).to(dev)
@@ -411,11 +409,11 @@ def kernels(torch, prism, wl, only=None):
             y = torch.empty((M, N), dtype=torch.float32, device=dev)
             t1, t = _time_launches(torch, [L.q4k(q, sa, *p, y) for p in planes], 10 if M > 1 else 50)
             ops = 2 * M * N * K
-            nb = N * K + 8 * N * (K // 32) + M * K + 4 * M + 4 * M * N
+            nb = N * K // 2 + nsb * 16 + M * K + 4 * M + 4 * M * N   # packed codes, headers, q, s_a, y
             out["q4k_m%d" % M] = dict(us=t * 1e6, tops=ops / t / 1e12, mfma_frac=ops / t / 1e12 / PEAK_INT8_TOPS,
                                       gbs=nb / t / 1e9, hbm_frac=nb / t / 1e9 / PEAK_HBM_GBS,
-                                      us_single_launch=t1 * 1e6, copies=R)
-        del planes, srcs
+                                      us_single_launch=t1 * 1e6, copies=R, algorithmic_bytes=nb)
+        del planes
     if only in (None, "decode"):
         # One activation row (decode) through the two projections of the step.
         for name, c in (("proj_up", wl.proj_up()), ("proj_down", wl.proj_down())):

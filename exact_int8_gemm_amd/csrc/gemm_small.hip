@@ -270,7 +270,8 @@ bool pick_variant(const int8_t* q, const float* s_a, const int8_t* w, const floa
 
 // ---------------------------------------------------------------------------
 // Small-M block-scale GEMMs (M <= 16): fp16 block scales (Q8_0 style) or the
-// Q4_K planes (fp32 D = d * sc and Mn = dmin * m).  The fp32 fold over the
+// Q4_K planes (packed 4-bit codes and 16-byte super-block headers, from which
+// D = d * sc and Mn = dmin * m are decoded; both exact in fp32).  The fp32 fold over the
 // blocks is a chain in ascending k that cannot be split, but the exact int32
 // block sums can: a workgroup owns 16 output columns and walks K in chunks of
 // 4 * WAVES blocks.  Phase 1: each wave computes the sums P = sum q * w of
@@ -278,8 +279,12 @@ bool pick_variant(const int8_t* q, const float* s_a, const int8_t* w, const floa
 // with v_mfma_i32_16x16x32_i8 (one 32-k block per instruction, lane l holding
 // row / column l % 16) into LDS; operands are fetched as 16 bytes per lane,
 // 64 contiguous bytes per row and load, and regrouped into one block per
-// MFMA with v_permlane32_swap.  Every thread also moves one of the chunk's
-// scales into LDS.  Phase 2:
+// MFMA with v_permlane32_swap.  Q4_K codes stay packed: 32 bytes hold the
+// codes of two sub-blocks (byte l: k = l in the low nibble, k = 32 + l in the
+// high one), so the lanes that need k 0-15 and 32-47 of a block pair load the
+// same 16 bytes and keep the low or the high nibbles.  Every thread also
+// moves one of the chunk's scales into LDS (Q4_K: it decodes sc and m of one
+// sub-block from its super-block header).  Phase 2:
 // thread (m, n) folds the chunk's blocks into its chain in order,
 // f = fmaf((float)P, d, f) (Q4_K: then f = fmaf(-(float)S, Mn, f)).  Chunks
 // rotate through RING register sets: the loads of chunk c + RING - 1 are
@@ -287,37 +292,44 @@ bool pick_variant(const int8_t* q, const float* s_a, const int8_t* w, const floa
 template <bool Q4K, int WAVES, int RING>
 __global__ __launch_bounds__(64 * WAVES) void gemm_block_small_kernel(
     const int8_t* __restrict__ q, const float* __restrict__ s_a, const int8_t* __restrict__ w,
-    const uint16_t* __restrict__ d16, const float* __restrict__ Dp, const float* __restrict__ Mp,
-    float* __restrict__ y, int M, int N, int K) {
+    const uint16_t* __restrict__ d16, const uint8_t* __restrict__ hdr, float* __restrict__ y, int M, int N, int K) {
   constexpr int CH = 4 * WAVES;    // blocks per chunk: one scale per thread
   constexpr int PER = CH / WAVES;  // blocks per wave per chunk
   static_assert(WAVES >= 4, "phase 2 needs a thread for each of the 16 x 16 outputs");
   static_assert(RING >= 2 && RING <= 4, "chunk ring depth");
-  __shared__ int pbuf[CH][16][16];  // [block][row][column]
-  __shared__ int sbuf[Q4K ? CH : 1][16];
-  __shared__ float sdv[CH][16];
-  __shared__ float smv[Q4K ? CH : 1][16];
+  // Chunk sums and scales, each output's CH values contiguous (padded to CHP
+  // so that rows stay 16-byte aligned and consecutive columns fall in
+  // different banks): a chain thread reads them with 16-byte loads before its
+  // chain of fmas instead of one 4-byte LDS read per step.
+  constexpr int CHP = CH + 4;
+  __shared__ __attribute__((aligned(16))) int pbuf[16][16][CHP];  // [row][column][block]
+  __shared__ __attribute__((aligned(16))) int sbuf[Q4K ? 16 : 1][CHP];  // [row][block]
+  __shared__ __attribute__((aligned(16))) float sdv[16][CHP];      // [column][block]
+  __shared__ __attribute__((aligned(16))) float smv[Q4K ? 16 : 1][CHP];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = blockIdx.x * 16;
   const int NB = K / 32;
   const int col = lane & 15, g = lane >> 4;
 
+  // Bytes per weight row: K int8 codes, or K / 2 packed 4-bit codes.
+  const int WR = Q4K ? K / 2 : K;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(q, (int64_t)M * K);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + (size_t)n0 * (size_t)K, (int64_t)(N - n0) * K);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + (size_t)n0 * (size_t)WR, (int64_t)(N - n0) * WR);
   // Rows / columns outside the matrices start out of range and stay there (+ 32 b < 2^31).
   // Blocks past K of an in-range row read the next row's bytes; their sums are never stored.
-  // Lane (col, g) loads 16 bytes at 16 g of each 64-byte pair of blocks.
+  // Lane (col, g) loads 16 bytes at 16 g of each 64-byte pair of blocks (Q4_K: at
+  // 16 (g % 2) of the pair's 32 packed bytes, low nibbles for g < 2).
   const uint32_t qbase = col < M ? (uint32_t)(col * K + 16 * g) : kOutOfRange;
-  const uint32_t wbase = n0 + col < N ? (uint32_t)(col * K + 16 * g) : kOutOfRange;
+  const uint32_t wbase = n0 + col < N ? (uint32_t)(col * WR + 16 * (Q4K ? (g & 1) : g)) : kOutOfRange;
+  const int nib = (g >> 1) * 4;  // Q4_K: 0 = low nibbles, 4 = high nibbles
   const int64_t ones = 0x0101010101010101LL;
   // Scales of the 16 columns through one buffer resource; this thread moves
-  // scale (block tb, column tc) of each chunk, zero past K or past N.
-  constexpr int kSB = Q4K ? 4 : 2;
-  const int64_t sbytes = (int64_t)(N - n0) * NB * kSB;
+  // scale (block tb, column tc) of each chunk, zero past K or past N (Q4_K: the
+  // 16-byte header of the block's super-block, of which it decodes one sub-block).
+  const int NS = K / 256;
+  const int64_t sbytes = Q4K ? (int64_t)(N - n0) * NS * 16 : (int64_t)(N - n0) * NB * 2;
   const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(Q4K ? (const void*)(Dp + (size_t)n0 * NB) : (const void*)(d16 + (size_t)n0 * NB), sbytes);
-  const __amdgpu_buffer_rsrc_t rm = make_rsrc(Q4K ? (const void*)(Mp + (size_t)n0 * NB) : (const void*)d16,
-                                              Q4K ? sbytes : 0);
+      make_rsrc(Q4K ? (const void*)(hdr + (size_t)n0 * NS * 16) : (const void*)(d16 + (size_t)n0 * NB), sbytes);
   // Consecutive threads take consecutive blocks of one column, so a wave's
   // scale load reads a few contiguous runs instead of 16 scattered pieces.
   const int tb = threadIdx.x % CH, tc = threadIdx.x / CH;
@@ -327,28 +339,32 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_block_small_kernel(
   const float sam = chain ? s_a[pm] : 0.0f;  // loaded early, used once at the end
   float f = 0.0f;
 
+  // A chunk's loads stay raw in registers until the chunk is consumed (Q4_K:
+  // packed codes and the header; unpacking them right after the loads would
+  // make every chunk wait for its own loads).
   struct Chunk {
     int64_t a[PER], b[PER];
-    float d, m;
+    uint32_t d;  // binary16 bits of the block scale
+    v4i h;
   };
   auto load = [&](int b0, Chunk& c) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < PER; j += 2) {
       const int b = b0 + wave * PER + j;
       const v4i x = __builtin_amdgcn_raw_buffer_load_b128(rq, qbase + 32 * b, 0, 0);
-      const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rw, wbase + 32 * b, 0, 0);
+      const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rw, wbase + (Q4K ? 16 : 32) * b, 0, 0);
       c.a[j] = ((int64_t)(uint32_t)x[1] << 32) | (uint32_t)x[0];
       c.a[j + 1] = ((int64_t)(uint32_t)x[3] << 32) | (uint32_t)x[2];
       c.b[j] = ((int64_t)(uint32_t)v[1] << 32) | (uint32_t)v[0];
       c.b[j + 1] = ((int64_t)(uint32_t)v[3] << 32) | (uint32_t)v[2];
     }
-    const uint32_t so = (b0 + tb < NB && n0 + tc < N) ? (uint32_t)(tc * NB + b0 + tb) * kSB : kOutOfRange;
+    const bool sin = b0 + tb < NB && n0 + tc < N;
     if constexpr (Q4K) {
-      c.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, so, 0, 0));
-      c.m = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rm, so, 0, 0));
+      const uint32_t so = sin ? (uint32_t)(tc * NS + ((b0 + tb) >> 3)) * 16u : kOutOfRange;
+      c.h = __builtin_amdgcn_raw_buffer_load_b128(rs, so, 0, 0);
     } else {
-      c.d = (float)__builtin_bit_cast(_Float16, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs, so, 0, 0));
-      c.m = 0.0f;
+      const uint32_t so = sin ? (uint32_t)(tc * NB + b0 + tb) * 2u : kOutOfRange;
+      c.d = __builtin_amdgcn_raw_buffer_load_b16(rs, so, 0, 0);
     }
   };
   auto consume = [&](int b0, const Chunk& c) __attribute__((always_inline)) {
@@ -357,7 +373,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_block_small_kernel(
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       av[j] = c.a[j];
-      bv[j] = c.b[j];
+      bv[j] = Q4K ? (int64_t)(((uint64_t)c.b[j] >> nib) & 0x0f0f0f0f0f0f0f0full) : c.b[j];
     }
     // Lanes 0-31 (g = 0, 1) loaded 16 bytes of block j, lanes 32-63 16
     // bytes of block j + 1, as two 8-byte halves av[j] and av[j + 1].  A
@@ -384,28 +400,49 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_block_small_kernel(
       if (bl < nb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (4 * g + i < M) pbuf[bl][4 * g + i][col] = p[i];
+          if (4 * g + i < M) pbuf[4 * g + i][col][bl] = p[i];
       }
       if constexpr (Q4K) {
         const v4i sa = __builtin_amdgcn_mfma_i32_16x16x32_i8(av[j], ones, v4i{0, 0, 0, 0}, 0, 0, 0);
         if (bl < nb && col == 0) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (4 * g + i < M) sbuf[bl][4 * g + i] = sa[i];
+            if (4 * g + i < M) sbuf[4 * g + i][bl] = sa[i];
         }
       }
     }
-    sdv[tb][tc] = c.d;
-    if constexpr (Q4K) smv[tb][tc] = c.m;
+    if constexpr (Q4K) {
+      float d, m;
+      q4k_scale_min(c.h, (b0 + tb) & 7, d, m);
+      sdv[tc][tb] = d;
+      smv[tc][tb] = m;
+    } else {
+      sdv[tc][tb] = (float)__builtin_bit_cast(_Float16, (uint16_t)c.d);
+    }
     __syncthreads();
     if (chain) {
       // Blocks past K (i >= nb) hold stale sums but zero scales: an fma with a
       // zero scale adds a zero and leaves f unchanged (f starts at +0 and never
       // becomes -0), so the chain runs the whole chunk without a branch.
+      constexpr int H = 8;  // blocks per batch of reads
 #pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        f = __builtin_fmaf((float)pbuf[i][pm][pn], sdv[i][pn], f);
-        if constexpr (Q4K) f = __builtin_fmaf(-(float)sbuf[i][pm], smv[i][pn], f);
+      for (int i0 = 0; i0 < CH; i0 += H) {
+        int pv[H], sv[H];
+        float dv[H], mv[H];
+#pragma unroll
+        for (int i = 0; i < H; i += 4) {
+          *reinterpret_cast<v4i*>(pv + i) = *reinterpret_cast<const v4i*>(&pbuf[pm][pn][i0 + i]);
+          *reinterpret_cast<v4f*>(dv + i) = *reinterpret_cast<const v4f*>(&sdv[pn][i0 + i]);
+          if constexpr (Q4K) {
+            *reinterpret_cast<v4i*>(sv + i) = *reinterpret_cast<const v4i*>(&sbuf[pm][i0 + i]);
+            *reinterpret_cast<v4f*>(mv + i) = *reinterpret_cast<const v4f*>(&smv[pn][i0 + i]);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < H; ++i) {
+          f = __builtin_fmaf((float)pv[i], dv[i], f);
+          if constexpr (Q4K) f = __builtin_fmaf(-(float)sv[i], mv[i], f);
+        }
       }
     }
     __syncthreads();  // the next chunk reuses the buffers
@@ -610,12 +647,12 @@ bool launch_gemv(const float* x, int8_t* q_out, float* s_out, const int8_t* q, c
 }  // namespace
 
 int launch_gemm_block_small(const int8_t* q, const float* s_a, const int8_t* w, const uint16_t* d16,
-                            const float* D, const float* Mn, float* y, int M, int N, int K, hipStream_t st) {
+                            const uint8_t* hdr, float* y, int M, int N, int K, hipStream_t st) {
   const unsigned grid = (unsigned)((N + 15) / 16);
   // 4 waves (16-block chunks), two chunks in flight: the fastest of waves in
   // {4, 8, 16} x ring depth in {2, 3, 4} at 17408 x 5120, M = 1 and 16.
-  if (D) gemm_block_small_kernel<true, 4, 2><<<grid, 256, 0, st>>>(q, s_a, w, nullptr, D, Mn, y, M, N, K);
-  else gemm_block_small_kernel<false, 4, 2><<<grid, 256, 0, st>>>(q, s_a, w, d16, nullptr, nullptr, y, M, N, K);
+  if (hdr) gemm_block_small_kernel<true, 4, 2><<<grid, 256, 0, st>>>(q, s_a, w, nullptr, hdr, y, M, N, K);
+  else gemm_block_small_kernel<false, 4, 2><<<grid, 256, 0, st>>>(q, s_a, w, d16, nullptr, y, M, N, K);
   return launch_status();
 }
 

@@ -222,17 +222,19 @@ int launch_gemm_tiled(const int8_t* q, const float* s_a, const void* w, bool w_i
 int launch_gemm_blockscale(const int8_t* q, const float* s_a, const int8_t* w, const uint16_t* d, float* y,
                            int32_t* partials, int M, int N, int K, hipStream_t st) {
   if (M <= kBlockSmallMMax && !partials)
-    return launch_gemm_block_small(q, s_a, w, d, nullptr, nullptr, y, M, N, K, st);
+    return launch_gemm_block_small(q, s_a, w, d, nullptr, y, M, N, K, st);
   tiled::dma::launch_block<128, 64, 2, 2, 2, 3>(q, s_a, w, d, y, partials, M, N, K, st);
   return launch_status();
 }
 
-// Q4_K-native W4A8 on the repacked planes: the block-scale pipeline with fp32
-// sub-block scales and mins (128 x 128 tiles, two workgroups per CU).
-int launch_gemm_q4k(const int8_t* q, const float* s_a, const int8_t* w, const float* D, const float* Mn, float* y,
-                    int M, int N, int K, hipStream_t st) {
-  if (M <= kBlockSmallMMax) return launch_gemm_block_small(q, s_a, w, nullptr, D, Mn, y, M, N, K, st);
-  tiled::dma::launch_q4k<128, 128, 2, 2, 2, 2>(q, s_a, w, D, Mn, y, M, N, K, st);
+// Q4_K-native W4A8 on the repacked planes (packed codes and super-block
+// headers): the block-scale pipeline with the scales decoded from the headers
+// (128 x 128 tiles, two workgroups per CU).
+int launch_gemm_q4k(const int8_t* q, const float* s_a, const uint8_t* w4, const uint8_t* hdr, float* y, int M, int N,
+                    int K, hipStream_t st) {
+  if (M <= kBlockSmallMMax)
+    return launch_gemm_block_small(q, s_a, reinterpret_cast<const int8_t*>(w4), nullptr, hdr, y, M, N, K, st);
+  tiled::dma::launch_q4k<128, 128, 2, 2, 2, 2>(q, s_a, w4, hdr, y, M, N, K, st);
   return launch_status();
 }
 

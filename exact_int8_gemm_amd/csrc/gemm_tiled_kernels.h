@@ -954,90 +954,107 @@ void launch_block(const int8_t* q, const float* s_a, const int8_t* w, const uint
         q, s_a, w, d, y, nullptr, M, N, K, tiles_m, tiles_n);
 }
 
-// Q4_K-native W4A8 on repacked planes: codes w [N][K] (0..15 as int8),
-// D = d * sc and Mn = dmin * m [N][K/32] fp32 (exact products).  Per 32-k
-// sub-block: P = sum code * a and S = sum a, both exact int32 from MFMAs
-// started at zero (S from a B operand of ones, so it lands in the same
-// row-per-register layout as P), folded in ascending sub-block order:
-// f = fmaf((float)P, D, f); f = fmaf(-(float)S, Mn, f); y = f * s_a[m].
-// Same direct-to-LDS pipeline as gemm_block_kernel; D and Mn of the stage's
-// blocks ride along (4-byte copies), D of block ks, column c at dword
-// ks * BN + c of the scale area and Mn KS * BN dwords further.
+// Q4_K-native W4A8 on the repacked planes: packed 4-bit codes w4 [N][K/2]
+// (32 bytes per pair of 32-k sub-blocks: byte l holds k = l in its low nibble
+// and k = 32 + l in its high one) and the 16-byte super-block headers hdr
+// [N][K/256][16] (d, dmin, 6-bit scales and mins).  Per 32-k sub-block: P =
+// sum code * a and S = sum a, both exact int32 from MFMAs started at zero (S
+// from a B operand of ones, so it lands in the same row-per-register layout
+// as P), folded in ascending sub-block order: f = fmaf((float)P, D, f);
+// f = fmaf(-(float)S, Mn, f); y = f * s_a[m], with D = d * sc and Mn = dmin *
+// m decoded from the header (exact in fp32).
+//
+// Direct-to-LDS pipeline as in gemm_block_kernel, a stage of 128 k: A rows of
+// 128 bytes, B rows of 64 packed bytes (chunk c of row r stored at c ^ ((r /
+// 4) % 4), so 16 consecutive rows reading one chunk hit 16 distinct 16-byte
+// bank groups), and the headers of the stage's super-block (one 16-byte copy
+// per column).  After a stage has landed, the workgroup decodes its BN x 4
+// (D, Mn) pairs into LDS (one barrier), then folds; the fragment reads
+// unpack the codes with one shift and mask per dword.
 template <int BM, int BN, int WM, int WN, int RING, int OCC>
 __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_q4k_kernel(const int8_t* __restrict__ q,
                                                                      const float* __restrict__ s_a,
-                                                                     const int8_t* __restrict__ w,
-                                                                     const float* __restrict__ Dp,
-                                                                     const float* __restrict__ Mp,
+                                                                     const uint8_t* __restrict__ w4,
+                                                                     const uint8_t* __restrict__ hdr,
                                                                      float* __restrict__ y, int M, int N, int K,
                                                                      int tiles_m, int tiles_n) {
   constexpr int BK = 128;
   constexpr int KS = BK / 32;  // sub-blocks per stage
   using C = Cfg<BM, BN, BK, WM, WN, RING>;
-  constexpr int kSCopies = 2 * KS * BN / 64;  // D and Mn
-  constexpr int kPerWaveS = kSCopies / C::kNW;
-  static_assert(kSCopies % C::kNW == 0, "scale copies must divide among waves");
-  constexpr int kPerWave = C::kPerWave + kPerWaveS;
-  constexpr int kSOff = (BM + BN) * BK;  // scale area within a stage
-  constexpr int kStage = kSOff + 2 * KS * BN * 4;
-  static_assert(RING * kStage <= 160 * 1024, "LDS ring exceeds 160 KiB");
-  static_assert((RING - 2) * kPerWave < 64, "vmcnt range");
+  constexpr int NT = C::kNT;
+  constexpr int kCopiesB = BN * (BK / 2) / 1024;  // packed B: 16 rows of 64 bytes per copy
+  constexpr int kCopiesH = BN * 16 / 256;         // headers: 4-byte copies, 16 columns per copy
+  static_assert(kCopiesB % C::kNW == 0 && kCopiesH % C::kNW == 0, "copies must divide among waves");
+  constexpr int kPerWaveB = kCopiesB / C::kNW;
+  constexpr int kPerWaveH = kCopiesH / C::kNW;
+  constexpr int kBOff = BM * BK;                  // packed B within a stage
+  constexpr int kHOff = kBOff + BN * (BK / 2);    // headers within a stage
+  constexpr int kStage = kHOff + BN * 16;
+  static_assert(RING * kStage + 2 * KS * BN * 4 <= 160 * 1024 / OCC, "LDS");
   __shared__ __attribute__((aligned(1024))) int8_t lds0[kStage];
   __shared__ __attribute__((aligned(1024))) int8_t lds1[kStage];
   __shared__ __attribute__((aligned(1024))) int8_t lds2[RING > 2 ? kStage : 16];
-  __shared__ __attribute__((aligned(1024))) int8_t lds3[RING > 3 ? kStage : 16];
+  __shared__ float dsc[KS][BN], msc[KS][BN];  // decoded D and Mn of the stage being folded
 
   int tm, tn;
   tile_of(tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  const int NB = K / 32;
+  const int NS = K / 256;
 
   const v4i ra = rsrc_words(q + (size_t)m0 * (size_t)K, (int64_t)(M - m0) * K);
-  const v4i rb = rsrc_words(w + (size_t)n0 * (size_t)K, (int64_t)(N - n0) * K);
-  const v4i rD = rsrc_words(Dp + (size_t)n0 * (size_t)NB, (int64_t)(N - n0) * NB * 4);
-  const v4i rM = rsrc_words(Mp + (size_t)n0 * (size_t)NB, (int64_t)(N - n0) * NB * 4);
-  uint32_t off[C::kPerWave];
-  int kc[C::kPerWave];
+  const v4i rb = rsrc_words(w4 + (size_t)n0 * (size_t)(K / 2), (int64_t)(N - n0) * (K / 2));
+  const v4i rh = rsrc_words(hdr + (size_t)n0 * (size_t)NS * 16, (int64_t)(N - n0) * NS * 16);
+  // A copies: as gemm_dma_kernel.  Rows past M or N read zeros (out of range).
+  uint32_t offa[C::kPerWaveA];
+  int kca[C::kPerWaveA];
 #pragma unroll
-  for (int s = 0; s < C::kPerWave; ++s) {
-    const bool isA = s < C::kPerWaveA;
-    const int copy = isA ? wave * C::kPerWaveA + s : wave * C::kPerWaveB + (s - C::kPerWaveA);
+  for (int s = 0; s < C::kPerWaveA; ++s) {
+    const int copy = wave * C::kPerWaveA + s;
     const int row = copy * C::kRowsPerCopy + lane / C::kChunks;
     const int chunk = (lane % C::kChunks) ^ C::swz(row);
-    kc[s] = chunk * 16;
-    const bool valid = isA ? (m0 + row < M) : (n0 + row < N);
-    off[s] = valid ? (uint32_t)(row * K + chunk * 16) : kOutOfRange;
+    kca[s] = chunk * 16;
+    offa[s] = (m0 + row < M) ? (uint32_t)(row * K + chunk * 16) : kOutOfRange;
   }
-  // Scale copies of this wave: copy c is array c / (KS * BN / 64) (D, then Mn),
-  // block (c % (KS * BN / 64)) / (BN / 64), columns ((c % (BN / 64)) * 64 + lane).
-  uint32_t soff[kPerWaveS];
-  int sks[kPerWaveS];
+  // B copies: lane -> row copy * 16 + lane / 4, LDS slot lane % 4, which holds
+  // logical chunk (lane % 4) ^ ((row / 4) % 4) of the row's 64 packed bytes.
+  // K is a multiple of 256 (whole super-blocks), so a 128-k stage is either
+  // inside K or past it as a whole.
+  uint32_t offb[kPerWaveB];
 #pragma unroll
-  for (int s = 0; s < kPerWaveS; ++s) {
-    const int c = (wave * kPerWaveS + s) % (KS * BN / 64);
-    const int col = (c % (BN / 64)) * 64 + lane;
-    sks[s] = c / (BN / 64);
-    soff[s] = (n0 + col < N) ? (uint32_t)(col * NB * 4) : kOutOfRange;
+  for (int s = 0; s < kPerWaveB; ++s) {
+    const int copy = wave * kPerWaveB + s;
+    const int row = copy * 16 + lane / 4;
+    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+    offb[s] = (n0 + row < N) ? (uint32_t)(row * (K / 2) + chunk * 16) : kOutOfRange;
+  }
+  // Header copies, 4 bytes per lane: copy c moves dword lane % 4 of the
+  // header of column 16 c + lane / 4, every wave the same number of copies
+  // (a branch around an LDS copy, even a uniform one, made the compiler spill
+  // hundreds of registers here).
+  uint32_t offh[kPerWaveH];
+#pragma unroll
+  for (int s = 0; s < kPerWaveH; ++s) {
+    const int col = (wave * kPerWaveH + s) * 16 + lane / 4;
+    offh[s] = (n0 + col < N) ? (uint32_t)(col * NS * 16 + (lane & 3) * 4) : kOutOfRange;
   }
   auto issue = [&](int8_t* base, int stage) __attribute__((always_inline)) {
     const int k0 = stage * BK;
 #pragma unroll
-    for (int s = 0; s < C::kPerWave; ++s) {
-      const bool isA = s < C::kPerWaveA;
-      const int copy = isA ? wave * C::kPerWaveA + s : wave * C::kPerWaveB + (s - C::kPerWaveA);
-      const uint32_t o = (k0 + kc[s] < K) ? off[s] + (uint32_t)k0 : kOutOfRange;
-      const int8_t* dst = base + (isA ? 0 : BM * BK) + copy * 1024;
-      copy_to_lds(isA ? ra : rb, lds_addr(dst), o);
+    for (int s = 0; s < C::kPerWaveA; ++s) {
+      const uint32_t o = (k0 + kca[s] < K) ? offa[s] + (uint32_t)k0 : kOutOfRange;
+      copy_to_lds(ra, lds_addr(base + (wave * C::kPerWaveA + s) * 1024), o);
     }
 #pragma unroll
-    for (int s = 0; s < kPerWaveS; ++s) {
-      const int cg = wave * kPerWaveS + s;  // 0 .. kSCopies - 1; the first half is D
-      const int b = stage * KS + sks[s];
-      const uint32_t o = (b < NB) ? soff[s] + (uint32_t)(b * 4) : kOutOfRange;
-      const int8_t* dst = base + kSOff + cg * 256;
-      copy4_to_lds(cg < kSCopies / 2 ? rD : rM, lds_addr(dst), o);
+    for (int s = 0; s < kPerWaveB; ++s) {
+      const uint32_t o = (k0 < K) ? offb[s] + (uint32_t)(k0 / 2) : kOutOfRange;
+      copy_to_lds(rb, lds_addr(base + kBOff + (wave * kPerWaveB + s) * 1024), o);
+    }
+#pragma unroll
+    for (int s = 0; s < kPerWaveH; ++s) {
+      const uint32_t o = (k0 < K && offh[s] != kOutOfRange) ? offh[s] + (uint32_t)(stage / 2) * 16u : kOutOfRange;
+      copy4_to_lds(rh, lds_addr(base + kHOff + (wave * kPerWaveH + s) * 256), o);
     }
   };
 
@@ -1051,12 +1068,28 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_q4k_kernel(const int8_
 
   const int rl = lane & 31;
   const int sw = C::swz(rl);
+  const int swb = (rl >> 2) & 3;
   const int arow = (wm * C::kWTM + rl) * BK;
-  const int brow = (BM + wn * C::kWTN + rl) * BK;
+  const int brow = kBOff + (wn * C::kWTN + rl) * (BK / 2);
   int ncol[C::kTN];
 #pragma unroll
   for (int j = 0; j < C::kTN; ++j) ncol[j] = wn * C::kWTN + j * 32 + rl;
 
+  // Decode the stage's (D, Mn) pairs: thread t takes column t % BN and
+  // sub-blocks KS * (t / BN) / (NT / BN) onwards of the stage (the stage is
+  // half of super-block stage / 2: sub-blocks 4 (stage % 2) + ks).
+  auto decode = [&](const int8_t* buf, int stage) __attribute__((always_inline)) {
+    constexpr int kPer = KS * BN / NT;  // pairs per thread
+    const int col = threadIdx.x % BN, ks0 = (threadIdx.x / BN) * kPer;
+    const v4i h = *reinterpret_cast<const v4i*>(buf + kHOff + col * 16);
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      float D, Mn;
+      q4k_scale_min(h, 4 * (stage & 1) + ks0 + e, D, Mn);
+      dsc[ks0 + e][col] = D;
+      msc[ks0 + e][col] = Mn;
+    }
+  };
   auto compute = [&](const int8_t* buf) __attribute__((always_inline)) {
     const v16i zero = v16i{};
     const v4i ones = v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101};
@@ -1065,15 +1098,19 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_q4k_kernel(const int8_
       // Sub-blocks past K read zero operands and zero scales: both fmas
       // return f unchanged (f starts at +0 and never becomes -0).
       const int c = ((2 * ks + (lane >> 5)) ^ sw) * 16;
+      const int cb = ((2 * (ks >> 1) + (lane >> 5)) ^ swb) * 16;  // packed chunk of this lane's 16 k
+      const int nib = (ks & 1) * 4;                               // odd sub-blocks: high nibbles
       v4i af[C::kTM], bf[C::kTN];
       float dv[C::kTN], mv[C::kTN];
 #pragma unroll
       for (int i = 0; i < C::kTM; ++i) af[i] = *reinterpret_cast<const v4i*>(buf + arow + i * 32 * BK + c);
 #pragma unroll
       for (int j = 0; j < C::kTN; ++j) {
-        bf[j] = *reinterpret_cast<const v4i*>(buf + brow + j * 32 * BK + c);
-        dv[j] = *reinterpret_cast<const float*>(buf + kSOff + (ks * BN + ncol[j]) * 4);
-        mv[j] = *reinterpret_cast<const float*>(buf + kSOff + ((KS + ks) * BN + ncol[j]) * 4);
+        const v4i p = *reinterpret_cast<const v4i*>(buf + brow + j * 32 * (BK / 2) + cb);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bf[j][e] = (int)(((uint32_t)p[e] >> nib) & 0x0f0f0f0fu);
+        dv[j] = dsc[ks][ncol[j]];
+        mv[j] = msc[ks][ncol[j]];
       }
 #pragma unroll
       for (int i = 0; i < C::kTM; ++i) {
@@ -1091,33 +1128,36 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_q4k_kernel(const int8_
           }
         }
       }
+      // keeps the next sub-block's fragment reads and unpacking after this
+      // one's folds (hoisting them spills registers)
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // Iteration: wait for this wave's copies of the stage, barrier (all copies
+  // landed, every wave done with the previous stage and its decoded scales),
+  // start the copies of stage + RING - 1, decode the scales, barrier, fold.
   auto step = [&](const int8_t* cur, int8_t* nxt, int stage) __attribute__((always_inline)) {
-    wait_vmcnt<(RING - 2) * kPerWave>();
+    wait_vmcnt<0>();
     __syncthreads();
     issue(nxt, stage + RING - 1);
+    decode(cur, stage);
+    __syncthreads();
     compute(cur);
   };
 
+  static_assert(RING == 2 || RING == 3, "ring depth");
   const int nk = (K + BK - 1) / BK;
   const int nkr = (nk + RING - 1) / RING * RING;
   issue(lds0, 0);
   if constexpr (RING > 2) issue(lds1, 1);
-  if constexpr (RING > 3) issue(lds2, 2);
   for (int k = 0; k < nkr; k += RING) {
     if constexpr (RING == 2) {
       step(lds0, lds1, k);
       step(lds1, lds0, k + 1);
-    } else if constexpr (RING == 3) {
+    } else {
       step(lds0, lds2, k);
       step(lds1, lds0, k + 1);
       step(lds2, lds1, k + 2);
-    } else {
-      step(lds0, lds3, k);
-      step(lds1, lds0, k + 1);
-      step(lds2, lds1, k + 2);
-      step(lds3, lds2, k + 3);
     }
   }
   wait_vmcnt<0>();
@@ -1138,11 +1178,11 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_q4k_kernel(const int8_
 }
 
 template <int BM, int BN, int WM, int WN, int RING, int OCC>
-void launch_q4k(const int8_t* q, const float* s_a, const int8_t* w, const float* D, const float* Mn, float* y, int M,
-                int N, int K, hipStream_t st) {
+void launch_q4k(const int8_t* q, const float* s_a, const uint8_t* w4, const uint8_t* hdr, float* y, int M, int N,
+                int K, hipStream_t st) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   gemm_q4k_kernel<BM, BN, WM, WN, RING, OCC><<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, 0, st>>>(
-      q, s_a, w, D, Mn, y, M, N, K, tiles_m, tiles_n);
+      q, s_a, w4, hdr, y, M, N, K, tiles_m, tiles_n);
 }
 
 }  // namespace dma

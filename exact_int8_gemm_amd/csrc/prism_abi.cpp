@@ -157,29 +157,27 @@ int prism_quantize_rows_static(const float* x, int8_t* q, float* scale, float s,
   return prism::launch_quantize_rows_static(x, q, scale, s, M, K, static_cast<hipStream_t>(stream));
 }
 
-int prism_repack_q4_k(const uint8_t* blocks, int8_t* w, float* D, float* Mn, int64_t N, int64_t K, void* stream) {
+int prism_repack_q4_k(const uint8_t* blocks, uint8_t* w4, uint8_t* hdr, int64_t N, int64_t K, void* stream) {
   if (N < 0 || K < 0) return PRISM_ERR_INVALID_ARG;
   if (N == 0) return PRISM_OK;
   if (K == 0 || N > INT_MAX || K > INT_MAX) return PRISM_ERR_INVALID_ARG;
-  if (!blocks || !w || !D || !Mn) return PRISM_ERR_INVALID_ARG;
-  if (K % 256 != 0 || !aligned(blocks, 16) || !aligned(w, 16) || !aligned(D, 4) || !aligned(Mn, 4))
-    return PRISM_ERR_ALIGNMENT;
-  if ((N * (K / 256) + 63) / 64 > INT_MAX) return PRISM_ERR_INVALID_ARG;  // grid size
+  if (!blocks || !w4 || !hdr) return PRISM_ERR_INVALID_ARG;
+  if (K % 256 != 0 || !aligned(blocks, 16) || !aligned(w4, 16) || !aligned(hdr, 16)) return PRISM_ERR_ALIGNMENT;
+  if ((N * (K / 256) * 9 + 255) / 256 > INT_MAX) return PRISM_ERR_INVALID_ARG;  // grid size
   const int dev = check_device();
   if (dev != PRISM_OK) return dev;
-  return prism::launch_repack_q4_k(blocks, w, D, Mn, N, K, static_cast<hipStream_t>(stream));
+  return prism::launch_repack_q4_k(blocks, w4, hdr, N, K, static_cast<hipStream_t>(stream));
 }
 
-int prism_gemm_w4a8_q4k(const int8_t* q, const float* s_a, const int8_t* w, const float* D, const float* Mn,
-                        float* y, int64_t M, int64_t N, int64_t K, void* stream) {
+int prism_gemm_w4a8_q4k(const int8_t* q, const float* s_a, const uint8_t* w4, const uint8_t* hdr, float* y, int64_t M,
+                        int64_t N, int64_t K, void* stream) {
   bool noop;
-  int st = check_gemm(q, s_a, w, D, y, nullptr, M, N, K, 32, &noop);
+  int st = check_gemm(q, s_a, w4, hdr, y, nullptr, M, N, K, 256, &noop);
   if (st != PRISM_OK || noop) return st;
-  if (!Mn) return PRISM_ERR_INVALID_ARG;
-  if (!aligned(D, 4) || !aligned(Mn, 4)) return PRISM_ERR_ALIGNMENT;
+  if (!aligned(hdr, 16)) return PRISM_ERR_ALIGNMENT;
   if (!grid_fits(M, N)) return PRISM_ERR_INVALID_ARG;
   if ((st = check_device()) != PRISM_OK) return st;
-  return prism::launch_gemm_q4k(q, s_a, w, D, Mn, y, (int)M, (int)N, (int)K, static_cast<hipStream_t>(stream));
+  return prism::launch_gemm_q4k(q, s_a, w4, hdr, y, (int)M, (int)N, (int)K, static_cast<hipStream_t>(stream));
 }
 
 int prism_repack_q8_0(const uint8_t* blocks, int8_t* w, uint16_t* d, int64_t N, int64_t K, void* stream) {

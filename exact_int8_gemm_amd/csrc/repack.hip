@@ -90,71 +90,29 @@ __global__ __launch_bounds__(kPerGroup) void repack_q8_0_kernel(const uint8_t* _
   }
 }
 
-// Q4_K super-blocks (public GGUF layout, 144 bytes per 256 weights): binary16
-// d and dmin, 12 bytes of 6-bit sub-block scales sc_j and mins m_j, 128 bytes
-// of 4-bit codes (byte 32 g + l: weight 64 g + l in the low nibble, weight
-// 64 g + 32 + l in the high one).  Output planes: the codes as int8 [N][K]
-// (0..15), D = d * sc_j and Mn = dmin * m_j as fp32 [N][K/32]; both products
-// are exact in fp32 (11 + 6 significant bits).  One workgroup moves 64
-// super-blocks (9216 bytes, a whole number of 16-byte pieces, each
-// super-block 16-byte aligned) through LDS.
-constexpr int kQ4kBytes = 144;
-constexpr int kQ4kPerGroup = 64;
-
-__global__ __launch_bounds__(256) void repack_q4_k_kernel(const uint8_t* __restrict__ blocks, int8_t* __restrict__ w,
-                                                          float* __restrict__ D, float* __restrict__ Mn,
-                                                          int64_t nsuper) {
-  __shared__ __attribute__((aligned(16))) uint8_t buf[kQ4kPerGroup * kQ4kBytes];
-  const int64_t s0 = (int64_t)blockIdx.x * kQ4kPerGroup;
-  const int ns = nsuper - s0 < kQ4kPerGroup ? (int)(nsuper - s0) : kQ4kPerGroup;
-  const uint32_t nbytes = (uint32_t)ns * kQ4kBytes;  // a multiple of 16
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(blocks + s0 * kQ4kBytes), (short)0, (int)nbytes,
-                                        0x00020000);
-  for (uint32_t i = threadIdx.x; i < nbytes / 16; i += 256)
-    *reinterpret_cast<v4i*>(buf + 16 * i) = __builtin_amdgcn_raw_buffer_load_b128(r, i * 16, 0, 0);
-  __syncthreads();
-
-  // Codes: piece h covers codes 16 h' .. 16 h' + 15 of super-block h / 16 (h' = h % 16),
-  // all within one half of one 64-code group, so one 16-byte read of qs gives them.
-  for (int h = threadIdx.x; h < ns * 16; h += 256) {
-    const int sb = h >> 4, k0 = (h & 15) * 16, g = k0 >> 6, l = k0 & 63;
-    const v4i v = *reinterpret_cast<const v4i*>(buf + sb * kQ4kBytes + 16 + 32 * g + (l & 31));
-    v4i o;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = (int)(l < 32 ? ((uint32_t)v[e] & 0x0f0f0f0fu) : (((uint32_t)v[e] >> 4) & 0x0f0f0f0fu));
-    *reinterpret_cast<v4i*>(w + (s0 + sb) * 256 + k0) = o;
-  }
-  // Scales: thread t handles sub-blocks 2 (t % 4) and 2 (t % 4) + 1 of super-block t / 4.
-  const int t = threadIdx.x, sb = t >> 2;
-  if (sb < ns) {
-    const uint8_t* b = buf + sb * kQ4kBytes;
-    const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(b[0] | (b[1] << 8)));
-    const float dmin = (float)__builtin_bit_cast(_Float16, (uint16_t)(b[2] | (b[3] << 8)));
-    const uint8_t* sc = b + 4;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int j = 2 * (t & 3) + e;
-      int c, m;
-      if (j < 4) {
-        c = sc[j] & 63;
-        m = sc[j + 4] & 63;
-      } else {
-        c = (sc[j + 4] & 15) | ((sc[j - 4] >> 6) << 4);
-        m = (sc[j + 4] >> 4) | ((sc[j] >> 6) << 4);
-      }
-      D[(s0 + sb) * 8 + j] = d * (float)c;
-      Mn[(s0 + sb) * 8 + j] = dmin * (float)m;
-    }
-  }
+// Q4_K super-blocks (144 bytes: d, dmin, 12 scale bytes, 128 code bytes) ->
+// the planes of the Q4_K GEMM: the 16 leading bytes of super-block s to
+// hdr + 16 s, its 128 code bytes, in the file's order, to w4 + 128 s (rows of
+// w4 are K / 2 bytes, super-blocks of a row follow each other).  144 = 9 x 16,
+// so with the blocks 16-byte aligned every 16-byte piece stays whole: thread
+// p moves piece p % 9 of super-block p / 9 with one 16-byte load and store.
+// Consecutive threads read consecutive pieces.
+__global__ __launch_bounds__(256) void repack_q4_k_kernel(const uint8_t* __restrict__ blocks, uint8_t* __restrict__ w4,
+                                                          uint8_t* __restrict__ hdr, int64_t npieces) {
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (p >= npieces) return;
+  const int64_t sb = p / 9;
+  const int i = (int)(p - sb * 9);
+  const v4i v = *reinterpret_cast<const v4i*>(blocks + 16 * p);
+  uint8_t* dst = i == 0 ? hdr + 16 * sb : w4 + 128 * sb + 16 * (i - 1);
+  *reinterpret_cast<v4i*>(dst) = v;
 }
 
 }  // namespace
 
-int launch_repack_q4_k(const uint8_t* blocks, int8_t* w, float* D, float* Mn, int64_t N, int64_t K, hipStream_t st) {
-  const int64_t nsuper = N * (K / 256);
-  const int64_t groups = (nsuper + kQ4kPerGroup - 1) / kQ4kPerGroup;
-  repack_q4_k_kernel<<<(unsigned)groups, 256, 0, st>>>(blocks, w, D, Mn, nsuper);
+int launch_repack_q4_k(const uint8_t* blocks, uint8_t* w4, uint8_t* hdr, int64_t N, int64_t K, hipStream_t st) {
+  const int64_t npieces = N * (K / 256) * 9;
+  repack_q4_k_kernel<<<(unsigned)((npieces + 255) / 256), 256, 0, st>>>(blocks, w4, hdr, npieces);
   return launch_status();
 }
 

@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libprism.so")
 
 PRISM_OK = 0
-ABI_VERSION = 10
+ABI_VERSION = 11
 K_MAX = 131040
 
 # Dispatch-table entries of the W8A8 / W4A8 calls (PRISM_VARIANT_* in include/prism.h).
@@ -55,9 +55,9 @@ def _declare(lib):
     lib.prism_repack_q8_0.restype = i32
     lib.prism_repack_q8_0.argtypes = [p, p, p, i64, i64, p]
     lib.prism_repack_q4_k.restype = i32
-    lib.prism_repack_q4_k.argtypes = [p, p, p, p, i64, i64, p]
+    lib.prism_repack_q4_k.argtypes = [p, p, p, i64, i64, p]
     lib.prism_gemm_w4a8_q4k.restype = i32
-    lib.prism_gemm_w4a8_q4k.argtypes = [p, p, p, p, p, p, i64, i64, i64, p]
+    lib.prism_gemm_w4a8_q4k.argtypes = [p, p, p, p, p, i64, i64, i64, p]
     lib.prism_quantize_gemm_w8a8.restype = i32
     lib.prism_quantize_gemm_w8a8.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, p]
     for name in ("prism_gemm_w8a8_variant", "prism_gemm_w4a8_variant"):
@@ -179,32 +179,31 @@ def repack_q8_0(blocks, N, K, w=None, d=None):
     return w, d
 
 
-def repack_q4_k(blocks, N, K, w=None, D=None, Mn=None):
+def repack_q4_k(blocks, N, K, w4=None, hdr=None):
     """Q4_K super-blocks (uint8 tensor of N * K/256 * 144 bytes on the GPU) ->
-    (w int8 [N, K] codes 0..15, D float32 [N, K/32] = d * sc, Mn float32 [N, K/32] = dmin * m)."""
+    (w4 uint8 [N, K/2] packed codes in the file's order, hdr uint8 [N, K/256, 16] super-block headers)."""
     dev = _gpu(blocks, "blocks")
     N, K = int(N), int(K)
     if K <= 0 or K % 256:
         raise ValueError("K must be a positive multiple of 256")
     _need(blocks, "blocks", torch.uint8, (N * (K // 256) * 144,), dev)
-    w = torch.empty((N, K), dtype=torch.int8, device=dev) if w is None else _need(w, "w", torch.int8, (N, K), dev)
-    D = torch.empty((N, K // 32), dtype=torch.float32, device=dev) if D is None else \
-        _need(D, "D", torch.float32, (N, K // 32), dev)
-    Mn = torch.empty((N, K // 32), dtype=torch.float32, device=dev) if Mn is None else \
-        _need(Mn, "Mn", torch.float32, (N, K // 32), dev)
+    w4 = torch.empty((N, K // 2), dtype=torch.uint8, device=dev) if w4 is None else \
+        _need(w4, "w4", torch.uint8, (N, K // 2), dev)
+    hdr = torch.empty((N, K // 256, 16), dtype=torch.uint8, device=dev) if hdr is None else \
+        _need(hdr, "hdr", torch.uint8, (N, K // 256, 16), dev)
     with torch.cuda.device(dev):
-        _check(lib().prism_repack_q4_k(_ptr(blocks), _ptr(w), _ptr(D), _ptr(Mn), N, K, _stream(dev)))
-    return w, D, Mn
+        _check(lib().prism_repack_q4_k(_ptr(blocks), _ptr(w4), _ptr(hdr), N, K, _stream(dev)))
+    return w4, hdr
 
 
-def gemm_w4a8_q4k(q, s_a, w, D, Mn, y=None):
-    """Q4_K-native W4A8: q int8 [M,K], s_a f32 [M], codes w int8 [N,K], D and Mn f32 [N,K/32] -> y f32 [M,N]."""
-    dev, M, N, K = _gemm_args(q, s_a, w, lambda k: k, torch.int8, "D", D, torch.float32, lambda n, k: (n, k // 32))
-    _need(Mn, "Mn", torch.float32, (N, K // 32), dev)
+def gemm_w4a8_q4k(q, s_a, w4, hdr, y=None):
+    """Q4_K-native W4A8: q int8 [M,K], s_a f32 [M], w4 uint8 [N,K/2] packed codes, hdr uint8 [N,K/256,16]
+    -> y f32 [M,N]."""
+    dev, M, N, K = _gemm_args(q, s_a, w4, lambda k: k // 2, torch.uint8, "hdr", hdr, torch.uint8,
+                              lambda n, k: (n, k // 256, 16))
     y = torch.empty((M, N), dtype=torch.float32, device=dev) if y is None else _need(y, "y", torch.float32, (M, N), dev)
     with torch.cuda.device(dev):
-        _check(lib().prism_gemm_w4a8_q4k(_ptr(q), _ptr(s_a), _ptr(w), _ptr(D), _ptr(Mn), _ptr(y), M, N, K,
-                                         _stream(dev)))
+        _check(lib().prism_gemm_w4a8_q4k(_ptr(q), _ptr(s_a), _ptr(w4), _ptr(hdr), _ptr(y), M, N, K, _stream(dev)))
     return y
 
 

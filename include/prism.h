@@ -42,7 +42,7 @@ extern "C" {
 #endif
 
 /* Bumped on any change of a signature or of the semantics below. */
-#define PRISM_ABI_VERSION 10
+#define PRISM_ABI_VERSION 11
 
 /* Largest accepted K.  For K <= 131040 every exact sum of K products of two
  * int8 values (|q|, |w| <= 128) lies strictly inside the int32 range. */
@@ -51,7 +51,7 @@ extern "C" {
 /* Status codes. */
 #define PRISM_OK 0
 #define PRISM_ERR_INVALID_ARG (-1) /* null required pointer, negative size, N or K = 0 with M > 0, K > PRISM_K_MAX */
-#define PRISM_ERR_ALIGNMENT (-2)   /* misaligned pointer, or K not a multiple of 16 (32 for block-scale and W4A8) */
+#define PRISM_ERR_ALIGNMENT (-2)   /* misaligned pointer, or K not a multiple of 16 (32 for block-scale and W4A8, 256 for Q4_K) */
 #define PRISM_ERR_UNSUPPORTED (-3) /* the current device is not gfx950, or no device is usable */
 #define PRISM_ERR_LAUNCH (-4)      /* the kernel launch reported an error */
 
@@ -128,24 +128,30 @@ int prism_repack_q8_0(const uint8_t* blocks, int8_t* w, uint16_t* d,
  * codes (byte 32 g + l: weight 64 g + l in the low nibble, 64 g + 32 + l in
  * the high one).  Weight = d * sc_j * code - dmin * m_j.
  *   blocks [N * K/256][144] bytes, input (16-byte aligned).
- *   w      [N][K] int8 output: the codes, 0..15 (16-byte aligned).
- *   D, Mn  [N][K/32] fp32 outputs: d * sc_j and dmin * m_j, exact (4-byte aligned).
+ *   w4     [N][K/2] bytes, output: the 128 code bytes of each super-block, in
+ *          the file's own order (super-block t of row n at bytes 128 t ..
+ *          128 t + 127 of row n); still 4 bits per weight (16-byte aligned).
+ *   hdr    [N][K/256][16] bytes, output: the 16 leading bytes of each
+ *          super-block (d, dmin, the 12 scale bytes) (16-byte aligned).
+ * Pure byte movement: the two planes hold every byte of the blocks once.
  * K must be a positive multiple of 256; N = 0 is a no-op.
  */
-int prism_repack_q4_k(const uint8_t* blocks, int8_t* w, float* D, float* Mn,
+int prism_repack_q4_k(const uint8_t* blocks, uint8_t* w4, uint8_t* hdr,
                       int64_t N, int64_t K, void* stream);
 
 /*
  * W4A8 on Q4_K weights (the planes of prism_repack_q4_k).
- *   q [M][K] int8, s_a [M] fp32, w [N][K] int8 codes, D and Mn [N][K/32] fp32.
+ *   q [M][K] int8, s_a [M] fp32, w4 [N][K/2] packed codes, hdr [N][K/256][16].
  *   y [M][N] fp32 output.
- * Per 32-k sub-block b: P_b = sum q[m][k] * w[n][k] and S_b = sum q[m][k],
- * both exact integers; f = +0; for b ascending: f = fmaf((float)P_b,
- * D[n][b], f); f = fmaf(-(float)S_b, Mn[n][b], f); then y[m][n] = f * s_a[m].
- * K must be a multiple of 32.
+ * For sub-block b (32 k) of super-block t = b / 8, j = b % 8: D = d * sc_j and
+ * Mn = dmin * m_j from the super-block's header (both exact in fp32);
+ * P_b = sum q[m][k] * code[n][k] and S_b = sum q[m][k], both exact integers;
+ * f = +0; for b ascending: f = fmaf((float)P_b, D, f); f = fmaf(-(float)S_b,
+ * Mn, f); then y[m][n] = f * s_a[m].
+ * K must be a multiple of 256; q, w4 and hdr 16-byte aligned.
  */
-int prism_gemm_w4a8_q4k(const int8_t* q, const float* s_a, const int8_t* w, const float* D,
-                        const float* Mn, float* y, int64_t M, int64_t N, int64_t K, void* stream);
+int prism_gemm_w4a8_q4k(const int8_t* q, const float* s_a, const uint8_t* w4, const uint8_t* hdr,
+                        float* y, int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
  * W8A8 GEMM with per-output-channel weight scales (README "Why

@@ -59,7 +59,7 @@ def bind(lib):
     lib.oracle_repack_q8_0.restype = ctypes.c_int
     lib.oracle_repack_q8_0.argtypes = [p, p, p, i64, i64]
     lib.oracle_repack_q4_k.restype = ctypes.c_int
-    lib.oracle_repack_q4_k.argtypes = [p, p, p, p, i64, i64]
+    lib.oracle_repack_q4_k.argtypes = [p, p, p, i64, i64]
     lib.oracle_gemm_w4a8_q4k.restype = ctypes.c_int
     lib.oracle_gemm_w4a8_q4k.argtypes = [p, p, p, p, i64, i64, i64]
     for name in ("oracle_gemm_w8a8", "oracle_gemm_w4a8", "oracle_gemm_w8a8_blockscale"):
@@ -135,15 +135,14 @@ def repack_q8_0(blocks, N, K):
 
 
 def repack_q4_k(blocks, N, K):
-    """Q4_K super-blocks (uint8, N * K/256 * 144 bytes) -> (codes int8 [N, K] in 0..15,
-    D float32 [N, K/32] = d * sc, Mn float32 [N, K/32] = dmin * m)."""
+    """Q4_K blocks (uint8, N * K/256 * 144 bytes) -> (w4 uint8 [N, K/2] packed codes,
+    hdr uint8 [N, K/256, 16] super-block headers)."""
     blocks = _c(blocks, np.uint8).reshape(-1)
     assert blocks.size == N * (K // 256) * 144
-    w = np.empty((N, K), np.int8)
-    D = np.empty((N, K // 32), np.float32)
-    Mn = np.empty((N, K // 32), np.float32)
-    _check(_load().oracle_repack_q4_k(_ptr(blocks), _ptr(w), _ptr(D), _ptr(Mn), N, K))
-    return w, D, Mn
+    w4 = np.empty((N, K // 2), np.uint8)
+    hdr = np.empty((N, K // 256, 16), np.uint8)
+    _check(_load().oracle_repack_q4_k(_ptr(blocks), _ptr(w4), _ptr(hdr), N, K))
+    return w4, hdr
 
 
 def gemm_w4a8_q4k(q, s_a, blocks, N):

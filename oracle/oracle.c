@@ -49,6 +49,10 @@
  *      code * a and S = sum a are exact integers, D = d * sc_j and Mn = dmin
  *      * m_j are exact in fp32, and f = +0; for each sub-block in ascending
  *      k: f = fmaf((float)P, D, f); f = fmaf(-(float)S, Mn, f); y = f * s_a.
+ *   R9 Q4_K planes for the GPU GEMM: the file's 128 code bytes of each
+ *      super-block, in their own order, form the row's packed codes (K/2
+ *      bytes per row, still 4 bits per weight), and its 16 leading bytes (d,
+ *      dmin, scales) form a separate header plane.
  *   R6 static activation scale ("Quick start": ranges measured once, ahead
  *      of time): one fp32 s > 0 for the whole tensor; q = clamp(rint(x / s),
  *      -127, 127) saturates values beyond the calibrated range (an infinite
@@ -202,22 +206,18 @@ static int oracle_q4k_code(const uint8_t* sb, int i) { /* i = 0..255 within the 
     return l < 32 ? (qs[32 * g + l] & 15) : (qs[32 * g + l - 32] >> 4);
 }
 
-/* Q4_K blocks -> codes w [N][K] (0..15 as int8), D [N][K/32] = d*sc and Mn [N][K/32] = dmin*m (fp32). */
-int oracle_repack_q4_k(const uint8_t* blocks, int8_t* w, float* D, float* Mn, int64_t N, int64_t K) {
-    if (N < 0 || K <= 0 || K % 256 != 0 || (N > 0 && (!blocks || !w || !D || !Mn))) return ORACLE_ERR_ARG;
+/* Q4_K blocks -> the two planes the GPU GEMM reads (R9): the 128 code bytes of
+ * each super-block, in the file's own order, to w4 [N][K/2] (super-block t of
+ * row n at bytes 128 t .. 128 t + 127 of row n), and its first 16 bytes (d,
+ * dmin and the 12 scale bytes) to hdr [N][K/256][16].  Pure byte movement. */
+int oracle_repack_q4_k(const uint8_t* blocks, uint8_t* w4, uint8_t* hdr, int64_t N, int64_t K) {
+    if (N < 0 || K <= 0 || K % 256 != 0 || (N > 0 && (!blocks || !w4 || !hdr))) return ORACLE_ERR_ARG;
     const int64_t NS = K / 256;
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t t = 0; t < NS; ++t) {
             const uint8_t* sb = blocks + (n * NS + t) * 144;
-            const float d = oracle_f16_to_f32((uint16_t)(sb[0] | (sb[1] << 8)));
-            const float dmin = oracle_f16_to_f32((uint16_t)(sb[2] | (sb[3] << 8)));
-            for (int j = 0; j < 8; ++j) {
-                int sc, mn;
-                oracle_q4k_scale_min(sb, j, &sc, &mn);
-                D[n * (K / 32) + t * 8 + j] = d * (float)sc;
-                Mn[n * (K / 32) + t * 8 + j] = dmin * (float)mn;
-            }
-            for (int i = 0; i < 256; ++i) w[n * K + t * 256 + i] = (int8_t)oracle_q4k_code(sb, i);
+            for (int i = 0; i < 16; ++i) hdr[(n * NS + t) * 16 + i] = sb[i];
+            for (int i = 0; i < 128; ++i) w4[n * (K / 2) + t * 128 + i] = sb[16 + i];
         }
     }
     return ORACLE_OK;

@@ -88,9 +88,9 @@ lib.prism_quantize_rows_static.argtypes = [p, p, p, ctypes.c_float, i64, i64, p]
 lib.prism_repack_q8_0.restype = i32
 lib.prism_repack_q8_0.argtypes = [p, p, p, i64, i64, p]
 lib.prism_repack_q4_k.restype = i32
-lib.prism_repack_q4_k.argtypes = [p, p, p, p, i64, i64, p]
+lib.prism_repack_q4_k.argtypes = [p, p, p, i64, i64, p]
 lib.prism_gemm_w4a8_q4k.restype = i32
-lib.prism_gemm_w4a8_q4k.argtypes = [p, p, p, p, p, p, i64, i64, i64, p]
+lib.prism_gemm_w4a8_q4k.argtypes = [p, p, p, p, p, i64, i64, i64, p]
 lib.prism_quantize_gemm_w8a8.restype = i32
 lib.prism_quantize_gemm_w8a8.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, p]
 for n in ("prism_gemm_w8a8_variant", "prism_gemm_w4a8_variant"):
@@ -171,34 +171,36 @@ CASES += [
 ]
 _RK = "prism_repack_q4_k"
 CASES += [
-    (_RK, [A, A, A, A, 0, 256, None], OK),
-    (_RK, [A, A, A, A, -1, 256, None], INVALID),
-    (_RK, [A, A, A, A, 4, 0, None], INVALID),
-    (_RK, [None, A, A, A, 4, 256, None], INVALID),
-    (_RK, [A, A, A, None, 4, 256, None], INVALID),
-    (_RK, [A, A, A, A, 4, 288, None], ALIGN),          # K % 256
-    (_RK, [A + 8, A, A, A, 4, 256, None], ALIGN),
-    (_RK, [A, A, A + 2, A, 4, 256, None], ALIGN),
-    (_RK, [A, A, A, A + 2, 4, 256, None], ALIGN),
+    (_RK, [A, A, A, 0, 256, None], OK),
+    (_RK, [A, A, A, -1, 256, None], INVALID),
+    (_RK, [A, A, A, 4, 0, None], INVALID),
+    (_RK, [None, A, A, 4, 256, None], INVALID),
+    (_RK, [A, None, A, 4, 256, None], INVALID),
+    (_RK, [A, A, None, 4, 256, None], INVALID),
+    (_RK, [A, A, A, 4, 288, None], ALIGN),          # K % 256
+    (_RK, [A + 8, A, A, 4, 256, None], ALIGN),
+    (_RK, [A, A + 8, A, 4, 256, None], ALIGN),
+    (_RK, [A, A, A + 8, 4, 256, None], ALIGN),
 ]
 _GK = "prism_gemm_w4a8_q4k"
 
 
-def _k(q=A, sa=A, w=A, D=A, Mn=A, y=A, M=4, N=16, K=256):
-    return [q, sa, w, D, Mn, y, M, N, K, None]
+def _k(q=A, sa=A, w4=A, hdr=A, y=A, M=4, N=16, K=256):
+    return [q, sa, w4, hdr, y, M, N, K, None]
 
 
 CASES += [
     (_GK, _k(M=0), OK),
     (_GK, _k(M=-1), INVALID),
     (_GK, _k(K=0), INVALID),
-    (_GK, _k(Mn=None), INVALID),
-    (_GK, _k(D=None), INVALID),
+    (_GK, _k(hdr=None), INVALID),
+    (_GK, _k(w4=None), INVALID),
     (_GK, _k(q=None), INVALID),
     (_GK, _k(K=48), ALIGN),
-    (_GK, _k(D=A + 2), ALIGN),
-    (_GK, _k(Mn=A + 2), ALIGN),
-    (_GK, _k(w=A + 8), ALIGN),
+    (_GK, _k(K=288), ALIGN),       # whole super-blocks only
+    (_GK, _k(hdr=A + 8), ALIGN),
+    (_GK, _k(w4=A + 8), ALIGN),
+    (_GK, _k(y=A + 2), ALIGN),
 ]
 
 

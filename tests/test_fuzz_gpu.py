@@ -48,8 +48,8 @@ def test_random_shape(kind, M, N, K):
     if kind == "q4k":
         from test_oracle_pins import _pack_q4_k, _q4k_case
         blocks = _pack_q4_k(*_q4k_case(M + N + K, N, K))
-        w, D, Mn = prism.repack_q4_k(dev(blocks), N, K)
-        y = prism.gemm_w4a8_q4k(q, s, w, D, Mn)
+        w4, hdr = prism.repack_q4_k(dev(blocks), N, K)
+        y = prism.gemm_w4a8_q4k(q, s, w4, hdr)
         torch.cuda.synchronize()
         assert_same_floats(host(y), oracle.gemm_w4a8_q4k(q_ref, s_ref, blocks, N), "y")
         return

@@ -66,6 +66,9 @@ MUTANTS = [
     ("q4k: min term unfused", "f = fmaf(-(float)sa, Mn, f);", "{ float t = -(float)sa * Mn; f = f + t; }", 1),
     ("q4k: d and dmin swapped", "const float d = oracle_f16_to_f32((uint16_t)(sb[0] | (sb[1] << 8)));",
      "const float d = oracle_f16_to_f32((uint16_t)(sb[2] | (sb[3] << 8)));", 0),
+    ("q4k repack: header one byte late", "hdr[(n * NS + t) * 16 + i] = sb[i];", "hdr[(n * NS + t) * 16 + i] = sb[(i + 1) % 16];", 1),
+    ("q4k repack: codes from the header's end", "w4[n * (K / 2) + t * 128 + i] = sb[16 + i];",
+     "w4[n * (K / 2) + t * 128 + i] = sb[12 + i];", 1),
     ("no int32 range check", "if (sum >= INT32_LIMIT || sum < -INT32_LIMIT) {", "if (0) {", 0),
 ]
 

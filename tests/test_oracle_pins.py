@@ -395,7 +395,8 @@ def _q4k_case(seed, N, K, zero_mins=False):
 
 
 def test_q4_k_hand_fixture():
-    # sub-block 0: sc 1, m 2; sub-block 4: sc 0b11_1010 = 58, m 0b01_0101 = 21; the rest 0
+    """One super-block written by hand; the repack only splits its bytes: the 16 leading
+    bytes (d, dmin, scales) go to the header plane, the 128 code bytes to the codes plane."""
     s = [0] * 12
     s[0] = 0b11000001     # sc0 = 1, top bits = high bits of sc4
     s[4] = 0b01000010     # m0 = 2, top bits = high bits of m4
@@ -404,24 +405,31 @@ def test_q4_k_hand_fixture():
     qs[0] = 0x73          # weight 0: code 3; weight 32: code 7
     qs[32 + 5] = 0xF0     # weight 64 + 5: code 0; weight 96 + 5: code 15
     raw = bytes([0x00, 0x3C, 0x00, 0x38]) + bytes(s) + bytes(qs)   # d = 1.0, dmin = 0.5
-    w, D, Mn = oracle.repack_q4_k(np.frombuffer(raw, np.uint8), 1, 256)
-    assert D[0].tolist() == [1.0, 0, 0, 0, 58.0, 0, 0, 0]
-    assert Mn[0].tolist() == [1.0, 0, 0, 0, 10.5, 0, 0, 0]
-    expect = np.zeros(256, np.int8)
-    expect[0], expect[32], expect[101] = 3, 7, 15
-    assert np.array_equal(w[0], expect)
+    two = raw + bytes(range(144))   # a second super-block of the same row: K = 512
+    w4, hdr = oracle.repack_q4_k(np.frombuffer(two, np.uint8), 1, 512)
+    assert hdr.shape == (1, 2, 16) and w4.shape == (1, 256)
+    assert bytes(hdr[0, 0]) == raw[:16] and bytes(hdr[0, 1]) == bytes(range(16))
+    assert w4[0, 0] == 0x73 and w4[0, 37] == 0xF0 and int(w4[0, :128].sum()) == 0x73 + 0xF0
+    assert bytes(w4[0, 128:]) == bytes(range(16, 144))
 
 
 def test_q4_k_round_trip_with_independent_packer():
+    """Blocks packed from the layout's description; putting the header and code planes back
+    together (numpy slicing) gives the blocks again, byte for byte."""
     codes, d16, dmin16, sc, mn = _q4k_case(140, 3, 512)
     d16[0, 0] = np.float16(6.0e-8)     # subnormal binary16 scale
-    w, D, Mn = oracle.repack_q4_k(_pack_q4_k(codes, d16, dmin16, sc, mn), 3, 512)
-    assert np.array_equal(w, codes)
-    dd = np.repeat(d16.astype(np.float64), 8, axis=1)
-    dm = np.repeat(dmin16.astype(np.float64), 8, axis=1)
-    # d * sc and dmin * m are exact in fp32 (11 + 6 significant bits)
-    assert np.array_equal(bits(D), bits((dd * sc).astype(np.float32)))
-    assert np.array_equal(bits(Mn), bits((dm * mn).astype(np.float32)))
+    blocks = _pack_q4_k(codes, d16, dmin16, sc, mn)
+    w4, hdr = oracle.repack_q4_k(blocks, 3, 512)
+    again = np.concatenate([hdr, w4.reshape(3, 2, 128)], axis=2).reshape(-1)
+    assert np.array_equal(again, blocks)
+    # the code plane keeps the file's nibble order: byte 32 g + l of a super-block holds
+    # the code of weight 64 g + l (low nibble) and of weight 64 g + 32 + l (high nibble)
+    for n in range(3):
+        for t in range(2):
+            qs = w4[n, 128 * t:128 * t + 128].astype(np.int64)
+            for g in range(4):
+                assert np.array_equal(qs[32 * g:32 * g + 32] & 15, codes[n, 256 * t + 64 * g:256 * t + 64 * g + 32])
+                assert np.array_equal(qs[32 * g:32 * g + 32] >> 4, codes[n, 256 * t + 64 * g + 32:256 * t + 64 * g + 64])
 
 
 def test_q4_k_gemm_within_bound_of_exact_dot_product():

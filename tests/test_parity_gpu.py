@@ -205,15 +205,14 @@ def test_repack_q8_0_then_blockscale_gemm():
 
 @pytest.mark.parametrize("N,K", [(1, 256), (3, 512), (63, 256), (65, 768), (100, 5120)])
 def test_repack_q4_k(N, K):
-    """Random bytes (every pattern is a block, NaN and infinite scales included)."""
+    """Random bytes: the code and header planes, byte for byte."""
     rng = np.random.default_rng(N * 17 + K)
     blocks = rng.integers(0, 256, N * (K // 256) * 144, dtype=np.uint8)
-    w_ref, D_ref, M_ref = oracle.repack_q4_k(blocks, N, K)
-    w, D, Mn = prism.repack_q4_k(dev(blocks), N, K)
+    w_ref, h_ref = oracle.repack_q4_k(blocks, N, K)
+    w4, hdr = prism.repack_q4_k(dev(blocks), N, K)
     torch.cuda.synchronize()
-    assert_same_ints(host(w), w_ref, "codes")
-    assert_same_floats(host(D), D_ref, "d * sc")
-    assert_same_floats(host(Mn), M_ref, "dmin * m")
+    assert_same_ints(host(w4), w_ref, "packed codes")
+    assert_same_ints(host(hdr), h_ref, "headers")
 
 
 @pytest.mark.parametrize("M", [1, 7, 16, 17, 65, 129, 257])
@@ -227,9 +226,29 @@ def test_gemm_w4a8_q4k(M, N, K):
     x = rng.standard_normal((M, K), dtype=np.float32)
     q_ref, sa_ref = oracle.quantize_rows(x)
     y_ref = oracle.gemm_w4a8_q4k(q_ref, sa_ref, blocks, N)
-    w, D, Mn = prism.repack_q4_k(dev(blocks), N, K)
-    y = prism.gemm_w4a8_q4k(dev(q_ref), dev(sa_ref), w, D, Mn)
+    w4, hdr = prism.repack_q4_k(dev(blocks), N, K)
+    y = prism.gemm_w4a8_q4k(dev(q_ref), dev(sa_ref), w4, hdr)
     torch.cuda.synchronize()
+    assert_same_floats(host(y), y_ref, "y")
+
+
+@pytest.mark.parametrize("M", [3, 40])
+def test_gemm_w4a8_q4k_on_oracle_planes_with_any_header_bytes(M):
+    """The GEMM on planes written by the oracle's repack (not the GPU's), from random
+    block bytes: headers with binary16 NaN, infinite, subnormal and zero d and dmin,
+    every 6-bit scale and min; rows of zeros and a NaN row of activations."""
+    N, K = 70, 768
+    rng = np.random.default_rng(M * 3 + 1)
+    blocks = rng.integers(0, 256, N * (K // 256) * 144, dtype=np.uint8)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    x[1] = 0.0
+    x[2, 5] = np.nan
+    q_ref, sa_ref = oracle.quantize_rows(x)
+    y_ref = oracle.gemm_w4a8_q4k(q_ref, sa_ref, blocks, N)
+    w_ref, h_ref = oracle.repack_q4_k(blocks, N, K)
+    y = prism.gemm_w4a8_q4k(dev(q_ref), dev(sa_ref), dev(w_ref), dev(h_ref))
+    torch.cuda.synchronize()
+    assert np.isnan(y_ref).any() and np.isfinite(y_ref).any()
     assert_same_floats(host(y), y_ref, "y")
 
 

@@ -440,6 +440,22 @@ def kernels(torch, prism, wl, only=None):
             nbytes_x = nbytes - K - 4 + 4 * K   # x read as fp32 instead of the codes
             out["decode_m1_" + name].update(quantize_then_gemm_us=t2 * 1e6, fused_quantize_gemm_us=t3 * 1e6,
                                             fused_hbm_frac=nbytes_x / t3 / 1e9 / PEAK_HBM_GBS)
+            # a few rows (batched decode): two launches against the one-launch call
+            for M in (2, 4, 16):
+                xm = T(c["x"][:M].copy())
+                qm = torch.empty((M, K), dtype=torch.int8, device=dev)
+                sam = torch.empty((M,), dtype=torch.float32, device=dev)
+                ym = torch.empty((M, N), dtype=torch.float32, device=dev)
+                pairs = []
+                for w in ws:
+                    fq, fg = L.quantize(xm, qm, sam), L.w8a8(qm, sam, w, sw, ym)
+                    pairs.append(lambda fq=fq, fg=fg: fq() or fg())
+                _, t2 = _time_launches(torch, pairs, 100)
+                _, t3 = _time_launches(torch, [L.quantize_w8a8(xm, qm, sam, w, sw, ym) for w in ws], 100)
+                nb = N * K + 4 * N + 4 * M * K + M * K + 4 * M + 4 * M * N   # w, s_w, x, q, scale, y
+                out["decode_m%d_%s" % (M, name)] = dict(quantize_then_gemm_us=t2 * 1e6, fused_quantize_gemm_us=t3 * 1e6,
+                                                        fused_hbm_frac=nb / t3 / 1e9 / PEAK_HBM_GBS,
+                                                        algorithmic_bytes=nb, copies=R)
             del ws
     if only in (None, "vendor"):
         # Context: the vendor int8 GEMM (hipBLASLt through torch._int_mm) on the

@@ -61,14 +61,21 @@ __device__ inline void unpack_w4(const v4i p, v4i& lo, v4i& hi) {
   hi = v4i{o[4], o[5], o[6], o[7]};
 }
 
-template <int MB, int CB, bool W4, int WAVES, int U>
-__global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(const int8_t* __restrict__ q,
-                                                                const float* __restrict__ s_a,
-                                                                const int8_t* __restrict__ w,
-                                                                const float* __restrict__ s_w,
-                                                                float* __restrict__ y,
-                                                                int32_t* __restrict__ acc_out, int M, int N,
-                                                                int K, int G) {
+// The body of the small-M GEMM, shared by gemm_small_kernel and the fused
+// quantize + GEMM kernel below.
+// EARLY: before() is called first, then the first batch of weights is
+// requested, then wait() is called, after which q (codes, rows a_stride
+// bytes apart) and s_a are read from LDS.
+struct NoWait {
+  __device__ void operator()() const {}
+};
+
+template <int MB, int CB, bool W4, int WAVES, int U, bool EARLY = false, class Before = NoWait,
+          class Wait = NoWait>
+__device__ inline void small_gemm(const int8_t* q, const float* s_a, const int8_t* __restrict__ w,
+                                  const float* __restrict__ s_w, float* __restrict__ y,
+                                  int32_t* __restrict__ acc_out, int M, int N, int K, int G,
+                                  Before before = Before(), Wait wait = Wait(), int a_stride = 0) {
   __shared__ int red[WAVES][CB * MB * 4][64];
 
   const int lane = threadIdx.x & 63;
@@ -96,21 +103,23 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(const int8_t* __
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) qbase[mb] = (mb * 16 + col < M) ? (uint32_t)((mb * 16 + col) * K) : kOutOfRange;
 
-  // The epilogue scales of this thread's outputs, loaded now so that the
+  // The epilogue scales of this thread's outputs, loaded ahead so that the
   // epilogue does not wait for a memory round trip after the reduction.
   constexpr int kOut = CB * MB * 4 * 64;
   constexpr int kEpt = (kOut + 64 * WAVES - 1) / (64 * WAVES);
   float ea[kEpt], ew[kEpt];
+  auto load_scales = [&](bool act) {
 #pragma unroll
-  for (int t = 0; t < kEpt; ++t) {
-    const int e = threadIdx.x + t * 64 * WAVES;
-    const int idx = e >> 6, l = e & 63;
-    const int m = ((idx / 4) % MB) * 16 + (l >> 4) * 4 + idx % 4;
-    const int n = n0 + (idx / (MB * 4)) * 16 + (l & 15);
-    const bool ok = e < kOut && m < M && n < n1;
-    ea[t] = ok ? s_a[m] : 0.0f;
-    ew[t] = ok ? s_w[n] : 0.0f;
-  }
+    for (int t = 0; t < kEpt; ++t) {
+      const int e = threadIdx.x + t * 64 * WAVES;
+      const int idx = e >> 6, l = e & 63;
+      const int m = ((idx / 4) % MB) * 16 + (l >> 4) * 4 + idx % 4;
+      const int n = n0 + (idx / (MB * 4)) * 16 + (l & 15);
+      const bool ok = e < kOut && m < M && n < n1;
+      if (act) ea[t] = ok ? s_a[m] : 0.0f;
+      else ew[t] = ok ? s_w[n] : 0.0f;
+    }
+  };
 
   v4i acc[CB][MB];
 #pragma unroll
@@ -118,10 +127,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(const int8_t* __
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[cb][mb] = v4i{0, 0, 0, 0};
 
-  for (int u0 = ub; u0 < ue; u0 += U) {
-    // All loads of the batch first.
-    v4i wl[CB][U][W4 ? 1 : 2];
-    v4i al[MB][U][2];
+  constexpr int WF = W4 ? 1 : 2;  // 16-byte weight fragments per unit and column
+  auto load_w = [&](int u0, v4i (&wl)[CB][U][WF]) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const int kk = (u0 + j) * kUnitK + g * 32;
@@ -133,18 +140,32 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(const int8_t* __
           wl[cb][j][0] = bload(rw, in ? wbase[cb] + (uint32_t)(kk / 2) : kOutOfRange);
         } else {
           wl[cb][j][0] = bload(rw, in ? wbase[cb] + (uint32_t)kk : kOutOfRange);
-          wl[cb][j][W4 ? 0 : 1] = bload(rw, in2 ? wbase[cb] + (uint32_t)(kk + 16) : kOutOfRange);
+          wl[cb][j][WF - 1] = bload(rw, in2 ? wbase[cb] + (uint32_t)(kk + 16) : kOutOfRange);
         }
       }
+    }
+  };
+  auto load_a = [&](int u0, v4i (&al)[MB][U][2]) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int kk = (u0 + j) * kUnitK + g * 32;
+      const bool in = (u0 + j < ue) && kk < K;
+      const bool in2 = (u0 + j < ue) && kk + 16 < K;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        al[mb][j][0] = bload(rq, in ? qbase[mb] + (uint32_t)kk : kOutOfRange);
-        al[mb][j][1] = bload(rq, in2 ? qbase[mb] + (uint32_t)(kk + 16) : kOutOfRange);
+        if constexpr (EARLY) {
+          const int row = mb * 16 + col;
+          const int8_t* pa = q + row * a_stride + kk;
+          al[mb][j][0] = (row < M && in) ? *reinterpret_cast<const v4i*>(pa) : v4i{0, 0, 0, 0};
+          al[mb][j][1] = (row < M && in2) ? *reinterpret_cast<const v4i*>(pa + 16) : v4i{0, 0, 0, 0};
+        } else {
+          al[mb][j][0] = bload(rq, in ? qbase[mb] + (uint32_t)kk : kOutOfRange);
+          al[mb][j][1] = bload(rq, in2 ? qbase[mb] + (uint32_t)(kk + 16) : kOutOfRange);
+        }
       }
     }
-    // Keep every load of the batch ahead of the first MFMA (the scheduler
-    // would otherwise pair each load with its use and wait on it).
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto mma = [&](const v4i (&wl)[CB][U][WF], const v4i (&al)[MB][U][2]) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
 #pragma unroll
@@ -154,7 +175,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(const int8_t* __
           unpack_w4(wl[cb][j][0], b0, b1);
         } else {
           b0 = wl[cb][j][0];
-          b1 = wl[cb][j][W4 ? 0 : 1];
+          b1 = wl[cb][j][WF - 1];
         }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -162,6 +183,40 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(const int8_t* __
           acc[cb][mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(al[mb][j][1], b1, acc[cb][mb], 0, 0, 0);
         }
       }
+    }
+  };
+
+  if constexpr (!EARLY) {
+    load_scales(true);
+    load_scales(false);
+    for (int u0 = ub; u0 < ue; u0 += U) {
+      // All loads of the batch first.
+      v4i wl[CB][U][WF];
+      v4i al[MB][U][2];
+      load_w(u0, wl);
+      load_a(u0, al);
+      // Keep every load of the batch ahead of the first MFMA (the scheduler
+      // would otherwise pair each load with its use and wait on it).
+      __builtin_amdgcn_sched_barrier(0);
+      mma(wl, al);
+    }
+  } else {
+    // The weights of the first batch are requested before the wait for the
+    // activations, which then overlaps their latency.  The weight scales are
+    // requested after it: a wait for any earlier load would wait for them
+    // too (loads complete in order).
+    before();
+    v4i wl[CB][U][WF];
+    load_w(ub, wl);
+    wait();
+    load_scales(false);
+    load_scales(true);
+    for (int u0 = ub; u0 < ue; u0 += U) {
+      if (u0 != ub) load_w(u0, wl);
+      v4i al[MB][U][2];
+      load_a(u0, al);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(wl, al);
     }
   }
 
@@ -195,6 +250,132 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(const int8_t* __
       y[o] = v * ew[t];
     }
   }
+}
+
+template <int MB, int CB, bool W4, int WAVES, int U>
+__global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(const int8_t* __restrict__ q,
+                                                                const float* __restrict__ s_a,
+                                                                const int8_t* __restrict__ w,
+                                                                const float* __restrict__ s_w,
+                                                                float* __restrict__ y,
+                                                                int32_t* __restrict__ acc_out, int M, int N,
+                                                                int K, int G) {
+  small_gemm<MB, CB, W4, WAVES, U>(q, s_a, w, s_w, y, acc_out, M, N, K, G);
+}
+
+// Quantize + W8A8 GEMM of MR = 2, 3 or 4 rows in one launch, with no
+// exchange between workgroups: every workgroup quantizes all MR rows itself
+// (the rows are short next to its share of the weights) and keeps the codes
+// in LDS, as the single-row fused kernel does.  Order of work: the rows of x
+// are loaded (CPT float4 of each row per thread, all in flight at once),
+// then the first batch of weights is requested; the row absmax and
+// finiteness are reduced over the workgroup, and the codes are written to
+// LDS with the quantizer's arithmetic (quant_math.h) while those weights
+// are in flight.
+// Workgroup 0 also writes the codes and scales to q and s_a, which then hold
+// what prism_quantize_rows would write.  The GEMM body then reads the
+// activation fragments from LDS.  K <= 4 * 512 * CPT.
+// Rows x K up to 30720 (15 float4 per thread): past that the workgroups spend
+// longer quantizing than the separate quantizer launch costs (MI355X,
+// N x K = 2560 x 9728: M = 3 takes 12.4 us in one kernel against 13.0 in
+// two launches, M = 4 took 14.3 against 13.2).
+constexpr int kFusedFloat4PerThread = 15;
+template <int MR>
+constexpr int fused_k_max() {
+  return 4 * 512 * (kFusedFloat4PerThread / MR);
+}
+
+template <int MR, int CB, int U>
+__global__ __launch_bounds__(512) void quantize_gemm_small_kernel(const float* __restrict__ x,
+                                                                  int8_t* __restrict__ q_out,
+                                                                  float* __restrict__ s_out,
+                                                                  const int8_t* __restrict__ w,
+                                                                  const float* __restrict__ s_w,
+                                                                  float* __restrict__ y,
+                                                                  int32_t* __restrict__ acc_out, int N, int K,
+                                                                  int G) {
+  constexpr int WAVES = 8, NT = 512;
+  constexpr int CPT = kFusedFloat4PerThread / MR;
+  constexpr int KMAX = fused_k_max<MR>();
+  __shared__ __attribute__((aligned(16))) int8_t codes[MR * (KMAX + 16)];
+  __shared__ float scales[MR];
+  __shared__ float rmax[MR][WAVES];
+  __shared__ int rfin[MR][WAVES];
+  const int stride = K + 16;  // LDS row stride of the codes (K % 16 == 0)
+  const int n4 = K / 4;
+  const float4* x4 = reinterpret_cast<const float4*>(x);
+  float4 v[MR][CPT];
+
+  float amax[MR];
+  bool finite[MR];
+  // The rows are loaded and this thread's absmax taken before any weight is
+  // requested: issued after the weights, the row loads would queue in HBM
+  // behind the whole weight stream (every workgroup requests its first
+  // batch at once), several microseconds.
+  auto load_rows = [&]() {
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int c = threadIdx.x + NT * i;
+        if (c < n4) v[m][i] = x4[(size_t)m * (size_t)n4 + (size_t)c];
+      }
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      amax[m] = 0.0f;
+      finite[m] = true;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        if (threadIdx.x + NT * i < n4) {
+          amax[m] = fmaxf(amax[m], quant::absmax4(v[m][i]));
+          finite[m] = finite[m] && quant::finite4(v[m][i]);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto quantize = [&]() {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const float a = quant::wave_max(amax[m]);
+      const bool f = __all(finite[m]);
+      if (lane == 0) {
+        rmax[m][wave] = a;
+        rfin[m][wave] = f ? 1 : 0;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      float amax = rmax[m][0];
+      int fin = rfin[m][0];
+#pragma unroll
+      for (int i = 1; i < WAVES; ++i) {
+        amax = fmaxf(amax, rmax[m][i]);
+        fin &= rfin[m][i];
+      }
+      const float sc = quant::row_scale(amax, fin != 0);
+      const bool zero = fin == 0 || sc == 0.0f;
+      const float rc = zero ? 0.0f : quant::fast_recip(sc);
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int c = threadIdx.x + NT * i;
+        if (c < n4) {
+          const uint32_t code = zero ? 0u : quant::pack4(v[m][i], sc, rc);
+          *reinterpret_cast<uint32_t*>(codes + m * stride + 4 * c) = code;
+          if (blockIdx.x == 0) reinterpret_cast<uint32_t*>(q_out)[(size_t)m * (size_t)n4 + (size_t)c] = code;
+        }
+      }
+      if (threadIdx.x == 0) {
+        scales[m] = sc;
+        if (blockIdx.x == 0) s_out[m] = sc;
+      }
+    }
+    __syncthreads();
+  };
+  small_gemm<1, CB, false, WAVES, U, true>(codes, scales, w, s_w, y, acc_out, MR, N, K, G, load_rows, quantize,
+                                           stride);
 }
 
 // G > 0: G workgroups with even shares of the N columns (each share at most
@@ -700,6 +881,34 @@ int launch_gemm_small(const int8_t* q, const float* s_a, const void* w, bool w_i
 bool launch_quantize_gemv(const float* x, int8_t* q, float* s_a, const int8_t* w, const float* s_w, float* y,
                           int32_t* acc, int N, int K, hipStream_t st) {
   return launch_gemv(x, q, s_a, nullptr, nullptr, w, s_w, y, acc, N, K, st);
+}
+
+bool launch_quantize_gemm_small(const float* x, int8_t* q, float* s_a, const int8_t* w, const float* s_w, float* y,
+                                int32_t* acc, int M, int N, int K, hipStream_t st) {
+  if (M < 2 || M > kFusedSmallMMax || N > 16384) return false;
+  if (K > (M == 2 ? fused_k_max<2>() : M == 3 ? fused_k_max<3>() : fused_k_max<4>())) return false;
+  // One even share of the columns per workgroup, at most one workgroup per
+  // CU (as launch_gemm_small_balanced).
+  const int G = N < 256 ? N : 256;
+  const int cb = ((N + G - 1) / G + 15) / 16;
+  // A first batch of two units instead of four for rows up to 4096 (each
+  // wave's share of K is then at most four units): the waves that quantize
+  // are held up less by their own weight requests (MI355X, N x K = 9728 x
+  // 2560, M = 2: 9.8 -> 9.1 us; at K = 9728 four units stay faster).
+  const bool u2 = K <= 4096 || cb == 4;
+#define PRISM_FUSED(MR, CB)                                                                                    \
+  if (M == MR && cb == CB) {                                                                                   \
+    if (u2)                                                                                                    \
+      quantize_gemm_small_kernel<MR, CB, 2><<<(unsigned)G, 512, 0, st>>>(x, q, s_a, w, s_w, y, acc, N, K, G);  \
+    else                                                                                                       \
+      quantize_gemm_small_kernel<MR, CB, 4><<<(unsigned)G, 512, 0, st>>>(x, q, s_a, w, s_w, y, acc, N, K, G);  \
+    return true;                                                                                               \
+  }
+  PRISM_FUSED(2, 1) PRISM_FUSED(2, 2) PRISM_FUSED(2, 3) PRISM_FUSED(2, 4)
+  PRISM_FUSED(3, 1) PRISM_FUSED(3, 2) PRISM_FUSED(3, 3) PRISM_FUSED(3, 4)
+  PRISM_FUSED(4, 1) PRISM_FUSED(4, 2) PRISM_FUSED(4, 3) PRISM_FUSED(4, 4)
+#undef PRISM_FUSED
+  return false;
 }
 
 }  // namespace prism

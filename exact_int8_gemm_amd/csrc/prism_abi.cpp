@@ -218,6 +218,9 @@ int prism_quantize_gemm_w8a8(const float* x, int8_t* q, float* scale, const int8
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (M == 1 && prism::launch_quantize_gemv(x, q, scale, w, s_w, y, acc, (int)N, (int)K, s))
     return prism::launch_status();
+  if (M <= prism::kFusedSmallMMax &&
+      prism::launch_quantize_gemm_small(x, q, scale, w, s_w, y, acc, (int)M, (int)N, (int)K, s))
+    return prism::launch_status();
   if ((st = prism::launch_quantize_rows(x, q, scale, M, K, s)) != PRISM_OK) return st;
   if (use_small(M, K, false))
     return prism::launch_gemm_small(q, scale, w, false, s_w, y, acc, (int)M, (int)N, (int)K, s);

@@ -57,6 +57,14 @@ int launch_gemm_small(const int8_t* q, const float* s_a, const void* w, bool w_i
 // K is too long for it.
 bool launch_quantize_gemv(const float* x, int8_t* q, float* s_a, const int8_t* w, const float* s_w, float* y,
                           int32_t* acc, int N, int K, hipStream_t st);
+// 2 <= M <= kFusedSmallMMax rows, N up to 16384, int8 weights: quantize x and
+// multiply in one kernel (every workgroup quantizes the rows into LDS, also
+// writing the codes to q and the scales to s_a).  False (nothing launched)
+// when the shape is outside its range (K up to 14336 for 2 rows, 10240 for
+// 3, 6144 for 4).
+constexpr int kFusedSmallMMax = 4;
+bool launch_quantize_gemm_small(const float* x, int8_t* q, float* s_a, const int8_t* w, const float* s_w, float* y,
+                                int32_t* acc, int M, int N, int K, hipStream_t st);
 
 int launch_gemm_tiled(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
                       float* y, int32_t* acc, int M, int N, int K, hipStream_t st);

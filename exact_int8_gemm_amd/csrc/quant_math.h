@@ -48,22 +48,29 @@ __device__ inline int code_fast(float x, float s, float r) {
 // code takes the division).
 __device__ inline float fast_recip(float s) { return (s >= 0x1p-126f && s <= 0x1p126f) ? 1.0f / s : 0.0f; }
 
-// Four codes packed little-endian into one dword; r = fast_recip(s).
+// Four codes packed little-endian into one dword; r = fast_recip(s).  The
+// four codes come from code_fast's multiplication unless one of them lies
+// next to a rounding tie (or r == 0): then all four take the division, in a
+// branch that is rarely entered (as one branch for the four, rather than one
+// per element, it stays a branch instead of being computed for every
+// element and selected).
 __device__ inline uint32_t pack4(const float4 v, float s, float r) {
-  int c0, c1, c2, c3;
-  if (r != 0.0f) {
-    c0 = code_fast(v.x, s, r);
-    c1 = code_fast(v.y, s, r);
-    c2 = code_fast(v.z, s, r);
-    c3 = code_fast(v.w, s, r);
-  } else {
-    c0 = code_of(v.x, s);
-    c1 = code_of(v.y, s);
-    c2 = code_of(v.z, s);
-    c3 = code_of(v.w, s);
+  const float xs[4] = {v.x, v.y, v.z, v.w};
+  int c[4];
+  bool exact = r == 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float t = xs[e] * r;
+    const float n = rintf(t);
+    exact = exact || !(fabsf(t - n) < 0.5f - 0x1p-15f);
+    c[e] = (int)fminf(fmaxf(n, -127.0f), 127.0f);
   }
-  return (uint32_t)(c0 & 0xff) | ((uint32_t)(c1 & 0xff) << 8) | ((uint32_t)(c2 & 0xff) << 16) |
-         ((uint32_t)(c3 & 0xff) << 24);
+  if (__builtin_expect(exact, 0)) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c[e] = code_of(xs[e], s);
+  }
+  return (uint32_t)(c[0] & 0xff) | ((uint32_t)(c[1] & 0xff) << 8) | ((uint32_t)(c[2] & 0xff) << 16) |
+         ((uint32_t)(c[3] & 0xff) << 24);
 }
 
 __device__ inline bool finite4(const float4 v) {

@@ -263,7 +263,8 @@ def gemm_w4a8_variant(q, s_a, w4, s_w, variant, y=None, acc=None):
 def quantize_gemm_w8a8(x, w, s_w, y=None, q=None, scale=None, acc=None):
     """Quantize x f32 [M,K] per row and multiply by int8 w [N,K] with s_w f32 [N] in one call:
     the bits of ``quantize_rows`` then ``gemm_w8a8``.  Returns (y, q, scale); q and scale are
-    the quantizer's outputs.  M = 1 (decode) runs as one kernel."""
+    the quantizer's outputs.  M = 1 (decode) and M = 2..4 with N <= 16384 and K up to
+    14336 / 10240 / 6144 run as one kernel."""
     dev = _gpu(x, "x")
     if x.dim() != 2:
         raise ValueError("x must be 2-D")

@@ -190,10 +190,12 @@ int prism_gemm_w8a8_blockscale(const int8_t* q, const float* s_a, const int8_t* 
  *         writes for x.
  *   w, s_w, y, acc: as for prism_gemm_w8a8 (acc may be NULL).
  * The results are those of prism_quantize_rows(x) followed by
- * prism_gemm_w8a8 on its outputs, bit for bit.  With M = 1 and K <= 16384
- * this is one kernel that quantizes the row on chip while the first weight
- * rows stream in (decode); otherwise the two steps run as two launches on
- * `stream`.  K must be a multiple of 16.
+ * prism_gemm_w8a8 on its outputs, bit for bit.  With M = 1 and K <= 16384,
+ * and with M = 2, 3 or 4 rows, N <= 16384 and K up to 14336, 10240 or 6144
+ * respectively, this is one kernel in which every workgroup quantizes the
+ * rows on chip while its first weight rows stream in (decode); otherwise
+ * the two steps run as two launches on `stream`.  Either way it allocates
+ * nothing.  K must be a multiple of 16.
  */
 int prism_quantize_gemm_w8a8(const float* x, int8_t* q, float* scale, const int8_t* w, const float* s_w,
                              float* y, int32_t* acc, int64_t M, int64_t N, int64_t K, void* stream);

@@ -390,6 +390,90 @@ def test_quantize_gemm_several_rows(M, N, K):
     assert_same_floats(host(y), y_ref, "y")
 
 
+_FUSED_KINDS = ["normal", "zero", "nan", "inf", "tiny", "huge", "ties"]
+
+
+def _fused_rows(M, K, seed):
+    """M >= 2 rows: a zero row first, a NaN row last, and between them rows cycling
+    through the quantizer's other cases (ordinary, inf, tiny and huge scales, rounding ties)."""
+    rng = np.random.default_rng(seed)
+    kinds = ["zero"] + [_FUSED_KINDS[(m + seed) % len(_FUSED_KINDS)] for m in range(1, M - 1)] + ["nan"]
+    return np.stack([_special_row(k, K, rng) for k in kinds])
+
+
+@pytest.mark.parametrize("M", [2, 3, 4, 7, 16])
+@pytest.mark.parametrize("N,K", [(9728, 2560), (2560, 9728), (300, 1040), (3, 16), (5, 2064), (16384, 6144),
+                                 (257, 10240), (1000, 14336), (16384, 32), (16400, 1024)])
+def test_quantize_gemm_few_rows(M, N, K):
+    """2..16 rows through the one call: M = 2, 3, 4 as one kernel in which every workgroup
+    quantizes the rows itself (the projection shapes, ragged N and K, N < M, the largest N
+    and K), more rows or N > 16384 as two launches.  Codes, scales, acc and y equal the
+    oracle's quantize-then-GEMM and the library's two separate calls, bit for bit, with zero
+    and NaN rows among them."""
+    rng = np.random.default_rng(M * 7919 + N + K)
+    x = _fused_rows(M, K, M + N + K)
+    w = rng.integers(-128, 128, (N, K), dtype=np.int8)
+    s_w = wl.channel_scales(rng, N)
+    q_ref, s_ref = oracle.quantize_rows(x)
+    y_ref, acc_ref = oracle.gemm_w8a8(q_ref, s_ref, w, s_w)
+    xd, wd, swd = dev(x), dev(w), dev(s_w)
+    acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    y, q, s = prism.quantize_gemm_w8a8(xd, wd, swd, acc=acc)
+    q2, s2 = prism.quantize_rows(xd)
+    y2 = prism.gemm_w8a8(q2, s2, wd, swd)
+    torch.cuda.synchronize()
+    assert np.isnan(s_ref).any() and (s_ref == 0).any()
+    assert_same_ints(host(q), q_ref, "q")
+    assert_same_floats(host(s), s_ref, "scale")
+    assert_same_ints(host(acc), acc_ref, "acc")
+    assert_same_floats(host(y), y_ref, "y")
+    assert_same_floats(host(y), host(y2), "y against the two-call path")
+
+
+@pytest.mark.parametrize("M,K", [(2, 14336), (2, 14352), (3, 10240), (3, 10256), (4, 6144), (4, 6160)])
+def test_quantize_gemm_few_rows_at_the_one_kernel_k_limit(M, K):
+    """The longest rows the one-kernel form takes for 2, 3 and 4 rows, and 16 more (two
+    launches): bit-exact against the oracle either way."""
+    N = 700
+    rng = np.random.default_rng(M + K)
+    x = _fused_rows(M, K, K)
+    w = rng.integers(-128, 128, (N, K), dtype=np.int8)
+    s_w = wl.channel_scales(rng, N)
+    q_ref, s_ref = oracle.quantize_rows(x)
+    y_ref, acc_ref = oracle.gemm_w8a8(q_ref, s_ref, w, s_w)
+    acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    y, q, s = prism.quantize_gemm_w8a8(dev(x), dev(w), dev(s_w), acc=acc)
+    torch.cuda.synchronize()
+    assert_same_ints(host(q), q_ref, "q")
+    assert_same_floats(host(s), s_ref, "scale")
+    assert_same_ints(host(acc), acc_ref, "acc")
+    assert_same_floats(host(y), y_ref, "y")
+
+
+def test_quantize_gemm_few_rows_back_to_back_and_two_streams():
+    """Calls of different row counts in a row on one stream, then the same calls on a second
+    stream while the first one runs them too: all equal the oracle bit for bit."""
+    N, K = 2560, 9728
+    rng = np.random.default_rng(5)
+    w = rng.integers(-128, 128, (N, K), dtype=np.int8)
+    s_w = wl.channel_scales(rng, N)
+    wd, swd = dev(w), dev(s_w)
+    cases = [(M, _fused_rows(M, K, 40 + M)) for M in (4, 2, 9, 16, 3)]
+    refs = [oracle.gemm_w8a8(*oracle.quantize_rows(x), w, s_w)[0] for _, x in cases]
+    outs = [prism.quantize_gemm_w8a8(dev(x), wd, swd)[0] for _, x in cases]
+    side = torch.cuda.Stream(device=DEV)
+    xs = [dev(x) for _, x in cases]
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        outs_side = [prism.quantize_gemm_w8a8(x, wd, swd)[0] for x in xs]
+    outs_main = [prism.quantize_gemm_w8a8(x, wd, swd)[0] for x in xs]
+    torch.cuda.synchronize()
+    for i, ref in enumerate(refs):
+        assert_same_floats(host(outs[i]), ref, "call %d" % i)
+        assert_same_floats(host(outs_side[i]), ref, "side stream, call %d" % i)
+        assert_same_floats(host(outs_main[i]), ref, "main stream beside it, call %d" % i)
+
+
 def test_full_int8_range_and_largest_k():
     """-128 codes and weights (valid inputs, though the quantizer never makes -128)
     and the largest accepted K: the exact sums reach K * 16384 < 2^31."""

@@ -46,7 +46,7 @@ def _args():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 256 MiB device copy three times (scale for HBM byte counters)")
     ap.add_argument("--only", default=None, help="run only one kernel measurement (for profiling): "
-                    "step | proj | w4a8 | block | repack | q4k | decode | vendor | stress | sweep (M sweep, not in the default run)")
+                    "step | proj | w4a8 | block | repack | q4k | decode | vendor | stress | peaks | sweep (M sweep, not in the default run)")
     return ap.parse_args()
 
 
@@ -478,6 +478,34 @@ def kernels(torch, prism, wl, only=None):
             except RuntimeError as e:   # not every torch build exposes an int8 GEMM
                 out["vendor_int_mm_" + name] = dict(error=str(e)[:120])
             del wts
+    if only in (None, "peaks"):
+        # What this GPU reaches on the two resources, with the library's own
+        # measurement kernels: int8 MFMA on registers (no memory traffic) at 1,
+        # 2 and 4 waves per SIMD, and a plain once-through read of 25.2 MB
+        # (the size of one projection's int8 weights; copies rotated so that
+        # nothing is cached) and of 1 GiB.
+        ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+        peaks = {}
+        for wps in (1, 2, 4):
+            iters = 8192 // wps
+            outp = torch.empty((2 * ncu * 128 * wps,), dtype=torch.int32, device=dev)
+            f = L.lib.prism_peak_mfma
+            args = (iters, wps, 1, L.p(outp), L.stream)
+            t1, t = _time_launches(torch, [lambda: f(*args)], 5)
+            ops = 2 * ncu * 2 * wps * iters * 16 * 65536
+            peaks["mfma_i8_%dw_per_simd" % wps] = dict(us=t * 1e6, tops=ops / t / 1e12,
+                                                       mfma_frac=ops / t / 1e12 / PEAK_INT8_TOPS)
+        parts = torch.empty((4096,), dtype=torch.int32, device=dev)
+        for name, nbytes in (("read_25.2MB", 9728 * 2560), ("read_1GiB", 1 << 30)):
+            R = _copies(nbytes)
+            bufs = [torch.empty((nbytes,), dtype=torch.uint8, device=dev).fill_(i) for i in range(R)]
+            f = L.lib.prism_peak_read
+            fns = [(lambda b=b: f(L.p(b), nbytes, L.p(parts), L.stream)) for b in bufs]
+            t1, t = _time_launches(torch, fns, max(10, 2 * R))
+            peaks[name] = dict(us=t * 1e6, gbs=nbytes / t / 1e9, hbm_frac=nbytes / t / 1e9 / PEAK_HBM_GBS,
+                               us_single_launch=t1 * 1e6, gbs_single_launch=nbytes / t1 / 1e9, copies=R)
+            del bufs
+        out["peaks"] = peaks
     if only == "sweep":
         # Not in the default run: the per-channel W8A8 GEMM across M at
         # N = K = 5120 (the plain call's own kernel choice at each M), next to

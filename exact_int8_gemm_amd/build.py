@@ -24,7 +24,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libprism.so")
 
-SOURCES = ["quantize.hip", "gemm_small.hip", "gemm_tiled.hip", "repack.hip", "prism_abi.cpp"]
+SOURCES = ["quantize.hip", "gemm_small.hip", "gemm_tiled.hip", "repack.hip", "peaks.hip", "prism_abi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -276,4 +276,21 @@ int prism_gemm_w8a8_blockscale(const int8_t* q, const float* s_a, const int8_t* 
                                        static_cast<hipStream_t>(stream));
 }
 
+int prism_peak_mfma(int64_t iters, int waves_per_simd, int seed, uint32_t* out, void* stream) {
+  if (iters < 1 || iters > (1 << 24) || seed < 0 || seed > (1 << 20) || !out) return PRISM_ERR_INVALID_ARG;
+  if (waves_per_simd != 1 && waves_per_simd != 2 && waves_per_simd != 4) return PRISM_ERR_INVALID_ARG;
+  if (!aligned(out, 4)) return PRISM_ERR_ALIGNMENT;
+  int st = check_device();
+  if (st != PRISM_OK) return st;
+  return prism::launch_peak_mfma(iters, waves_per_simd, seed, out, static_cast<hipStream_t>(stream));
+}
+
+int prism_peak_read(const void* buf, int64_t bytes, uint32_t* parts, void* stream) {
+  if (!buf || !parts || bytes <= 0 || bytes > ((int64_t)1 << 40)) return PRISM_ERR_INVALID_ARG;
+  if (bytes % 16 != 0 || !aligned(buf, 16) || !aligned(parts, 4)) return PRISM_ERR_ALIGNMENT;
+  int st = check_device();
+  if (st != PRISM_OK) return st;
+  return prism::launch_peak_read(buf, bytes, parts, PRISM_PEAK_READ_PARTS, static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

@@ -82,6 +82,10 @@ int launch_gemm_tiled_variant(const int8_t* q, const float* s_a, const void* w, 
 int launch_gemm_blockscale(const int8_t* q, const float* s_a, const int8_t* w, const uint16_t* d, float* y,
                            int32_t* partials, int M, int N, int K, hipStream_t st);
 
+// Measurement kernels (peaks.hip).
+int launch_peak_mfma(int64_t iters, int waves_per_simd, int seed, uint32_t* out, hipStream_t st);
+int launch_peak_read(const void* buf, int64_t bytes, uint32_t* parts, int nparts, hipStream_t st);
+
 // Status of the most recent launch on this thread.
 int launch_status();
 

@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libprism.so")
 
 PRISM_OK = 0
-ABI_VERSION = 11
+ABI_VERSION = 12
 K_MAX = 131040
 
 # Dispatch-table entries of the W8A8 / W4A8 calls (PRISM_VARIANT_* in include/prism.h).
@@ -68,6 +68,10 @@ def _declare(lib):
         fn = getattr(lib, name)
         fn.restype = i32
         fn.argtypes = [p, p, p, p, p, p, i64, i64, i64, p]
+    lib.prism_peak_mfma.restype = i32
+    lib.prism_peak_mfma.argtypes = [i64, i32, i32, p, p]
+    lib.prism_peak_read.restype = i32
+    lib.prism_peak_read.argtypes = [p, i64, p, p]
     return lib
 
 
@@ -311,3 +315,34 @@ def gemm_w8a8_blockscale(q, s_a, w, d, y=None, partials=None):
         _check(lib().prism_gemm_w8a8_blockscale(_ptr(q), _ptr(s_a), _ptr(w), _ptr(d), _ptr(y), _ptr(partials),
                                                 M, N, K, _stream(dev)))
     return y
+
+
+# ------------------------------------------------------------ measurement kernels
+
+PEAK_READ_PARTS = 4096
+
+
+def peak_mfma(iters, waves_per_simd, seed=0, out=None, device=None):
+    """Run the MFMA throughput kernel (int8 32x32x32 on registers, no memory traffic):
+    2 x CUs workgroups of 2 x waves_per_simd waves, iters x 16 MFMAs per wave.  Returns
+    the per-thread checksums (uint32 as int32 [2 * CUs * 128 * waves_per_simd])."""
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    n = 2 * torch.cuda.get_device_properties(dev).multi_processor_count * 128 * waves_per_simd
+    out = torch.empty((n,), dtype=torch.int32, device=dev) if out is None else _need(out, "out", torch.int32, (n,), dev)
+    with torch.cuda.device(dev):
+        _check(lib().prism_peak_mfma(iters, waves_per_simd, seed, _ptr(out), _stream(dev)))
+    return out
+
+
+def peak_read(buf, parts=None):
+    """Read the bytes of the contiguous CUDA tensor ``buf`` once (16-byte loads); returns
+    parts (int32 [PEAK_READ_PARTS]) whose XOR is the XOR of the buffer's 32-bit words."""
+    dev = _gpu(buf, "buf")
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    nbytes = buf.numel() * buf.element_size()
+    parts = (torch.empty((PEAK_READ_PARTS,), dtype=torch.int32, device=dev) if parts is None
+             else _need(parts, "parts", torch.int32, (PEAK_READ_PARTS,), dev))
+    with torch.cuda.device(dev):
+        _check(lib().prism_peak_read(_ptr(buf), nbytes, _ptr(parts), _stream(dev)))
+    return parts

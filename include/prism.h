@@ -42,7 +42,7 @@ extern "C" {
 #endif
 
 /* Bumped on any change of a signature or of the semantics below. */
-#define PRISM_ABI_VERSION 11
+#define PRISM_ABI_VERSION 12
 
 /* Largest accepted K.  For K <= 131040 every exact sum of K products of two
  * int8 values (|q|, |w| <= 128) lies strictly inside the int32 range. */
@@ -271,6 +271,33 @@ int prism_gemm_w8a8_variant(const int8_t* q, const float* s_a, const int8_t* w, 
 int prism_gemm_w4a8_variant(const int8_t* q, const float* s_a, const uint8_t* w4, const float* s_w,
                             float* y, int32_t* acc, int64_t M, int64_t N, int64_t K, int variant,
                             void* stream);
+
+/*
+ * Measurement kernels (not part of the GEMM path): what this GPU reaches on
+ * the two resources the GEMMs are bound by, for the roofline figures.
+ *
+ * prism_peak_mfma: 2 x (compute units) workgroups, each of 2 x
+ * waves_per_simd waves (waves_per_simd in {1, 2, 4}), every wave running
+ * iters x 16 v_mfma_i32_32x32x32_i8 on register operands: iters x 16 x 65536
+ * integer ops per wave.  out [2 x CUs x 128 x waves_per_simd] uint32 gets
+ * one checksum per thread: the sum modulo 2^32 of the thread's NACC x 16
+ * accumulator registers after 16 / NACC steps per iteration on NACC
+ * accumulators (NACC = 8, or 4 for waves_per_simd = 4) that alternate the
+ * operand pairs (A0, B0) and (A1, B1).  Byte j (0..15) of the fragment of
+ * operand s (A0, B0, A1, B1 = 0, 1, 2, 3) in lane l is the top byte of
+ * (37 l + 101 j + 7919 s + 13 seed) * 2654435761 modulo 2^32, as int8.
+ * iters in [1, 2^24], seed in [0, 2^20]; accumulators wrap past 2^31 for
+ * large iters (the checksum is then only a data dependence).
+ *
+ * prism_peak_read: reads `bytes` (a multiple of 16, at most 2^40) of `buf`
+ * (16-byte aligned) once with 16-byte loads and writes the XOR of the
+ * 32-bit words each workgroup read to parts[workgroup]; all
+ * PRISM_PEAK_READ_PARTS entries of parts are written (unused ones 0), so the
+ * XOR of parts is the XOR of every 32-bit word of the buffer.
+ */
+#define PRISM_PEAK_READ_PARTS 4096
+int prism_peak_mfma(int64_t iters, int waves_per_simd, int seed, uint32_t* out, void* stream);
+int prism_peak_read(const void* buf, int64_t bytes, uint32_t* parts, void* stream);
 
 #ifdef __cplusplus
 }

@@ -45,7 +45,7 @@ def test_header_declares_every_call():
     assert {"prism_quantize_rows", "prism_quantize_rows_static", "prism_repack_q8_0", "prism_gemm_w8a8",
             "prism_gemm_w8a8_blockscale", "prism_gemm_w4a8", "prism_gemm_w8a8_variant", "prism_gemm_w4a8_variant",
             "prism_repack_q4_k", "prism_gemm_w4a8_q4k", "prism_quantize_gemm_w8a8",
-            "prism_abi_version", "prism_build_id", "prism_status_string"} <= names
+            "prism_peak_mfma", "prism_peak_read", "prism_abi_version", "prism_build_id", "prism_status_string"} <= names
 
 
 def test_library_exports_every_declared_symbol(built):
@@ -99,6 +99,10 @@ for n in ("prism_gemm_w8a8_variant", "prism_gemm_w4a8_variant"):
 for n in ("prism_gemm_w8a8", "prism_gemm_w8a8_blockscale", "prism_gemm_w4a8"):
     getattr(lib, n).restype = i32
     getattr(lib, n).argtypes = [p, p, p, p, p, p, i64, i64, i64, p]
+lib.prism_peak_mfma.restype = i32
+lib.prism_peak_mfma.argtypes = [i64, i32, i32, p, p]
+lib.prism_peak_read.restype = i32
+lib.prism_peak_read.argtypes = [p, i64, p, p]
 A = 0x7f0000000000          # 256-byte aligned fake address, never dereferenced
 res = {"version": lib.prism_abi_version(),
        "strings": {str(s): lib.prism_status_string(s).decode() for s in (0, -1, -2, -3, -4, 7)}}
@@ -281,6 +285,23 @@ for fn, kmul in (("prism_gemm_w8a8", 16), ("prism_gemm_w4a8", 32), ("prism_gemm_
     ]
     if kmul == 32:
         CASES.append((fn, _g(K=48), ALIGN))
+CASES += [
+    ("prism_peak_mfma", [0, 2, 0, A, None], INVALID),            # iters >= 1
+    ("prism_peak_mfma", [(1 << 24) + 1, 2, 0, A, None], INVALID),
+    ("prism_peak_mfma", [10, 3, 0, A, None], INVALID),           # waves per SIMD in {1, 2, 4}
+    ("prism_peak_mfma", [10, 0, 0, A, None], INVALID),
+    ("prism_peak_mfma", [10, 2, -1, A, None], INVALID),
+    ("prism_peak_mfma", [10, 2, 0, None, None], INVALID),
+    ("prism_peak_mfma", [10, 2, 0, A + 2, None], ALIGN),
+    ("prism_peak_read", [A, 0, A, None], INVALID),
+    ("prism_peak_read", [A, -16, A, None], INVALID),
+    ("prism_peak_read", [None, 64, A, None], INVALID),
+    ("prism_peak_read", [A, 64, None, None], INVALID),
+    ("prism_peak_read", [A, (1 << 40) + 16, A, None], INVALID),
+    ("prism_peak_read", [A, 40, A, None], ALIGN),                # bytes % 16
+    ("prism_peak_read", [A + 8, 64, A, None], ALIGN),
+    ("prism_peak_read", [A, 64, A + 1, None], ALIGN),
+]
 CASES.append(("prism_gemm_w8a8", _g(sw=A + 2), ALIGN))
 CASES.append(("prism_gemm_w4a8", _g(sw=A + 1), ALIGN))
 CASES.append(("prism_gemm_w8a8_blockscale", _g(sw=A + 1), ALIGN))   # d is 2-byte data

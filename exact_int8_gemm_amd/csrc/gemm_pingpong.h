@@ -69,17 +69,38 @@ __device__ inline void pp_barrier() { asm volatile("s_barrier" ::: "memory"); }
 // s_waitcnt lgkmcnt(0), no wait on vmcnt or expcnt (gfx9 encoding).
 __device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-template <int BK, int BN = 256, int KSP = 2>
+// W4: w holds packed signed 4-bit weights [N][K/2] (low nibble = even k).
+// Their bytes are copied to LDS as they are and unpacked at fragment read:
+// each nibble moves to the top half of a byte, which as int8 is 16 w, so the
+// MFMAs sum 16 acc exactly and the epilogue shifts it back.  A stage of
+// 128 k holds only 64 packed bytes of a weight row, and 64-byte row pieces
+// copy much slower than 128-byte ones, so B moves in pairs of stages (256 k,
+// 128 bytes per row) through a ring of two pair buffers after the A ring:
+// every stage copies one half of the pair after the one being read (the
+// BN / 64 copies per wave of a pair split as evenly as they go: stage 0 of
+// a pair copies the larger half), with a cursor of its own, and stages are
+// padded to whole pairs of pairs so that each tile starts in pair buffer 0.
+template <int BK, int BN = 256, int KSP = 2, bool W4 = false>
 __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restrict__ q, const float* __restrict__ s_a,
                                                         const int8_t* __restrict__ w, const float* __restrict__ s_w,
                                                         float* __restrict__ y, int32_t* __restrict__ acc_out, int M,
                                                         int N, int K, int tiles_m, int tiles_n) {
   constexpr int BM = 256, RING = 2;
-  using C = Cfg<BM, BN, BK, 4, 2, RING>;
+  using C = Cfg<BM, BN, BK, 4, 2, RING>;  // copies and LDS rows of A and B (W4: BK bytes of a pair's row)
+  constexpr int kPerWaveA = C::kPerWaveA;
+  constexpr int kPerWaveB = C::kPerWaveB;       // int8: per stage; W4: per pair
+  constexpr int kPerWave = kPerWaveA + kPerWaveB;
+  constexpr int kHalf0 = (kPerWaveB + 1) / 2;   // W4: copies per wave of the first half of a pair
+  constexpr int kHalf1 = kPerWaveB / 2;
+  constexpr int kStage = W4 ? BM * BK : (BM + BN) * BK;  // a stage of the ring (W4: A only)
+  constexpr int kPair = BN * BK;                         // W4: a pair buffer
+  constexpr int kLds = RING * kStage + (W4 ? 2 * kPair : 0);
   constexpr int P = BK / (32 * KSP);  // read/compute phase pairs per stage (KSP 32-k steps each)
   constexpr int TM = 2, TN = BN / 64;
-  static_assert(C::kNW == 8 && C::kPerWaveA * 8 == C::kCopiesA, "eight waves");
-  __shared__ __attribute__((aligned(1024))) int8_t lds[RING * C::kStage];
+  static_assert(C::kNW == 8 && C::kPerWaveA * 8 == C::kCopiesA && C::kPerWaveB * 8 == C::kCopiesB, "eight waves");
+  static_assert(!W4 || BK == 128, "W4: 128-k stages");
+  static_assert(kLds <= 160 * 1024, "LDS exceeds 160 KiB");
+  __shared__ __attribute__((aligned(1024))) int8_t lds[kLds];
   __shared__ float sa_l[BM], sw_l[BN];
 
   // This workgroup's tiles: t, t + g, ... below t_end.
@@ -95,24 +116,37 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = wave >> 2, wm = wave & 3;
   const int nk = (K + BK - 1) / BK;
-  const int nkr = (nk + RING - 1) / RING * RING;  // padded stages read zeros
+  const int nkr = W4 ? (nk + 3) / 4 * 4 : (nk + RING - 1) / RING * RING;  // padded stages read zeros
 
-  // The k offset of a lane's chunk (chunk * 16) is recomputed at each issue
-  // from the lane and the copy index instead of being kept per copy: a few
-  // VALU operations in a read phase, against one register per copy.
-  auto chunk_of = [&](int copy) __attribute__((always_inline)) {
+  const int KB = W4 ? K / 2 : K;  // bytes of a weight row
+  // Index of this wave's i-th B copy (W4: the first half of a pair holds
+  // copies 0 .. 8 kHalf0 - 1, the second half the rest).
+  auto b_copy = [&](int i) __attribute__((always_inline)) {
+    if (!W4) return wave * kPerWaveB + i;
+    return i < kHalf0 ? wave * kHalf0 + i : 8 * kHalf0 + wave * kHalf1 + (i - kHalf0);
+  };
+
+  // The byte offset within the stage's k range of a lane's chunk (chunk * 16)
+  // is recomputed at each issue from the lane and the copy index instead of
+  // being kept per copy: a few VALU operations in a read phase, against one
+  // register per copy.
+  auto chunk_a = [&](int copy) __attribute__((always_inline)) {
     return (lane % C::kChunks) ^ C::swz(copy * C::kRowsPerCopy + lane / C::kChunks);
   };
+
   // Byte offset of this lane's chunk in each of its copies at k = 0, relative
   // to the tile's first row.  Rows past M or N lie beyond the tile's buffer
   // bound (below) and read zeros.
-  uint32_t off[C::kPerWave];
+  uint32_t off[kPerWave];
 #pragma unroll
-  for (int s = 0; s < C::kPerWave; ++s) {
-    const bool isA = s < C::kPerWaveA;
-    const int copy = isA ? wave * C::kPerWaveA + s : wave * C::kPerWaveB + (s - C::kPerWaveA);
-    const int row = copy * C::kRowsPerCopy + lane / C::kChunks;
-    off[s] = (uint32_t)(row * K + chunk_of(copy) * 16);
+  for (int s = 0; s < kPerWave; ++s) {
+    if (s < kPerWaveA) {
+      const int copy = wave * kPerWaveA + s;
+      off[s] = (uint32_t)((copy * C::kRowsPerCopy + lane / C::kChunks) * K + chunk_a(copy) * 16);
+    } else {
+      const int copy = b_copy(s - kPerWaveA);
+      off[s] = (uint32_t)((copy * C::kRowsPerCopy + lane / C::kChunks) * KB + chunk_a(copy) * 16);
+    }
   }
   auto sources = [&](int tile, v4i& ra, v4i& rb, int& m0, int& n0) __attribute__((always_inline)) {
     int tm, tn;
@@ -120,7 +154,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
     m0 = tm * BM;
     n0 = tn * BN;
     ra = rsrc_words(q + (size_t)m0 * (size_t)K, (int64_t)(M - m0) * K);
-    rb = rsrc_words(w + (size_t)n0 * (size_t)K, (int64_t)(N - n0) * K);
+    rb = rsrc_words(w + (size_t)n0 * (size_t)KB, (int64_t)(N - n0) * KB);
   };
 
   // Copy cursor: the next stage to copy starts at byte ck of k in the tile
@@ -131,15 +165,43 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
   sources(t, ca, cb, m0, n0);
   int ck = 0;
   bool clive = true, has_next = false;
-  auto issue = [&](int buf) __attribute__((always_inline)) {
+  // W4 pair cursor: the next pair to copy starts at packed byte bk of the
+  // rows of source wb; after a tile's last pair it moves to pair 0 of the
+  // next tile.  Half h of a pair is copied by the stage whose index within
+  // its own pair is h, so the half is known where the copy is issued.
+  v4i wb = cb;
+  int bk = 0;
+  bool blive = true;
+  auto issue_half_pair = [&](int h) __attribute__((always_inline)) {
+    const int s0 = kPerWaveA + (h == 0 ? 0 : kHalf0), s1 = h == 0 ? kPerWaveA + kHalf0 : kPerWave;
 #pragma unroll
-    for (int s = 0; s < C::kPerWave; ++s) {
-      const bool isA = s < C::kPerWaveA;
-      const int copy = isA ? wave * C::kPerWaveA + s : wave * C::kPerWaveB + (s - C::kPerWaveA);
-      const uint32_t o = (clive && ck + chunk_of(copy) * 16 < K) ? off[s] + (uint32_t)ck : kOutOfRange;
-      const int8_t* dst = lds + buf * C::kStage + (isA ? 0 : BM * BK) + copy * 1024;
+    for (int s = s0; s < s1; ++s) {
+      const int copy = b_copy(s - kPerWaveA);
+      const uint32_t o = (blive && bk + chunk_a(copy) * 16 < KB) ? off[s] + (uint32_t)bk : kOutOfRange;
+      const int8_t* dst = lds + RING * kStage + ((bk / BK) & 1) * kPair + copy * 1024;
+      copy_to_lds(wb, lds_addr(dst), o);
+    }
+    if (h == 1) {
+      bk += BK;
+      if (bk >= nkr / 2 * BK) {
+        wb = rbn;
+        bk = 0;
+        blive = has_next;
+      }
+    }
+  };
+  // Copies of the next stage into ring buffer buf (W4: and half h of the
+  // next pair).
+  auto issue = [&](int buf, int h) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < (W4 ? kPerWaveA : kPerWave); ++s) {
+      const bool isA = s < kPerWaveA;
+      const int copy = isA ? wave * kPerWaveA + s : b_copy(s - kPerWaveA);
+      const uint32_t o = (clive && ck + chunk_a(copy) * 16 < K) ? off[s] + (uint32_t)ck : kOutOfRange;
+      const int8_t* dst = lds + buf * kStage + (isA ? 0 : BM * BK) + copy * 1024;
       copy_to_lds(isA ? ca : cb, lds_addr(dst), o);
     }
+    if constexpr (W4) issue_half_pair(h);
     ck += BK;
     if (ck >= nkr * BK) {
       ca = ran;
@@ -153,20 +215,31 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
   const int rl = lane & 31;
   const int sw = C::swz(rl);
   const int arow = (wm * 64 + rl) * BK;
-  const int brow = (BM + grp * (BN / 2) + rl) * BK;
+  const int brow = W4 ? RING * kStage + (grp * (BN / 2) + rl) * BK : (BM + grp * (BN / 2) + rl) * BK;
   v4i af[TM][KSP], bf[TN][KSP];
   // Fragments of the (32 KSP)-k slice `half` of the stage in buffer `buf`:
   // logical chunk 2 (KSP half + ks) + lane / 32 of row (lane % 32) of each
-  // 32-row tile.
-  auto read = [&](int buf, int half) __attribute__((always_inline)) {
-    const int8_t* base = lds + buf * C::kStage;
+  // 32-row tile, i.e. k = 32 (KSP half + ks) + 16 (lane / 32) + [0, 16).
+  // Packed B (stage `buf` of the pair in pair buffer `pb`): the same 16 k are
+  // the 8 bytes at 8 (lane / 32) of logical chunk 4 buf + KSP half + ks of
+  // the pair's 128-byte row.
+  auto read = [&](int buf, int half, int pb) __attribute__((always_inline)) {
+    const int8_t* base = lds + buf * kStage;
 #pragma unroll
     for (int ks = 0; ks < KSP; ++ks) {
       const int c = ((2 * (KSP * half + ks) + (lane >> 5)) ^ sw) * 16;
 #pragma unroll
       for (int i = 0; i < TM; ++i) af[i][ks] = *reinterpret_cast<const v4i*>(base + arow + i * 32 * BK + c);
+      if constexpr (W4) {
+        const int cb4 = ((4 * buf + KSP * half + ks) ^ sw) * 16 + (lane >> 5) * 8;
+        const int8_t* pbase = lds + pb * kPair;
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bf[j][ks] = *reinterpret_cast<const v4i*>(base + brow + j * 32 * BK + c);
+        for (int j = 0; j < TN; ++j)
+          bf[j][ks] = unpack_w4_8(*reinterpret_cast<const v2i*>(pbase + brow + j * 32 * BK + cb4));
+      } else {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bf[j][ks] = *reinterpret_cast<const v4i*>(base + brow + j * 32 * BK + c);
+      }
     }
   };
   auto mma = [&]() __attribute__((always_inline)) {
@@ -179,7 +252,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i][ks], bf[j][ks], acc[i][j], 0, 0, 0);
   };
 
-  issue(0);  // stage 0 of the first tile
+  if constexpr (W4) issue_half_pair(0);  // half 0 of the first tile's pair 0
+  issue(0, 1);                           // stage 0 of the first tile (W4: and half 1 of pair 0)
   while (true) {
     const int t_next = t + g;
     has_next = t_next < t_end;
@@ -199,8 +273,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
 #pragma unroll
         for (int h = 0; h < P; ++h) {
           // read phase of slice h of stage u + r (buffer r)
-          if (h == 0) issue((r + RING - 1) % RING);
-          read(r, h);
+          if (h == 0) issue((r + RING - 1) % RING, r);
+          read(r, h, (u >> 1) & 1);
           wait_lgkm0();
           if (h == P - 1 && grp == 1) wait_vmcnt<0>();
           __builtin_amdgcn_sched_barrier(0);
@@ -240,7 +314,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
         for (int r = 0; r < 16; ++r) {
           const int m = mb + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
           if (m < M) {
-            const int a = acc[i][j][r];
+            const int a = W4 ? acc[i][j][r] >> 4 : acc[i][j][r];  // exact: 16 w sums to a multiple of 16
             const size_t o = (size_t)m * (size_t)N + (size_t)n;
             if (acc_out) __builtin_nontemporal_store(a, acc_out + o);
             const float tv = (float)a * sa_l[m - m0];
@@ -260,14 +334,14 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
 // Number of compute units of the current device (cached per device).
 int device_cus();
 
-template <int BK, int BN = 256, int KSP = 2>
+template <int BK, int BN = 256, int KSP = 2, bool W4 = false>
 void launch_pp(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc, int M,
                int N, int K, hipStream_t st) {
   const int tiles_m = (M + 255) / 256, tiles_n = (N + BN - 1) / BN;
   const int64_t T = (int64_t)tiles_m * tiles_n;
   const int cus = device_cus();
   const unsigned grid = (unsigned)(T < cus ? T : cus);
-  gemm_pp_kernel<BK, BN, KSP><<<grid, 512, 0, st>>>(q, s_a, w, s_w, y, acc, M, N, K, tiles_m, tiles_n);
+  gemm_pp_kernel<BK, BN, KSP, W4><<<grid, 512, 0, st>>>(q, s_a, w, s_w, y, acc, M, N, K, tiles_m, tiles_n);
 }
 
 }  // namespace dma

@@ -147,13 +147,35 @@ void pick_int8(const int8_t* q, const float* s_a, const int8_t* w, const float* 
   }
 }
 
-// 4-bit weights: register-staged pipeline that unpacks the nibbles on their
-// way into LDS; 128 x 128 tiles of 8 waves (32 x 64 each; 4-20% faster than
-// 4 waves of 64 x 64, e.g. M = 256, N = K = 5120: 38.5 -> 30.3 us), with K
-// split (split_int4) when there are fewer tiles than CUs.
-
+// 4-bit weights, two kernels:
+//  * the persistent ping-pong kernel on 256-row tiles with the packed bytes
+//    copied to LDS as they are (256 x 192, 256 x 256 or 256 x 320);
+//  * a register-staged pipeline that unpacks the nibbles on their way into
+//    LDS: 128 x 128 tiles of 8 waves (32 x 64 each; 4-20% faster than 4 waves
+//    of 64 x 64, e.g. M = 256, N = K = 5120: 38.5 -> 30.3 us), two workgroups
+//    per CU, with K split (split_int4) when there are fewer tiles than CUs.
+// Estimate per 256-row round of tiles as for int8 (0.83, 1 and 1.23 for the
+// three widths), against 0.63 per 512 tiles (at least one round) for
+// 128 x 128, from N x K = 12288 x 4096 on MI355X: M = 512: 44.4 us on
+// 128 x 128 against 53.7 on the best 256-row tile; M = 1024: 72.8 -> 58.8 us
+// (256 x 192); 2048: 135 -> 118 (256 x 192); 3072: 201 -> 170-173 (256 x 192
+// or 320); 4096: 260 -> 214 (256 x 256).
 void pick_int4(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc, int M,
                int N, int K, hipStream_t st) {
+  auto rounds = [](int64_t t) { return (double)((t + 255) / 256); };
+  const double pp[3] = {0.83 * rounds(tiles(M, N, 256, 192)), rounds(tiles(M, N, 256, 256)),
+                        1.23 * rounds(tiles(M, N, 256, 320))};
+  const int64_t t128 = tiles(M, N, 128, 128);
+  const double c128 = 0.63 * (t128 > 512 ? (double)t128 / 512.0 : 1.0);
+  int best = 0;
+  for (int i = 1; i < 3; ++i)
+    if (pp[i] < pp[best]) best = i;
+  if (pp[best] < c128) {
+    if (best == 0) tiled::dma::launch_pp<128, 192, 2, true>(q, s_a, w, s_w, y, acc, M, N, K, st);
+    else if (best == 1) tiled::dma::launch_pp<128, 256, 2, true>(q, s_a, w, s_w, y, acc, M, N, K, st);
+    else tiled::dma::launch_pp<128, 320, 1, true>(q, s_a, w, s_w, y, acc, M, N, K, st);
+    return;
+  }
   launch_tiled<128, 128, 128, 4, 2, true, 2>(q, s_a, w, s_w, y, acc, M, N, K, st,
                                               split_int4(tiles(M, N, 128, 128), K));
 }
@@ -163,11 +185,18 @@ void pick_int4(const int8_t* q, const float* s_a, const int8_t* w, const float* 
 // One named entry of the table above (7: 256 x 256, 8: 256 x 128, 9..12:
 // 128 x 128 with K split over 1..4 workgroups, 17: 256 x 192, 18: 256 x 320,
 // 19..22: 64 x 128 with K split over 1..4 workgroups, 23, 24: 128 x 96 with
-// K split over 1, 2 workgroups, 26: 192 x 128; the 4-bit path has 9..12).
+// K split over 1, 2 workgroups, 26: 192 x 128; the 4-bit path has 7, 9..12,
+// 17 and 18).
 int launch_gemm_tiled_variant(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
                               float* y, int32_t* acc, int M, int N, int K, int variant, hipStream_t st) {
   const int8_t* wb = static_cast<const int8_t*>(w);
   if (w_is_int4) {
+    if (variant == 7 || variant == 17 || variant == 18) {
+      if (variant == 7) tiled::dma::launch_pp<128, 256, 2, true>(q, s_a, wb, s_w, y, acc, M, N, K, st);
+      else if (variant == 17) tiled::dma::launch_pp<128, 192, 2, true>(q, s_a, wb, s_w, y, acc, M, N, K, st);
+      else tiled::dma::launch_pp<128, 320, 1, true>(q, s_a, wb, s_w, y, acc, M, N, K, st);
+      return launch_status();
+    }
     if (variant < 9 || variant > 12) return PRISM_ERR_INVALID_ARG;  // 128 x 128 only
     const int stages = (K + 127) / 128;
     int splits = variant - 8;

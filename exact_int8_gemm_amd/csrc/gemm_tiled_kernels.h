@@ -51,6 +51,20 @@ __device__ inline void unpack_w4(const v4i p, v4i& lo, v4i& hi) {
   hi = v4i{o[4], o[5], o[6], o[7]};
 }
 
+// The same for 8 packed bytes (16 nibbles) -> one 16-byte fragment.
+__device__ inline v4i unpack_w4_8(const v2i p) {
+  int o[4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t u = (uint32_t)p[j];
+    const uint32_t L = (u << 4) & 0xF0F0F0F0u;
+    const uint32_t H = u & 0xF0F0F0F0u;
+    o[2 * j] = (int)__builtin_amdgcn_perm(H, L, 0x05010400u);
+    o[2 * j + 1] = (int)__builtin_amdgcn_perm(H, L, 0x07030602u);
+  }
+  return v4i{o[0], o[1], o[2], o[3]};
+}
+
 // Tile index of this workgroup: XCD-contiguous renumbering, then grouped
 // row-major order over the tile grid.
 __device__ inline void tile_of(int tiles_m, int tiles_n, int& tm, int& tn) {

@@ -22,7 +22,8 @@ SMALL = ["small_1x4", "small_1x8", "small_1x16", "small_2x4", "small_2x8", "smal
 TILES8 = ["tile_256x256", "tile_256x192", "tile_256x320", "tile_256x128", "tile_128x128", "tile_128x128_split2",
           "tile_128x128_split3", "tile_128x128_split4", "tile_64x128", "tile_64x128_split2", "tile_64x128_split3",
           "tile_64x128_split4", "tile_128x96", "tile_128x96_split2", "tile_192x128"]
-TILES4 = ["tile_128x128", "tile_128x128_split2", "tile_128x128_split3", "tile_128x128_split4"]
+TILES4 = ["tile_256x256", "tile_256x192", "tile_256x320", "tile_128x128", "tile_128x128_split2", "tile_128x128_split3",
+          "tile_128x128_split4"]
 
 
 def _inputs(seed, M, N, K, w4=False):
@@ -160,6 +161,36 @@ def test_256_row_tiles_full_size_sampled_rows(M, N, K):
     for name in ["auto", "tile_256x256", "tile_256x192", "tile_256x320", "tile_192x128"]:
         acc = torch.full((M, N), 7, dtype=torch.int32, device=DEV)
         y = prism.gemm_w8a8_variant(qd, sad, wd, swd, name, acc=acc)
+        torch.cuda.synchronize()
+        assert_same_ints(host(acc)[rows], acc_ref, "acc (%s)" % name)
+        assert_same_floats(host(y)[rows], y_ref, "y (%s)" % name)
+
+
+@pytest.mark.parametrize("M,N,K", [(600, 1300, 1056), (513, 1100, 4128), (256, 1024, 384), (1030, 2100, 2080),
+                                   (300, 700, 32)])
+def test_w4a8_256_row_tiles_several_column_groups(M, N, K):
+    """4-bit weights on the 256-row ping-pong tiles: the packed bytes move in pairs of
+    128-k stages, stages are padded to whole pairs of pairs (K = 32, 384, 1056, 2080, 4128
+    leave 1-4 padded stages), and a tile's last pair already fetches the next tile's first;
+    every width and the plain call give the oracle's bits on ragged shapes."""
+    q, s_a, w4, s_w = _inputs(M + 5 * N + K, M, N, K, w4=True)
+    y_ref, acc_ref = oracle.gemm_w4a8(q, s_a, w4, s_w)
+    _run_all(prism.gemm_w4a8_variant, ["auto", "tile_256x256", "tile_256x192", "tile_256x320"], dev(q), dev(s_a),
+             dev(w4), dev(s_w), y_ref, acc_ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(2048, 12288, 4096), (4096, 12288, 4096), (3072, 2560, 9728)])
+def test_w4a8_256_row_tiles_full_size_sampled_rows(M, N, K):
+    """The 4-bit shapes where the plain call picks 256-row tiles, at full size: the plain
+    call and every width against the oracle on sampled rows."""
+    q, s_a, w4, s_w = _inputs(M + N + K + 1, M, N, K, w4=True)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, M // 2, M - 257, M - 256, M - 1],
+                                     np.random.default_rng(M + N + 1).choice(M, 16, replace=False)]))
+    y_ref, acc_ref = oracle.gemm_w4a8(q[rows], s_a[rows], w4, s_w)
+    qd, sad, wd, swd = dev(q), dev(s_a), dev(w4), dev(s_w)
+    for name in ["auto", "tile_256x256", "tile_256x192", "tile_256x320"]:
+        acc = torch.full((M, N), 7, dtype=torch.int32, device=DEV)
+        y = prism.gemm_w4a8_variant(qd, sad, wd, swd, name, acc=acc)
         torch.cuda.synchronize()
         assert_same_ints(host(acc)[rows], acc_ref, "acc (%s)" % name)
         assert_same_floats(host(y)[rows], y_ref, "y (%s)" % name)

@@ -278,7 +278,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(const int8_t* __
 // Rows x K up to 30720 (15 float4 per thread): past that the workgroups spend
 // longer quantizing than the separate quantizer launch costs (MI355X,
 // N x K = 2560 x 9728: M = 3 takes 12.4 us in one kernel against 13.0 in
-// two launches, M = 4 took 14.3 against 13.2).
+// two launches, M = 4 took 14.3 against 13.2).  More rows lose for the same
+// reason even with short rows: every workgroup reads all M rows of x in
+// float32, M K 4 bytes per CU from L2 against M K for the codes the GEMM
+// reads after a separate quantizer launch (N x K = 9728 x 2560: 5 rows 12.1
+// us against 11.3 in two launches, 8 rows 13.9 against 11.5, 16 rows 21.3
+// against 12.0).
 constexpr int kFusedFloat4PerThread = 15;
 template <int MR>
 constexpr int fused_k_max() {

@@ -401,13 +401,13 @@ def _fused_rows(M, K, seed):
     return np.stack([_special_row(k, K, rng) for k in kinds])
 
 
-@pytest.mark.parametrize("M", [2, 3, 4, 7, 16])
+@pytest.mark.parametrize("M", [2, 3, 4, 5, 7, 8, 9, 16])
 @pytest.mark.parametrize("N,K", [(9728, 2560), (2560, 9728), (300, 1040), (3, 16), (5, 2064), (16384, 6144),
-                                 (257, 10240), (1000, 14336), (16384, 32), (16400, 1024)])
+                                 (257, 10240), (1000, 14336), (16384, 32), (16400, 1024), (4000, 4096)])
 def test_quantize_gemm_few_rows(M, N, K):
     """2..16 rows through the one call: M = 2, 3, 4 as one kernel in which every workgroup
     quantizes the rows itself (the projection shapes, ragged N and K, N < M, the largest N
-    and K), more rows or N > 16384 as two launches.  Codes, scales, acc and y equal the
+    and K), more rows, longer rows or N > 16384 as two launches.  Codes, scales, acc and y equal the
     oracle's quantize-then-GEMM and the library's two separate calls, bit for bit, with zero
     and NaN rows among them."""
     rng = np.random.default_rng(M * 7919 + N + K)

@@ -495,6 +495,16 @@ def kernels(torch, prism, wl, only=None):
             ops = 2 * ncu * 2 * wps * iters * 16 * 65536
             peaks["mfma_i8_%dw_per_simd" % wps] = dict(us=t * 1e6, tops=ops / t / 1e12,
                                                        mfma_frac=ops / t / 1e12 / PEAK_INT8_TOPS)
+        # The block-scale fold on registers: ns per 32-k block of one 32 x 32
+        # tile per SIMD (two waves per SIMD), int8 MFMA + convert + fmaf
+        # against f16 MFMA pairs + fmaf, and each part alone.
+        outf = torch.empty((ncu * 512,), dtype=torch.float32, device=dev)
+        iters = 4000
+        for mode, name in enumerate(prism.FOLD_MODES):
+            f = L.lib.prism_peak_fold
+            args = (mode, iters, L.p(outf), L.stream)
+            t1, t = _time_launches(torch, [lambda: f(*args)], 5)
+            peaks["fold_" + name] = dict(us=t * 1e6, ns_per_tile_block_per_simd=t * 1e9 / (2 * iters * prism.FOLD_TILES))
         parts = torch.empty((4096,), dtype=torch.int32, device=dev)
         for name, nbytes in (("read_25.2MB", 9728 * 2560), ("read_1GiB", 1 << 30)):
             R = _copies(nbytes)

@@ -293,4 +293,12 @@ int prism_peak_read(const void* buf, int64_t bytes, uint32_t* parts, void* strea
   return prism::launch_peak_read(buf, bytes, parts, PRISM_PEAK_READ_PARTS, static_cast<hipStream_t>(stream));
 }
 
+int prism_peak_fold(int mode, int64_t iters, float* out, void* stream) {
+  if (mode < 0 || mode > 4 || iters < 1 || iters > (1 << 20) || !out) return PRISM_ERR_INVALID_ARG;
+  if (!aligned(out, 4)) return PRISM_ERR_ALIGNMENT;
+  int st = check_device();
+  if (st != PRISM_OK) return st;
+  return prism::launch_peak_fold(mode, iters, out, static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

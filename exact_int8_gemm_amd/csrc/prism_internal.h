@@ -86,6 +86,7 @@ int launch_gemm_blockscale(const int8_t* q, const float* s_a, const int8_t* w, c
 // Measurement kernels (peaks.hip).
 int launch_peak_mfma(int64_t iters, int waves_per_simd, int seed, uint32_t* out, hipStream_t st);
 int launch_peak_read(const void* buf, int64_t bytes, uint32_t* parts, int nparts, hipStream_t st);
+int launch_peak_fold(int mode, int64_t iters, float* out, hipStream_t st);
 
 // Status of the most recent launch on this thread.
 int launch_status();

@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libprism.so")
 
 PRISM_OK = 0
-ABI_VERSION = 12
+ABI_VERSION = 13
 K_MAX = 131040
 
 # Dispatch-table entries of the W8A8 / W4A8 calls (PRISM_VARIANT_* in include/prism.h).
@@ -72,6 +72,8 @@ def _declare(lib):
     lib.prism_peak_mfma.argtypes = [i64, i32, i32, p, p]
     lib.prism_peak_read.restype = i32
     lib.prism_peak_read.argtypes = [p, i64, p, p]
+    lib.prism_peak_fold.restype = i32
+    lib.prism_peak_fold.argtypes = [i32, i64, p, p]
     return lib
 
 
@@ -331,6 +333,23 @@ def peak_mfma(iters, waves_per_simd, seed=0, out=None, device=None):
     out = torch.empty((n,), dtype=torch.int32, device=dev) if out is None else _need(out, "out", torch.int32, (n,), dev)
     with torch.cuda.device(dev):
         _check(lib().prism_peak_mfma(iters, waves_per_simd, seed, _ptr(out), _stream(dev)))
+    return out
+
+
+FOLD_MODES = ("i8_mfma_cvt_fold", "f16_mfma_fold", "i8_mfma_only", "f16_mfma_only", "fold_only")
+FOLD_TILES = 5
+
+
+def peak_fold(mode, iters, out=None, device=None):
+    """Run the block-fold probe (one workgroup of 8 waves per CU, 5 tiles of 32 x 32 per
+    wave, one 32-k block per tile per iteration) in ``mode`` (index into FOLD_MODES).
+    Returns the per-thread sums (float32 [CUs * 512])."""
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    n = torch.cuda.get_device_properties(dev).multi_processor_count * 512
+    out = (torch.empty((n,), dtype=torch.float32, device=dev) if out is None
+           else _need(out, "out", torch.float32, (n,), dev))
+    with torch.cuda.device(dev):
+        _check(lib().prism_peak_fold(mode, iters, _ptr(out), _stream(dev)))
     return out
 
 

@@ -42,7 +42,7 @@ extern "C" {
 #endif
 
 /* Bumped on any change of a signature or of the semantics below. */
-#define PRISM_ABI_VERSION 12
+#define PRISM_ABI_VERSION 13
 
 /* Largest accepted K.  For K <= 131040 every exact sum of K products of two
  * int8 values (|q|, |w| <= 128) lies strictly inside the int32 range. */
@@ -294,10 +294,23 @@ int prism_gemm_w4a8_variant(const int8_t* q, const float* s_a, const uint8_t* w4
  * 32-bit words each workgroup read to parts[workgroup]; all
  * PRISM_PEAK_READ_PARTS entries of parts are written (unused ones 0), so the
  * XOR of parts is the XOR of every 32-bit word of the buffer.
+ *
+ * prism_peak_fold: the cost of the block-scale fold (an exact sum per 32-k
+ * block of a 32 x 32 output tile, then one fp32 fmaf per output,
+ * StartLux-Prism README, "Why StartLux-Prism": Q8_0 weights as W8A8) on
+ * registers only.  One workgroup of 8 waves per compute unit; each wave
+ * holds 5 tiles and gives each one 32-k block per iteration.  mode 0: int8
+ * MFMA from zero, convert, fold; 1: two f16 MFMAs on the same values (the
+ * sum exact in fp32, no convert), fold; 2: the int8 MFMAs only
+ * (accumulating); 3: the f16 MFMA pairs only (accumulating); 4: the folds
+ * only.  out [CUs x 512] float gets one sum per thread.  Modes 0 and 1
+ * write the same bits; so do modes 2 and 3 for iters <= 32.  iters in [1,
+ * 2^20].
  */
 #define PRISM_PEAK_READ_PARTS 4096
 int prism_peak_mfma(int64_t iters, int waves_per_simd, int seed, uint32_t* out, void* stream);
 int prism_peak_read(const void* buf, int64_t bytes, uint32_t* parts, void* stream);
+int prism_peak_fold(int mode, int64_t iters, float* out, void* stream);
 
 #ifdef __cplusplus
 }

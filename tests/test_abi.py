@@ -45,7 +45,7 @@ def test_header_declares_every_call():
     assert {"prism_quantize_rows", "prism_quantize_rows_static", "prism_repack_q8_0", "prism_gemm_w8a8",
             "prism_gemm_w8a8_blockscale", "prism_gemm_w4a8", "prism_gemm_w8a8_variant", "prism_gemm_w4a8_variant",
             "prism_repack_q4_k", "prism_gemm_w4a8_q4k", "prism_quantize_gemm_w8a8",
-            "prism_peak_mfma", "prism_peak_read", "prism_abi_version", "prism_build_id", "prism_status_string"} <= names
+            "prism_peak_mfma", "prism_peak_read", "prism_peak_fold", "prism_abi_version", "prism_build_id", "prism_status_string"} <= names
 
 
 def test_library_exports_every_declared_symbol(built):
@@ -103,6 +103,8 @@ lib.prism_peak_mfma.restype = i32
 lib.prism_peak_mfma.argtypes = [i64, i32, i32, p, p]
 lib.prism_peak_read.restype = i32
 lib.prism_peak_read.argtypes = [p, i64, p, p]
+lib.prism_peak_fold.restype = i32
+lib.prism_peak_fold.argtypes = [i32, i64, p, p]
 A = 0x7f0000000000          # 256-byte aligned fake address, never dereferenced
 res = {"version": lib.prism_abi_version(),
        "strings": {str(s): lib.prism_status_string(s).decode() for s in (0, -1, -2, -3, -4, 7)}}
@@ -301,6 +303,12 @@ CASES += [
     ("prism_peak_read", [A, 40, A, None], ALIGN),                # bytes % 16
     ("prism_peak_read", [A + 8, 64, A, None], ALIGN),
     ("prism_peak_read", [A, 64, A + 1, None], ALIGN),
+    ("prism_peak_fold", [-1, 10, A, None], INVALID),             # mode in 0..4
+    ("prism_peak_fold", [5, 10, A, None], INVALID),
+    ("prism_peak_fold", [0, 0, A, None], INVALID),               # iters in [1, 2^20]
+    ("prism_peak_fold", [0, (1 << 20) + 1, A, None], INVALID),
+    ("prism_peak_fold", [0, 10, None, None], INVALID),
+    ("prism_peak_fold", [1, 10, A + 2, None], ALIGN),
 ]
 CASES.append(("prism_gemm_w8a8", _g(sw=A + 2), ALIGN))
 CASES.append(("prism_gemm_w4a8", _g(sw=A + 1), ALIGN))

@@ -4,6 +4,8 @@ derives from them count real work.
 * prism_peak_read: the XOR of its parts equals the XOR of every 32-bit word of the
   buffer (every byte read once, none dropped), on sizes from one 16-byte piece to a
   buffer larger than one pass of the grid.
+* prism_peak_fold: the int8 and f16 MFMA forms of the block fold write the same bits
+  (each 32-k block sum is exact either way), and so do the two MFMA-only forms.
 * prism_peak_mfma: each thread's checksum equals a CPU model of the MFMA loop.  The
   model needs only the row/column roles of the 32x32x32 int8 MFMA (lane l holds row
   l % 32 of A and column l % 32 of B for one half of k, lanes l and l + 32 the two
@@ -67,3 +69,18 @@ def test_peak_mfma_checksums(wps, iters, seed):
     got = got.reshape(-1, threads)
     for t in range(threads):
         assert (got[:, t] == want[t % 64]).all(), (t, got[:, t][:4], want[t % 64])
+
+
+@pytest.mark.parametrize("iters", [1, 2, 7, 32])
+def test_peak_fold_int8_and_f16_forms_agree(iters):
+    a = prism.peak_fold(0, iters)
+    b = prism.peak_fold(1, iters)
+    c = prism.peak_fold(2, iters)
+    d = prism.peak_fold(3, iters)
+    e = prism.peak_fold(4, iters)
+    torch.cuda.synchronize()
+    a, b, c, d, e = (t.cpu().numpy() for t in (a, b, c, d, e))
+    assert np.isfinite(a).all() and np.isfinite(e).all()
+    assert (a != 0).any() and (c != 0).any()
+    assert np.array_equal(a.view(np.int32), b.view(np.int32))
+    assert np.array_equal(c.view(np.int32), d.view(np.int32))

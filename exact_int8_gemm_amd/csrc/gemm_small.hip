@@ -651,6 +651,207 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_block_small_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// M = 1 block-scale and Q4_K GEMMs (one activation row).  Each fold chain
+// is one output, so the kernel for M <= 16 spends most of a chunk with one
+// wave folding 16 chains between two barriers while the rest wait.  Here a
+// wave is a workgroup of its own and owns R weight rows; it walks K in
+// groups of 256 k (8 blocks or sub-blocks: one Q4_K super-block) with W
+// groups of loads in flight and no workgroup barrier in the loop.  Per group:
+//  * the exact sum of every (row, block) comes from 16-byte pieces of the
+//    row, one piece per lane and load (Q4_K: 8 lanes per row and load, each
+//    piece holding half of two sub-blocks' nibbles; int8: 16 lanes per row,
+//    each piece half a block), with v_dot4 against the activation bytes in
+//    LDS, and the two halves of a block added from the neighbouring lane;
+//    it goes to LDS as fp32 (exact: |P| < 2^24);
+//  * lane l decodes the scales of R / 8 blocks of one row into LDS
+//    (binary16 d; Q4_K: D = d sc and Mn = dmin m from the row's super-block
+//    header);
+//  * lane r < R then runs the fold of row r over the group's 8 blocks:
+//    f = fmaf(P, d, f) (Q4_K: f = fmaf(P, D, f), then f = fmaf(-S, Mn, f),
+//    with -S the sub-block's activation sum, computed once per workgroup),
+//    in ascending block order, as every other kernel.
+// The tables are double-buffered, so the next group's sums need not wait for
+// this group's fold.  The activation row (K <= kGemvBlockKMax bytes) and -S
+// sit in dynamic LDS.  Rows past N read nothing (out of range) and store
+// nothing.  Requires K % 256 == 0 and 16-byte aligned q, w and scale arrays.
+constexpr int kGemvBlockKMax = 16384;
+
+template <bool Q4K, int R>
+constexpr size_t gemv_block_lds(int K) {
+  // row, -S (Q4_K), then per buffer: P and d (Q4_K: P, D and Mn), R x 8 fp32 each
+  return (size_t)K + (Q4K ? (size_t)K / 8 : 0) + 2 * (Q4K ? 3 : 2) * R * 8 * 4;
+}
+
+template <bool Q4K, int R, int W>
+__global__ __launch_bounds__(64) void gemv_block_kernel(const int8_t* __restrict__ q, const float* __restrict__ s_a,
+                                                        const int8_t* __restrict__ w,
+                                                        const uint16_t* __restrict__ d16,
+                                                        const uint8_t* __restrict__ hdr, float* __restrict__ y,
+                                                        int N, int K) {
+  static_assert(R == 8 || R == 16, "rows per wave");
+  constexpr int LPR = Q4K ? 8 : 16;   // lanes per row and load (16-byte pieces of a row's group)
+  constexpr int LW = R * LPR / 64;    // weight loads per lane per group of 256 k
+  constexpr int ND = R / 8;           // blocks whose scales each lane decodes
+  constexpr int NTAB = Q4K ? 3 : 2;
+  constexpr int TS = R * 8;           // floats per table
+  extern __shared__ __attribute__((aligned(16))) int8_t gv_lds[];
+  int8_t* qs = gv_lds;                                                     // the activation row, K bytes
+  float* nsum = reinterpret_cast<float*>(gv_lds + K);                      // Q4_K: -S per sub-block
+  float* tab = reinterpret_cast<float*>(gv_lds + K + (Q4K ? K / 8 : 0));  // [2][NTAB][16][8]
+  const int lane = threadIdx.x;
+  const int n0 = blockIdx.x * R;
+  const int NG = K / 256;  // groups
+  const int WR = Q4K ? K / 2 : K;
+
+  // This lane's pieces: load j covers row rl + j * (64 / LPR), piece p of
+  // the row's bytes of a group.
+  const int rl = lane / LPR;
+  const int p = lane % LPR;
+  const int gbytes = Q4K ? 128 : 256;  // weight bytes of one row per group
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + (size_t)n0 * (size_t)WR, (int64_t)(N - n0) * WR);
+  uint32_t wofs[LW];
+#pragma unroll
+  for (int j = 0; j < LW; ++j) {
+    const int r = rl + j * (64 / LPR);
+    wofs[j] = n0 + r < N ? (uint32_t)(r * WR + 16 * p) : kOutOfRange;
+  }
+  // Scales: lane l takes row l / (8 / ND) and decodes its blocks sb .. sb +
+  // ND - 1 of each group (int8: loads those ND binary16 scales; Q4_K: loads
+  // the row's 16-byte super-block header).
+  const int sr = lane / (8 / ND), sb = ND * (lane % (8 / ND));
+  const int NS = K / 256;
+  const __amdgpu_buffer_rsrc_t rs =
+      Q4K ? make_rsrc(hdr + (size_t)n0 * NS * 16, (int64_t)(N - n0) * NS * 16)
+          : make_rsrc(d16 + (size_t)n0 * (K / 32), (int64_t)(N - n0) * (K / 32) * 2);
+  const uint32_t sofs = n0 + sr < N ? (uint32_t)(sr * NS * 16 + (Q4K ? 0 : 2 * sb)) : kOutOfRange;
+
+  struct Group {
+    v4i b[LW];
+    v4i h;   // Q4_K: the header
+    int d2;  // int8: the ND binary16 scales
+  };
+  auto issue = [&](int g, Group& c) __attribute__((always_inline)) {
+    const bool in = g < NG;
+#pragma unroll
+    for (int j = 0; j < LW; ++j) c.b[j] = bload(rw, in ? wofs[j] + (uint32_t)(g * gbytes) : kOutOfRange);
+    const uint32_t so = in && sofs != kOutOfRange ? sofs + (uint32_t)(16 * g) : kOutOfRange;
+    if constexpr (Q4K) c.h = bload(rs, so);
+    else if constexpr (ND == 2) c.d2 = __builtin_amdgcn_raw_buffer_load_b32(rs, so, 0, 0);
+    else c.d2 = __builtin_amdgcn_raw_buffer_load_b16(rs, so, 0, 0);
+  };
+
+  // The first groups' loads go out before the row is staged.
+  Group c[W];
+#pragma unroll
+  for (int u = 0; u < W; ++u) issue(u, c[u]);
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q, K);
+    for (int i = lane; i < K / 16; i += 64)
+      *reinterpret_cast<v4i*>(qs + 16 * i) = bload(rq, (uint32_t)(16 * i));
+    __syncthreads();
+    if constexpr (Q4K) {
+      for (int b = lane; b < K / 32; b += 64) {
+        const v4i x0 = *reinterpret_cast<const v4i*>(qs + 32 * b);
+        const v4i x1 = *reinterpret_cast<const v4i*>(qs + 32 * b + 16);
+        int t = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          t = __builtin_amdgcn_sdot4(x0[e], 0x01010101, t, false);
+          t = __builtin_amdgcn_sdot4(x1[e], 0x01010101, t, false);
+        }
+        nsum[b] = -(float)t;
+      }
+      __syncthreads();
+    }
+  }
+
+  float f = 0.0f;
+  auto consume = [&](int g, const Group& c, float* tb) __attribute__((always_inline)) {
+    float* tp = tb;           // P [R][8]
+    float* td = tb + TS;      // d or D [R][8]
+    float* tm = tb + 2 * TS;  // Q4_K: Mn [R][8]
+    const int k0 = 256 * g;
+    if constexpr (Q4K) {
+      // Piece p: half p & 1 of the pair p >> 1 (32 bytes: byte l holds k = l
+      // of the pair in its low nibble and k = 32 + l in its high one).
+      const int8_t* qa = qs + k0 + 64 * (p >> 1) + 16 * (p & 1);
+      const v4i ql = *reinterpret_cast<const v4i*>(qa);
+      const v4i qh = *reinterpret_cast<const v4i*>(qa + 32);
+#pragma unroll
+      for (int j = 0; j < LW; ++j) {
+        int lo = 0, hi = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t v = (uint32_t)c.b[j][e];
+          lo = __builtin_amdgcn_sdot4((int)(v & 0x0f0f0f0fu), ql[e], lo, false);
+          hi = __builtin_amdgcn_sdot4((int)((v >> 4) & 0x0f0f0f0fu), qh[e], hi, false);
+        }
+        // The other half of each sub-block is in lane ^ 1; sub-block p of
+        // the group is the low nibbles' sum on even p, the high on odd.
+        const int mine = (p & 1) ? hi : lo, other = (p & 1) ? lo : hi;
+        const int t = mine + __builtin_amdgcn_mov_dpp(other, 0xB1, 0xF, 0xF, false);
+        tp[(rl + j * (64 / LPR)) * 8 + p] = (float)t;
+      }
+#pragma unroll
+      for (int e = 0; e < ND; ++e) {
+        float D, Mn;
+        q4k_scale_min(c.h, sb + e, D, Mn);
+        td[sr * 8 + sb + e] = D;
+        tm[sr * 8 + sb + e] = Mn;
+      }
+    } else {
+      const v4i qv = *reinterpret_cast<const v4i*>(qs + k0 + 16 * p);
+#pragma unroll
+      for (int j = 0; j < LW; ++j) {
+        int t = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t = __builtin_amdgcn_sdot4(c.b[j][e], qv[e], t, false);
+        t += __builtin_amdgcn_mov_dpp(t, 0xB1, 0xF, 0xF, false);
+        if ((p & 1) == 0) tp[(rl + j * (64 / LPR)) * 8 + (p >> 1)] = (float)t;
+      }
+      const uint32_t d2 = (uint32_t)c.d2;
+#pragma unroll
+      for (int e = 0; e < ND; ++e)
+        td[sr * 8 + sb + e] = (float)__builtin_bit_cast(_Float16, (uint16_t)(d2 >> (16 * e)));
+    }
+    if (lane < R) {
+      const v4f p0 = *reinterpret_cast<const v4f*>(tp + lane * 8);
+      const v4f p1 = *reinterpret_cast<const v4f*>(tp + lane * 8 + 4);
+      const v4f d0 = *reinterpret_cast<const v4f*>(td + lane * 8);
+      const v4f d1 = *reinterpret_cast<const v4f*>(td + lane * 8 + 4);
+      const float pv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+      const float dv[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+      if constexpr (Q4K) {
+        const v4f m0 = *reinterpret_cast<const v4f*>(tm + lane * 8);
+        const v4f m1 = *reinterpret_cast<const v4f*>(tm + lane * 8 + 4);
+        const v4f s0 = *reinterpret_cast<const v4f*>(nsum + 8 * g);
+        const v4f s1 = *reinterpret_cast<const v4f*>(nsum + 8 * g + 4);
+        const float mv[8] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
+        const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          f = __builtin_fmaf(pv[b], dv[b], f);
+          f = __builtin_fmaf(sv[b], mv[b], f);
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < 8; ++b) f = __builtin_fmaf(pv[b], dv[b], f);
+      }
+    }
+  };
+
+  for (int g0 = 0; g0 < NG; g0 += W) {
+#pragma unroll
+    for (int u = 0; u < W; ++u) {
+      if (g0 + u >= NG) break;
+      consume(g0 + u, c[u], tab + ((g0 + u) & 1) * NTAB * TS);
+      issue(g0 + u + W, c[u]);
+    }
+  }
+  if (lane < R && n0 + lane < N) y[n0 + lane] = f * s_a[0];
+}
+
+// ---------------------------------------------------------------------------
 // M = 1 with int8 weights (a single activation row): one output per weight
 // row, so no MFMA tile has to cover 16 columns and the rows can be spread
 // evenly over all waves of the grid (each CU then reads an equal share of the
@@ -835,6 +1036,19 @@ bool launch_gemv(const float* x, int8_t* q_out, float* s_out, const int8_t* q, c
 int launch_gemm_block_small(const int8_t* q, const float* s_a, const int8_t* w, const uint16_t* d16,
                             const uint8_t* hdr, float* y, int M, int N, int K, hipStream_t st) {
   const unsigned grid = (unsigned)((N + 15) / 16);
+  if (M == 1 && K <= kGemvBlockKMax && K % 256 == 0 && (hdr || reinterpret_cast<uintptr_t>(d16) % 16 == 0)) {
+#define PRISM_GEMV_BLOCK(Q4, R, W)                                                                 \
+  gemv_block_kernel<Q4, R, W><<<(unsigned)((N + R - 1) / R), 64, gemv_block_lds<Q4, R>(K), st>>>( \
+      q, s_a, w, Q4 ? nullptr : d16, Q4 ? hdr : nullptr, y, N, K)
+    // 8 rows per wave (two waves per SIMD at 17408 rows), Q4_K with 6 groups
+    // in flight, int8 with 3: the fastest of 8 or 16 rows and 2 to 16 groups
+    // at 17408 x 5120 (MI355X: Q4_K 28.5 -> 16.0 us against the M <= 16
+    // kernel, block-scale 23.5 -> 20.3 us).
+    if (hdr) PRISM_GEMV_BLOCK(true, 8, 6);
+    else PRISM_GEMV_BLOCK(false, 8, 3);
+#undef PRISM_GEMV_BLOCK
+    return launch_status();
+  }
   // 4 waves (16-block chunks), two chunks in flight: the fastest of waves in
   // {4, 8, 16} x ring depth in {2, 3, 4} at 17408 x 5120, M = 1 and 16.
   if (hdr) gemm_block_small_kernel<true, 4, 2><<<grid, 256, 0, st>>>(q, s_a, w, nullptr, hdr, y, M, N, K);

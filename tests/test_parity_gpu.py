@@ -526,6 +526,74 @@ def test_w4a8_extremes():
         assert_same_ints(host(acc)[:M], acc_ref, "acc rows=%d" % rows)
 
 
+@pytest.mark.parametrize("N,K", [(1, 256), (15, 768), (17, 4096), (300, 2560), (33, 16384), (20, 16640),
+                                 (40, 1056)])
+def test_blockscale_single_row(N, K):
+    """M = 1 (the one-row block kernel for K % 256 == 0 up to 16384; longer or ragged K
+    take the M <= 16 kernel): every output against the oracle, with full-range codes and
+    weights (-128 included) and scales from the whole finite binary16 range."""
+    rng = np.random.default_rng(N * 7 + K)
+    q = rng.integers(-128, 128, (1, K), dtype=np.int8)
+    w = rng.integers(-128, 128, (N, K), dtype=np.int8)
+    d = rng.integers(0, 0x7c00, (N, K // 32), dtype=np.uint16)   # finite, both signs below
+    d |= (rng.integers(0, 2, d.shape) << 15).astype(np.uint16)
+    s_a = np.array([0.0123], np.float32)
+    y_ref, _ = oracle.gemm_w8a8_blockscale(q, s_a, w, d)
+    y = prism.gemm_w8a8_blockscale(dev(q), dev(s_a), dev(w), dev(d))
+    torch.cuda.synchronize()
+    assert_same_floats(host(y), y_ref, "y")
+
+
+def test_blockscale_single_row_every_fp16_pattern():
+    """K = 256, one row: block b of weight row n has scale pattern 8 n + b, so all 65536
+    binary16 patterns (NaN, inf, subnormal, -0) pass through the one-row kernel's fold
+    (a row with an infinite scale also holds NaN patterns, so its output is NaN)."""
+    N, K = 8192, 256
+    rng = np.random.default_rng(3)
+    q = rng.integers(-127, 128, (1, K), dtype=np.int8)
+    w = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    d = np.arange(N * 8, dtype=np.uint32).astype(np.uint16).reshape(N, 8)
+    s_a = np.array([1.0], np.float32)
+    y_ref, _ = oracle.gemm_w8a8_blockscale(q, s_a, w, d)
+    y = prism.gemm_w8a8_blockscale(dev(q), dev(s_a), dev(w), dev(d))
+    torch.cuda.synchronize()
+    assert np.isnan(y_ref).any() and np.isfinite(y_ref).any()
+    assert_same_floats(host(y), y_ref, "y")
+
+
+def test_blockscale_single_row_scales_not_16_byte_aligned():
+    """A scale array that is only 2-byte aligned takes the M <= 16 kernel: same bits."""
+    N, K = 50, 512
+    rng = np.random.default_rng(8)
+    q = rng.integers(-127, 128, (1, K), dtype=np.int8)
+    w = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    d = (rng.uniform(1e-4, 1e-2, (N, K // 32))).astype(np.float16).view(np.uint16)
+    s_a = np.array([0.5], np.float32)
+    y_ref, _ = oracle.gemm_w8a8_blockscale(q, s_a, w, d)
+    buf = torch.zeros(N * (K // 32) + 1, dtype=torch.int16, device=DEV)
+    dd = buf[1:].view(N, K // 32)
+    dd.copy_(dev(d.view(np.int16)))
+    assert dd.data_ptr() % 16 != 0
+    y = prism.gemm_w8a8_blockscale(dev(q), dev(s_a), dev(w), dd)
+    torch.cuda.synchronize()
+    assert_same_floats(host(y), y_ref, "y")
+
+
+@pytest.mark.parametrize("N,K", [(1, 256), (70, 768), (33, 16384), (20, 16640)])
+def test_gemm_w4a8_q4k_single_row_any_header_bytes(N, K):
+    """M = 1 on planes written by the oracle's repack from random block bytes: headers with
+    binary16 NaN, infinite, subnormal and zero d and dmin, every 6-bit scale and min."""
+    rng = np.random.default_rng(N + K)
+    blocks = rng.integers(0, 256, N * (K // 256) * 144, dtype=np.uint8)
+    x = rng.standard_normal((1, K), dtype=np.float32)
+    q_ref, sa_ref = oracle.quantize_rows(x)
+    y_ref = oracle.gemm_w4a8_q4k(q_ref, sa_ref, blocks, N)
+    w_ref, h_ref = oracle.repack_q4_k(blocks, N, K)
+    y = prism.gemm_w4a8_q4k(dev(q_ref), dev(sa_ref), dev(w_ref), dev(h_ref))
+    torch.cuda.synchronize()
+    assert_same_floats(host(y), y_ref, "y")
+
+
 def test_blockscale_every_fp16_pattern():
     """One output per binary16 bit pattern: y = fmaf(1, d, +0) * 1 = d (NaN stays NaN)."""
     N, K = 65536, 32

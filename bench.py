@@ -127,10 +127,11 @@ def _copies(bytes_per_set):
     return max(2, -(-ROTATE_BYTES // max(1, bytes_per_set)))
 
 
-# Sources of the GEMM kernels: a traffic figure is used only if it was
-# measured on exactly these sources.
-KERNEL_SOURCES = ["gemm_tiled_kernels.h", "gemm_pingpong.h", "gemm_tiled.hip", "gemm_small.hip", "prism_abi.cpp", "prism_internal.h",
-                  "quant_math.h"]
+# Sources of the per-channel W8A8 GEMM path of M > 64 (dispatch, tiled and
+# persistent kernels, direct-to-LDS copies): a traffic figure is used only if
+# it was measured on exactly these sources.
+KERNEL_SOURCES = ["gemm_tiled_kernels.h", "gemm_pingpong.h", "gemm_tiled.hip", "lds_copy.h", "prism_abi.cpp",
+                  "prism_internal.h"]
 
 
 def _src_hash(names):
@@ -634,9 +635,6 @@ def main():
     from exact_int8_gemm_amd import prism
     from exact_int8_gemm_amd import workloads as wl
 
-    if args.only is not None and args.only != "step":
-        print(json.dumps(kernels(torch, prism, wl, only=args.only)))
-        return
     if args.calib_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda:0")
         dst = torch.empty_like(src)
@@ -644,6 +642,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.only is not None and args.only != "step":
+        print(json.dumps(kernels(torch, prism, wl, only=args.only)))
+        return
     h = headline(torch, prism, wl, args)
     print("headline step done: %.1f us per step" % (h["ms_per_step"] * 1e3), file=sys.stderr, flush=True)
     rec = {

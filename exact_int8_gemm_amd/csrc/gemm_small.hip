@@ -651,55 +651,66 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_block_small_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// M = 1 block-scale and Q4_K GEMMs (one activation row).  Each fold chain
-// is one output, so the kernel for M <= 16 spends most of a chunk with one
-// wave folding 16 chains between two barriers while the rest wait.  Here a
-// wave is a workgroup of its own and owns R weight rows; it walks K in
-// groups of 256 k (8 blocks or sub-blocks: one Q4_K super-block) with W
-// groups of loads in flight and no workgroup barrier in the loop.  Per group:
-//  * the exact sum of every (row, block) comes from 16-byte pieces of the
-//    row, one piece per lane and load (Q4_K: 8 lanes per row and load, each
-//    piece holding half of two sub-blocks' nibbles; int8: 16 lanes per row,
-//    each piece half a block), with v_dot4 against the activation bytes in
-//    LDS, and the two halves of a block added from the neighbouring lane;
-//    it goes to LDS as fp32 (exact: |P| < 2^24);
-//  * lane l decodes the scales of R / 8 blocks of one row into LDS
+// Block-scale and Q4_K GEMMs of 1 to 4 activation rows.  Each fold chain is
+// one output, so the kernel for M <= 16 above spends most of a chunk with
+// one wave folding 16 M chains between two barriers while the rest wait.
+// Here each wave owns R weight rows and walks K on its own, in groups of 256
+// k (8 blocks or sub-blocks: one Q4_K super-block) with W groups of loads in
+// flight and no workgroup barrier in the loop (the NWV waves of a workgroup
+// share only the activation rows, staged into LDS once).  Per group:
+//  * the exact sum of every (activation row, weight row, block) comes from
+//    16-byte pieces of the weight rows, one piece per lane and load (Q4_K:
+//    8 lanes per row and load, each piece holding half of two sub-blocks'
+//    nibbles; int8: 16 lanes per row, each piece half a block), with v_dot4
+//    against the activation bytes in LDS, and the two halves of a block
+//    added from the neighbouring lane; it goes to LDS as fp32 (exact:
+//    |P| < 2^24);
+//  * lane l decodes the scales of R / 8 blocks of one weight row into LDS
 //    (binary16 d; Q4_K: D = d sc and Mn = dmin m from the row's super-block
 //    header);
-//  * lane r < R then runs the fold of row r over the group's 8 blocks:
-//    f = fmaf(P, d, f) (Q4_K: f = fmaf(P, D, f), then f = fmaf(-S, Mn, f),
-//    with -S the sub-block's activation sum, computed once per workgroup),
-//    in ascending block order, as every other kernel.
+//  * lane c < M R then runs the fold of output (c / R, c % R) over the
+//    group's 8 blocks: f = fmaf(P, d, f) per block (Q4_K: f = fmaf(P, D, f),
+//    then f = fmaf(-S, Mn, f), with -S the sub-block's activation sum,
+//    computed once per workgroup), in ascending block order, as every other
+//    kernel.
 // The tables are double-buffered, so the next group's sums need not wait for
-// this group's fold.  The activation row (K <= kGemvBlockKMax bytes) and -S
-// sit in dynamic LDS.  Rows past N read nothing (out of range) and store
-// nothing.  Requires K % 256 == 0 and 16-byte aligned q, w and scale arrays.
-constexpr int kGemvBlockKMax = 16384;
-
-template <bool Q4K, int R>
-constexpr size_t gemv_block_lds(int K) {
-  // row, -S (Q4_K), then per buffer: P and d (Q4_K: P, D and Mn), R x 8 fp32 each
-  return (size_t)K + (Q4K ? (size_t)K / 8 : 0) + 2 * (Q4K ? 3 : 2) * R * 8 * 4;
+// this group's fold.  The activation rows (M K bytes) and -S sit in dynamic
+// LDS.  Weight rows past N read nothing (out of range) and store nothing.
+// Requires K % 256 == 0 and 16-byte aligned q, w and scale arrays.
+template <bool Q4K, int R, int MR>
+constexpr int gemv_block_tab() {
+  // floats per table buffer of one wave: P [MR][R][8], d or D [R][8], Q4_K Mn [R][8]
+  return (MR + (Q4K ? 2 : 1)) * R * 8;
+}
+template <bool Q4K, int R, int MR, int NWV>
+size_t gemv_block_lds(int M, int K) {
+  return (size_t)M * K + (Q4K ? (size_t)M * K / 8 : 0) + (size_t)NWV * 2 * gemv_block_tab<Q4K, R, MR>() * 4;
 }
 
-template <bool Q4K, int R, int W>
-__global__ __launch_bounds__(64) void gemv_block_kernel(const int8_t* __restrict__ q, const float* __restrict__ s_a,
-                                                        const int8_t* __restrict__ w,
-                                                        const uint16_t* __restrict__ d16,
-                                                        const uint8_t* __restrict__ hdr, float* __restrict__ y,
-                                                        int N, int K) {
+template <bool Q4K, int R, int MR, int NWV, int W>
+__global__ __launch_bounds__(64 * NWV) void gemv_block_kernel(const int8_t* __restrict__ q,
+                                                              const float* __restrict__ s_a,
+                                                              const int8_t* __restrict__ w,
+                                                              const uint16_t* __restrict__ d16,
+                                                              const uint8_t* __restrict__ hdr,
+                                                              float* __restrict__ y, int M, int N, int K) {
   static_assert(R == 8 || R == 16, "rows per wave");
+  static_assert(MR * R <= 64, "one fold chain per lane");
   constexpr int LPR = Q4K ? 8 : 16;   // lanes per row and load (16-byte pieces of a row's group)
   constexpr int LW = R * LPR / 64;    // weight loads per lane per group of 256 k
   constexpr int ND = R / 8;           // blocks whose scales each lane decodes
-  constexpr int NTAB = Q4K ? 3 : 2;
-  constexpr int TS = R * 8;           // floats per table
+  constexpr int TS = R * 8;           // floats per [R][8] table
   extern __shared__ __attribute__((aligned(16))) int8_t gv_lds[];
-  int8_t* qs = gv_lds;                                                     // the activation row, K bytes
-  float* nsum = reinterpret_cast<float*>(gv_lds + K);                      // Q4_K: -S per sub-block
-  float* tab = reinterpret_cast<float*>(gv_lds + K + (Q4K ? K / 8 : 0));  // [2][NTAB][16][8]
-  const int lane = threadIdx.x;
-  const int n0 = blockIdx.x * R;
+  int8_t* qs = gv_lds;                                                         // activation rows, M K bytes
+  float* nsum = reinterpret_cast<float*>(gv_lds + M * K);                      // Q4_K: -S [M][K / 32]
+  // The wave index goes through readfirstlane so that the compiler sees it
+  // (and the buffer resources built from it) as uniform; a divergent
+  // resource makes it loop over the lanes around every buffer load.
+  const int lane = threadIdx.x & 63;
+  const int wv = NWV == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  float* tab = reinterpret_cast<float*>(gv_lds + M * K + (Q4K ? M * K / 8 : 0)) +
+               wv * 2 * gemv_block_tab<Q4K, R, MR>();                          // this wave's [2] buffers
+  const int n0 = (blockIdx.x * NWV + wv) * R;
   const int NG = K / 256;  // groups
   const int WR = Q4K ? K / 2 : K;
 
@@ -708,22 +719,24 @@ __global__ __launch_bounds__(64) void gemv_block_kernel(const int8_t* __restrict
   const int rl = lane / LPR;
   const int p = lane % LPR;
   const int gbytes = Q4K ? 128 : 256;  // weight bytes of one row per group
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + (size_t)n0 * (size_t)WR, (int64_t)(N - n0) * WR);
+  const int nrows = n0 < N ? N - n0 : 0;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w + (size_t)(n0 < N ? n0 : 0) * (size_t)WR, (int64_t)nrows * WR);
   uint32_t wofs[LW];
 #pragma unroll
   for (int j = 0; j < LW; ++j) {
     const int r = rl + j * (64 / LPR);
-    wofs[j] = n0 + r < N ? (uint32_t)(r * WR + 16 * p) : kOutOfRange;
+    wofs[j] = r < nrows ? (uint32_t)(r * WR + 16 * p) : kOutOfRange;
   }
   // Scales: lane l takes row l / (8 / ND) and decodes its blocks sb .. sb +
   // ND - 1 of each group (int8: loads those ND binary16 scales; Q4_K: loads
   // the row's 16-byte super-block header).
   const int sr = lane / (8 / ND), sb = ND * (lane % (8 / ND));
   const int NS = K / 256;
+  const size_t nc = (size_t)(n0 < N ? n0 : 0);
   const __amdgpu_buffer_rsrc_t rs =
-      Q4K ? make_rsrc(hdr + (size_t)n0 * NS * 16, (int64_t)(N - n0) * NS * 16)
-          : make_rsrc(d16 + (size_t)n0 * (K / 32), (int64_t)(N - n0) * (K / 32) * 2);
-  const uint32_t sofs = n0 + sr < N ? (uint32_t)(sr * NS * 16 + (Q4K ? 0 : 2 * sb)) : kOutOfRange;
+      Q4K ? make_rsrc(hdr + nc * NS * 16, (int64_t)nrows * NS * 16)
+          : make_rsrc(d16 + nc * (K / 32), (int64_t)nrows * (K / 32) * 2);
+  const uint32_t sofs = sr < nrows ? (uint32_t)(sr * NS * 16 + (Q4K ? 0 : 2 * sb)) : kOutOfRange;
 
   struct Group {
     v4i b[LW];
@@ -740,17 +753,17 @@ __global__ __launch_bounds__(64) void gemv_block_kernel(const int8_t* __restrict
     else c.d2 = __builtin_amdgcn_raw_buffer_load_b16(rs, so, 0, 0);
   };
 
-  // The first groups' loads go out before the row is staged.
+  // The first groups' loads go out before the rows are staged.
   Group c[W];
 #pragma unroll
   for (int u = 0; u < W; ++u) issue(u, c[u]);
   {
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q, K);
-    for (int i = lane; i < K / 16; i += 64)
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q, (int64_t)M * K);
+    for (int i = threadIdx.x; i < M * K / 16; i += 64 * NWV)
       *reinterpret_cast<v4i*>(qs + 16 * i) = bload(rq, (uint32_t)(16 * i));
     __syncthreads();
     if constexpr (Q4K) {
-      for (int b = lane; b < K / 32; b += 64) {
+      for (int b = threadIdx.x; b < M * K / 32; b += 64 * NWV) {
         const v4i x0 = *reinterpret_cast<const v4i*>(qs + 32 * b);
         const v4i x1 = *reinterpret_cast<const v4i*>(qs + 32 * b + 16);
         int t = 0;
@@ -765,32 +778,45 @@ __global__ __launch_bounds__(64) void gemv_block_kernel(const int8_t* __restrict
     }
   }
 
+  // Output of this lane's fold chain: activation row fm, weight row fr.
+  const int fm = lane / R, fr = lane % R;
+  const bool chain = fm < M;
   float f = 0.0f;
   auto consume = [&](int g, const Group& c, float* tb) __attribute__((always_inline)) {
-    float* tp = tb;           // P [R][8]
-    float* td = tb + TS;      // d or D [R][8]
-    float* tm = tb + 2 * TS;  // Q4_K: Mn [R][8]
+    float* tp = tb;                 // P [MR][R][8]
+    float* td = tb + MR * TS;       // d or D [R][8]
+    float* tm = tb + (MR + 1) * TS; // Q4_K: Mn [R][8]
     const int k0 = 256 * g;
     if constexpr (Q4K) {
       // Piece p: half p & 1 of the pair p >> 1 (32 bytes: byte l holds k = l
       // of the pair in its low nibble and k = 32 + l in its high one).
-      const int8_t* qa = qs + k0 + 64 * (p >> 1) + 16 * (p & 1);
-      const v4i ql = *reinterpret_cast<const v4i*>(qa);
-      const v4i qh = *reinterpret_cast<const v4i*>(qa + 32);
+      const int ka = k0 + 64 * (p >> 1) + 16 * (p & 1);
 #pragma unroll
       for (int j = 0; j < LW; ++j) {
-        int lo = 0, hi = 0;
+        v4i lo4, hi4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t v = (uint32_t)c.b[j][e];
-          lo = __builtin_amdgcn_sdot4((int)(v & 0x0f0f0f0fu), ql[e], lo, false);
-          hi = __builtin_amdgcn_sdot4((int)((v >> 4) & 0x0f0f0f0fu), qh[e], hi, false);
+          lo4[e] = (int)(v & 0x0f0f0f0fu);
+          hi4[e] = (int)((v >> 4) & 0x0f0f0f0fu);
         }
-        // The other half of each sub-block is in lane ^ 1; sub-block p of
-        // the group is the low nibbles' sum on even p, the high on odd.
-        const int mine = (p & 1) ? hi : lo, other = (p & 1) ? lo : hi;
-        const int t = mine + __builtin_amdgcn_mov_dpp(other, 0xB1, 0xF, 0xF, false);
-        tp[(rl + j * (64 / LPR)) * 8 + p] = (float)t;
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+          if (m >= M) break;
+          const v4i ql = *reinterpret_cast<const v4i*>(qs + m * K + ka);
+          const v4i qh = *reinterpret_cast<const v4i*>(qs + m * K + ka + 32);
+          int lo = 0, hi = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            lo = __builtin_amdgcn_sdot4(lo4[e], ql[e], lo, false);
+            hi = __builtin_amdgcn_sdot4(hi4[e], qh[e], hi, false);
+          }
+          // The other half of each sub-block is in lane ^ 1; sub-block p of
+          // the group is the low nibbles' sum on even p, the high on odd.
+          const int mine = (p & 1) ? hi : lo, other = (p & 1) ? lo : hi;
+          const int t = mine + __builtin_amdgcn_mov_dpp(other, 0xB1, 0xF, 0xF, false);
+          tp[m * TS + (rl + j * (64 / LPR)) * 8 + p] = (float)t;
+        }
       }
 #pragma unroll
       for (int e = 0; e < ND; ++e) {
@@ -800,32 +826,38 @@ __global__ __launch_bounds__(64) void gemv_block_kernel(const int8_t* __restrict
         tm[sr * 8 + sb + e] = Mn;
       }
     } else {
-      const v4i qv = *reinterpret_cast<const v4i*>(qs + k0 + 16 * p);
 #pragma unroll
-      for (int j = 0; j < LW; ++j) {
-        int t = 0;
+      for (int m = 0; m < MR; ++m) {
+        if (m >= M) break;
+        const v4i qv = *reinterpret_cast<const v4i*>(qs + m * K + k0 + 16 * p);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) t = __builtin_amdgcn_sdot4(c.b[j][e], qv[e], t, false);
-        t += __builtin_amdgcn_mov_dpp(t, 0xB1, 0xF, 0xF, false);
-        if ((p & 1) == 0) tp[(rl + j * (64 / LPR)) * 8 + (p >> 1)] = (float)t;
+        for (int j = 0; j < LW; ++j) {
+          int t = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) t = __builtin_amdgcn_sdot4(c.b[j][e], qv[e], t, false);
+          t += __builtin_amdgcn_mov_dpp(t, 0xB1, 0xF, 0xF, false);
+          if ((p & 1) == 0) tp[m * TS + (rl + j * (64 / LPR)) * 8 + (p >> 1)] = (float)t;
+        }
       }
       const uint32_t d2 = (uint32_t)c.d2;
 #pragma unroll
       for (int e = 0; e < ND; ++e)
         td[sr * 8 + sb + e] = (float)__builtin_bit_cast(_Float16, (uint16_t)(d2 >> (16 * e)));
     }
-    if (lane < R) {
-      const v4f p0 = *reinterpret_cast<const v4f*>(tp + lane * 8);
-      const v4f p1 = *reinterpret_cast<const v4f*>(tp + lane * 8 + 4);
-      const v4f d0 = *reinterpret_cast<const v4f*>(td + lane * 8);
-      const v4f d1 = *reinterpret_cast<const v4f*>(td + lane * 8 + 4);
+    if (chain) {
+      const float* pr = tp + fm * TS + fr * 8;
+      const v4f p0 = *reinterpret_cast<const v4f*>(pr);
+      const v4f p1 = *reinterpret_cast<const v4f*>(pr + 4);
+      const v4f d0 = *reinterpret_cast<const v4f*>(td + fr * 8);
+      const v4f d1 = *reinterpret_cast<const v4f*>(td + fr * 8 + 4);
       const float pv[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
       const float dv[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
       if constexpr (Q4K) {
-        const v4f m0 = *reinterpret_cast<const v4f*>(tm + lane * 8);
-        const v4f m1 = *reinterpret_cast<const v4f*>(tm + lane * 8 + 4);
-        const v4f s0 = *reinterpret_cast<const v4f*>(nsum + 8 * g);
-        const v4f s1 = *reinterpret_cast<const v4f*>(nsum + 8 * g + 4);
+        const v4f m0 = *reinterpret_cast<const v4f*>(tm + fr * 8);
+        const v4f m1 = *reinterpret_cast<const v4f*>(tm + fr * 8 + 4);
+        const float* ns = nsum + fm * (K / 32) + 8 * g;
+        const v4f s0 = *reinterpret_cast<const v4f*>(ns);
+        const v4f s1 = *reinterpret_cast<const v4f*>(ns + 4);
         const float mv[8] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
         const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
 #pragma unroll
@@ -844,11 +876,11 @@ __global__ __launch_bounds__(64) void gemv_block_kernel(const int8_t* __restrict
 #pragma unroll
     for (int u = 0; u < W; ++u) {
       if (g0 + u >= NG) break;
-      consume(g0 + u, c[u], tab + ((g0 + u) & 1) * NTAB * TS);
+      consume(g0 + u, c[u], tab + ((g0 + u) & 1) * gemv_block_tab<Q4K, R, MR>());
       issue(g0 + u + W, c[u]);
     }
   }
-  if (lane < R && n0 + lane < N) y[n0 + lane] = f * s_a[0];
+  if (chain && fr < nrows) y[(size_t)fm * N + n0 + fr] = f * s_a[fm];
 }
 
 // ---------------------------------------------------------------------------
@@ -1036,16 +1068,25 @@ bool launch_gemv(const float* x, int8_t* q_out, float* s_out, const int8_t* q, c
 int launch_gemm_block_small(const int8_t* q, const float* s_a, const int8_t* w, const uint16_t* d16,
                             const uint8_t* hdr, float* y, int M, int N, int K, hipStream_t st) {
   const unsigned grid = (unsigned)((N + 15) / 16);
-  if (M == 1 && K <= kGemvBlockKMax && K % 256 == 0 && (hdr || reinterpret_cast<uintptr_t>(d16) % 16 == 0)) {
-#define PRISM_GEMV_BLOCK(Q4, R, W)                                                                 \
-  gemv_block_kernel<Q4, R, W><<<(unsigned)((N + R - 1) / R), 64, gemv_block_lds<Q4, R>(K), st>>>( \
-      q, s_a, w, Q4 ? nullptr : d16, Q4 ? hdr : nullptr, y, N, K)
-    // 8 rows per wave (two waves per SIMD at 17408 rows), Q4_K with 6 groups
-    // in flight, int8 with 3: the fastest of 8 or 16 rows and 2 to 16 groups
-    // at 17408 x 5120 (MI355X: Q4_K 28.5 -> 16.0 us against the M <= 16
-    // kernel, block-scale 23.5 -> 20.3 us).
-    if (hdr) PRISM_GEMV_BLOCK(true, 8, 6);
-    else PRISM_GEMV_BLOCK(false, 8, 3);
+  // 1 <= M <= 4 rows of at most 16 KB (M = 1) or 32 KB in all, whole
+  // super-blocks, aligned scales: the per-wave kernel above.
+  if (M <= 4 && K % 256 == 0 && (M == 1 ? K <= 16384 : M * K <= 32768) &&
+      (hdr || reinterpret_cast<uintptr_t>(d16) % 16 == 0)) {
+    // M = 1: 8 rows per wave in a workgroup of its own (two waves per SIMD
+    // at 17408 rows), Q4_K with 6 groups in flight, int8 with 3: the fastest
+    // of 8 or 16 rows and 2 to 16 groups at 17408 x 5120 (MI355X: Q4_K 28.5
+    // -> 16.0 us against the M <= 16 kernel, block-scale 23.5 -> 20.3 us).
+#define PRISM_GEMV_BLOCK(Q4, R, MR, NWV, W)                                                                \
+  gemv_block_kernel<Q4, R, MR, NWV, W><<<(unsigned)((N + R * NWV - 1) / (R * NWV)), 64 * NWV,                \
+                                        gemv_block_lds<Q4, R, MR, NWV>(M, K), st>>>(                           \
+      q, s_a, w, Q4 ? nullptr : d16, Q4 ? hdr : nullptr, y, M, N, K)
+    if (M == 1) {
+      if (hdr) PRISM_GEMV_BLOCK(true, 8, 1, 1, 6);
+      else PRISM_GEMV_BLOCK(false, 8, 1, 1, 3);
+    } else {
+      if (hdr) PRISM_GEMV_BLOCK(true, 8, 4, 4, 6);
+      else PRISM_GEMV_BLOCK(false, 8, 4, 4, 3);
+    }
 #undef PRISM_GEMV_BLOCK
     return launch_status();
   }

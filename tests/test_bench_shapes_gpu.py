@@ -49,10 +49,10 @@ def test_w4a8_prefill_full_size_sampled_rows(M):
     assert_same_floats(y[rows], y_ref, "y sampled rows")
 
 
-@pytest.mark.parametrize("M", [1, 16])
+@pytest.mark.parametrize("M", [1, 4, 16])
 def test_block_scale_decode_full_size(M):
-    """N = 17408, K = 5120 with fp16 block scales, M <= 16: the small-M block
-    kernel, every row against the oracle."""
+    """N = 17408, K = 5120 with fp16 block scales, M <= 16: the per-wave kernel (M = 1, 4)
+    and the small-M block kernel (M = 16), every row against the oracle."""
     c = wl.block()
     q, s, q_ref, s_ref = _quantize_both(c["x"][:M].copy())
     y = host(prism.gemm_w8a8_blockscale(q, s, dev(c["w"]), dev(c["d"])))
@@ -72,7 +72,7 @@ def _q4k_blocks(seed, N, K):
     return blocks.reshape(-1)
 
 
-@pytest.mark.parametrize("M", [1, 2048])
+@pytest.mark.parametrize("M", [1, 4, 2048])
 def test_q4k_full_size(M):
     """Q4_K weights of the block-scale shape (17408 x 5120): the repacked
     planes in full, and the GEMM (M = 1: small-M block kernel, every output;

@@ -215,7 +215,7 @@ def test_repack_q4_k(N, K):
     assert_same_ints(host(hdr), h_ref, "headers")
 
 
-@pytest.mark.parametrize("M", [1, 7, 16, 17, 65, 129, 257])
+@pytest.mark.parametrize("M", [1, 2, 4, 7, 16, 17, 65, 129, 257])
 @pytest.mark.parametrize("N,K", [(100, 256), (300, 1024), (130, 2304)])
 def test_gemm_w4a8_q4k(M, N, K):
     """Q4_K bytes -> GPU repack -> GPU GEMM, against the oracle straight from the bytes."""
@@ -526,18 +526,20 @@ def test_w4a8_extremes():
         assert_same_ints(host(acc)[:M], acc_ref, "acc rows=%d" % rows)
 
 
-@pytest.mark.parametrize("N,K", [(1, 256), (15, 768), (17, 4096), (300, 2560), (33, 16384), (20, 16640),
-                                 (40, 1056)])
-def test_blockscale_single_row(N, K):
-    """M = 1 (the one-row block kernel for K % 256 == 0 up to 16384; longer or ragged K
-    take the M <= 16 kernel): every output against the oracle, with full-range codes and
-    weights (-128 included) and scales from the whole finite binary16 range."""
-    rng = np.random.default_rng(N * 7 + K)
-    q = rng.integers(-128, 128, (1, K), dtype=np.int8)
+@pytest.mark.parametrize("M,N,K", [(1, 1, 256), (1, 15, 768), (1, 17, 4096), (1, 300, 2560), (1, 33, 16384),
+                                   (1, 20, 16640), (1, 40, 1056), (2, 1, 256), (2, 71, 16384), (2, 30, 16640),
+                                   (3, 33, 2560), (4, 129, 8192), (4, 20, 8448), (4, 9, 1056)])
+def test_blockscale_few_rows(M, N, K):
+    """1 to 4 rows (the per-wave block kernel for K % 256 == 0 and K <= 16384 at M = 1, M K
+    <= 32768 otherwise; longer or ragged rows take the M <= 16 kernel): every output
+    against the oracle, with full-range codes and weights (-128 included) and scales from
+    the whole finite binary16 range."""
+    rng = np.random.default_rng(M * 1000 + N * 7 + K)
+    q = rng.integers(-128, 128, (M, K), dtype=np.int8)
     w = rng.integers(-128, 128, (N, K), dtype=np.int8)
     d = rng.integers(0, 0x7c00, (N, K // 32), dtype=np.uint16)   # finite, both signs below
     d |= (rng.integers(0, 2, d.shape) << 15).astype(np.uint16)
-    s_a = np.array([0.0123], np.float32)
+    s_a = (np.float32(0.0123) * (1 + np.arange(M))).astype(np.float32)
     y_ref, _ = oracle.gemm_w8a8_blockscale(q, s_a, w, d)
     y = prism.gemm_w8a8_blockscale(dev(q), dev(s_a), dev(w), dev(d))
     torch.cuda.synchronize()
@@ -579,13 +581,17 @@ def test_blockscale_single_row_scales_not_16_byte_aligned():
     assert_same_floats(host(y), y_ref, "y")
 
 
-@pytest.mark.parametrize("N,K", [(1, 256), (70, 768), (33, 16384), (20, 16640)])
-def test_gemm_w4a8_q4k_single_row_any_header_bytes(N, K):
-    """M = 1 on planes written by the oracle's repack from random block bytes: headers with
-    binary16 NaN, infinite, subnormal and zero d and dmin, every 6-bit scale and min."""
-    rng = np.random.default_rng(N + K)
+@pytest.mark.parametrize("M,N,K", [(1, 1, 256), (1, 70, 768), (1, 33, 16384), (1, 20, 16640), (2, 70, 768),
+                                   (2, 17, 16384), (3, 41, 2560), (4, 9, 8192), (4, 20, 8448)])
+def test_gemm_w4a8_q4k_few_rows_any_header_bytes(M, N, K):
+    """1 to 4 rows on planes written by the oracle's repack from random block bytes:
+    headers with binary16 NaN, infinite, subnormal and zero d and dmin, every 6-bit scale
+    and min; a zero activation row among them."""
+    rng = np.random.default_rng(M * 100 + N + K)
     blocks = rng.integers(0, 256, N * (K // 256) * 144, dtype=np.uint8)
-    x = rng.standard_normal((1, K), dtype=np.float32)
+    x = rng.standard_normal((M, K), dtype=np.float32)
+    if M > 1:
+        x[1] = 0.0
     q_ref, sa_ref = oracle.quantize_rows(x)
     y_ref = oracle.gemm_w4a8_q4k(q_ref, sa_ref, blocks, N)
     w_ref, h_ref = oracle.repack_q4_k(blocks, N, K)

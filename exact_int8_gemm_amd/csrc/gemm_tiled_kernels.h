@@ -735,7 +735,9 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_block_kernel(const int
   int tm, tn;
   tile_of(tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // The wave index through readfirstlane: the copies' LDS destinations are
+  // then scalar (no readfirstlane per copy).
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int wm = wave / WN, wn = wave % WN;
   const int NB = K / 32;
 
@@ -743,14 +745,12 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_block_kernel(const int
   const v4i rb = rsrc_words(w + (size_t)n0 * (size_t)K, (int64_t)(N - n0) * K);
   const v4i rd = rsrc_words(d + (size_t)n0 * (size_t)NB, (int64_t)(N - n0) * NB * 2);
   uint32_t off[C::kPerWave];
-  int kc[C::kPerWave];
 #pragma unroll
   for (int s = 0; s < C::kPerWave; ++s) {
     const bool isA = s < C::kPerWaveA;
     const int copy = isA ? wave * C::kPerWaveA + s : wave * C::kPerWaveB + (s - C::kPerWaveA);
     const int row = copy * C::kRowsPerCopy + lane / C::kChunks;
     const int chunk = (lane % C::kChunks) ^ C::swz(row);
-    kc[s] = chunk * 16;
     const bool valid = isA ? (m0 + row < M) : (n0 + row < N);
     off[s] = valid ? (uint32_t)(row * K + chunk * 16) : kOutOfRange;
   }
@@ -771,7 +771,10 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_block_kernel(const int
     for (int s = 0; s < C::kPerWave; ++s) {
       const bool isA = s < C::kPerWaveA;
       const int copy = isA ? wave * C::kPerWaveA + s : wave * C::kPerWaveB + (s - C::kPerWaveA);
-      const uint32_t o = (k0 + kc[s] < K) ? off[s] + (uint32_t)k0 : kOutOfRange;
+      // No per-lane check against K: bytes past K (the next row, or zeros past
+      // the end of the buffer) only enter blocks past K, whose scales load as
+      // zero, and fmaf(P, 0, f) leaves f unchanged.
+      const uint32_t o = off[s] + (uint32_t)k0;
       const int8_t* dst = base + (isA ? 0 : BM * BK) + copy * 1024;
       copy_to_lds(isA ? ra : rb, lds_addr(dst), o);
     }
@@ -818,6 +821,10 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_block_kernel(const int
         bf[j] = *reinterpret_cast<const v4i*>(buf + brow + j * 32 * BK + c);
         const uint32_t hbits = *reinterpret_cast<const uint32_t*>(buf + kDOff + (ks * BN + ncol[j]) * 4);
         dv[j] = half_bits_to_float((uint16_t)hbits);
+        // fp32 from here on: folded into the fma as a binary16 operand, the
+        // compiler emits v_fma_mix_f32, which issues slower than v_fmac_f32
+        // (M = 2048, 17408 x 5120: 505 -> 470 us).
+        asm volatile("" : "+v"(dv[j]));
       }
       // All MFMAs of the block first, then the folds at a raised wave
       // priority: the workgroups sharing a SIMD then tend to alternate, one
@@ -952,7 +959,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_q4k_kernel(const int8_
   int tm, tn;
   tile_of(tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // scalar
   const int wm = wave / WN, wn = wave % WN;
   const int NS = K / 256;
 
@@ -961,13 +968,11 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_q4k_kernel(const int8_
   const v4i rh = rsrc_words(hdr + (size_t)n0 * (size_t)NS * 16, (int64_t)(N - n0) * NS * 16);
   // A copies: as gemm_dma_kernel.  Rows past M or N read zeros (out of range).
   uint32_t offa[C::kPerWaveA];
-  int kca[C::kPerWaveA];
 #pragma unroll
   for (int s = 0; s < C::kPerWaveA; ++s) {
     const int copy = wave * C::kPerWaveA + s;
     const int row = copy * C::kRowsPerCopy + lane / C::kChunks;
     const int chunk = (lane % C::kChunks) ^ C::swz(row);
-    kca[s] = chunk * 16;
     offa[s] = (m0 + row < M) ? (uint32_t)(row * K + chunk * 16) : kOutOfRange;
   }
   // B copies: lane -> row copy * 16 + lane / 4, LDS slot lane % 4, which holds
@@ -994,20 +999,25 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_q4k_kernel(const int8_
   }
   auto issue = [&](int8_t* base, int stage) __attribute__((always_inline)) {
     const int k0 = stage * BK;
+    // The LDS address of the stage as a scalar once (not a pointer per copy,
+    // which the compiler kept in VGPRs and read back with readfirstlane).
+    const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(base));
 #pragma unroll
     for (int s = 0; s < C::kPerWaveA; ++s) {
-      const uint32_t o = (k0 + kca[s] < K) ? offa[s] + (uint32_t)k0 : kOutOfRange;
-      copy_to_lds(ra, lds_addr(base + (wave * C::kPerWaveA + s) * 1024), o);
+      // No check against K on the operand copies: a stage past K (ring
+      // padding) meets zero headers below, so both fmas leave f unchanged.
+      const uint32_t o = offa[s] + (uint32_t)k0;
+      copy_to_lds(ra, lb + (uint32_t)((wave * C::kPerWaveA + s) * 1024), o);
     }
 #pragma unroll
     for (int s = 0; s < kPerWaveB; ++s) {
-      const uint32_t o = (k0 < K) ? offb[s] + (uint32_t)(k0 / 2) : kOutOfRange;
-      copy_to_lds(rb, lds_addr(base + kBOff + (wave * kPerWaveB + s) * 1024), o);
+      const uint32_t o = offb[s] + (uint32_t)(k0 / 2);
+      copy_to_lds(rb, lb + (uint32_t)(kBOff + (wave * kPerWaveB + s) * 1024), o);
     }
 #pragma unroll
     for (int s = 0; s < kPerWaveH; ++s) {
       const uint32_t o = (k0 < K && offh[s] != kOutOfRange) ? offh[s] + (uint32_t)(stage / 2) * 16u : kOutOfRange;
-      copy4_to_lds(rh, lds_addr(base + kHOff + (wave * kPerWaveH + s) * 256), o);
+      copy4_to_lds(rh, lb + (uint32_t)(kHOff + (wave * kPerWaveH + s) * 256), o);
     }
   };
 

@@ -918,9 +918,9 @@ void launch_block(const int8_t* q, const float* s_a, const int8_t* w, const uint
 // (32 bytes per pair of 32-k sub-blocks: byte l holds k = l in its low nibble
 // and k = 32 + l in its high one) and the 16-byte super-block headers hdr
 // [N][K/256][16] (d, dmin, 6-bit scales and mins).  Per 32-k sub-block: P =
-// sum code * a and S = sum a, both exact int32 from MFMAs started at zero (S
-// from a B operand of ones, so it lands in the same row-per-register layout
-// as P), folded in ascending sub-block order: f = fmaf((float)P, D, f);
+// sum code * a (exact int32 from an MFMA started at zero) and S = sum a (exact
+// int32, v_dot4 over the activation tile in LDS, once per workgroup and
+// stage), folded in ascending sub-block order: f = fmaf((float)P, D, f);
 // f = fmaf(-(float)S, Mn, f); y = f * s_a[m], with D = d * sc and Mn = dmin *
 // m decoded from the header (exact in fp32).
 //
@@ -929,8 +929,11 @@ void launch_block(const int8_t* q, const float* s_a, const int8_t* w, const uint
 // 4) % 4), so 16 consecutive rows reading one chunk hit 16 distinct 16-byte
 // bank groups), and the headers of the stage's super-block (one 16-byte copy
 // per column).  After a stage has landed, the workgroup decodes its BN x 4
-// (D, Mn) pairs into LDS (one barrier), then folds; the fragment reads
-// unpack the codes with one shift and mask per dword.
+// (D, Mn) pairs and computes its BM x 4 values of -S into LDS (one barrier),
+// then folds; the fragment reads unpack the codes with one shift and mask per
+// dword.  (-S from an MFMA against ones, converted per lane in every wave,
+// cost 16 converts per 32 rows and sub-block: M = 2048, 17408 x 5120, 650 ->
+// 600 us without them.)
 template <int BM, int BN, int WM, int WN, int RING, int OCC>
 __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_q4k_kernel(const int8_t* __restrict__ q,
                                                                      const float* __restrict__ s_a,
@@ -950,11 +953,13 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_q4k_kernel(const int8_
   constexpr int kBOff = BM * BK;                  // packed B within a stage
   constexpr int kHOff = kBOff + BN * (BK / 2);    // headers within a stage
   constexpr int kStage = kHOff + BN * 16;
-  static_assert(RING * kStage + 2 * KS * BN * 4 <= 160 * 1024 / OCC, "LDS");
+  static_assert(RING * kStage + 2 * KS * BN * 4 + KS * BM * 4 <= 160 * 1024 / OCC, "LDS");
+  static_assert(KS * BM % NT == 0, "-S values must divide among threads");
   __shared__ __attribute__((aligned(1024))) int8_t lds0[kStage];
   __shared__ __attribute__((aligned(1024))) int8_t lds1[kStage];
   __shared__ __attribute__((aligned(1024))) int8_t lds2[RING > 2 ? kStage : 16];
   __shared__ float dsc[KS][BN], msc[KS][BN];  // decoded D and Mn of the stage being folded
+  __shared__ __attribute__((aligned(16))) float nsc[KS][BM];  // -S of the stage's sub-blocks, per activation row
 
   int tm, tn;
   tile_of(tiles_m, tiles_n, tm, tn);
@@ -1052,10 +1057,26 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_q4k_kernel(const int8_
       dsc[ks0 + e][col] = D;
       msc[ks0 + e][col] = Mn;
     }
+    // -S of every (sub-block, row) of the stage, from the activation tile in
+    // LDS (chunk c of row r at (c ^ swz(r)) * 16): exact int32, then fp32.
+#pragma unroll
+    for (int e = 0; e < KS * BM / NT; ++e) {
+      const int idx = (int)threadIdx.x + NT * e;
+      const int ks = idx / BM, row = idx % BM;
+      const int8_t* ar = buf + row * BK;
+      const v4i x0 = *reinterpret_cast<const v4i*>(ar + ((2 * ks) ^ C::swz(row)) * 16);
+      const v4i x1 = *reinterpret_cast<const v4i*>(ar + ((2 * ks + 1) ^ C::swz(row)) * 16);
+      int t = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        t = __builtin_amdgcn_sdot4(x0[u], 0x01010101, t, false);
+        t = __builtin_amdgcn_sdot4(x1[u], 0x01010101, t, false);
+      }
+      nsc[ks][row] = -(float)t;
+    }
   };
   auto compute = [&](const int8_t* buf) __attribute__((always_inline)) {
     const v16i zero = v16i{};
-    const v4i ones = v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       // Sub-blocks past K read zero operands and zero scales: both fmas
@@ -1077,10 +1098,14 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_q4k_kernel(const int8_
       }
 #pragma unroll
       for (int i = 0; i < C::kTM; ++i) {
-        const v16i sa = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], ones, zero, 0, 0, 0);
+        // -S of this lane's 16 rows (rows 8 (r / 4) + 4 (lane / 32) + r % 4 of the tile)
         float ns[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ns[r] = -(float)sa[r];
+        for (int g = 0; g < 4; ++g) {
+          const v4f v = *reinterpret_cast<const v4f*>(&nsc[ks][wm * C::kWTM + i * 32 + 8 * g + 4 * (lane >> 5)]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ns[4 * g + e] = v[e];
+        }
 #pragma unroll
         for (int j = 0; j < C::kTN; ++j) {
           const v16i p = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], zero, 0, 0, 0);

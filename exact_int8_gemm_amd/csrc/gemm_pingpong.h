@@ -42,6 +42,8 @@
 // 202 at M = 8192).
 #pragma once
 
+#include <type_traits>
+
 #include "gemm_tiled_kernels.h"
 
 namespace prism {
@@ -101,7 +103,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
   static_assert(!W4 || BK == 128, "W4: 128-k stages");
   static_assert(kLds <= 160 * 1024, "LDS exceeds 160 KiB");
   __shared__ __attribute__((aligned(1024))) int8_t lds[kLds];
-  __shared__ float sa_l[BM], sw_l[BN];
+  __shared__ __attribute__((aligned(16))) float sa_l[BM];
+  __shared__ float sw_l[BN];
 
   // This workgroup's tiles: t, t + g, ... below t_end.
   const int T = tiles_m * tiles_n;
@@ -302,26 +305,50 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
       else sw_l[i - BM] = n0 + i - BM < N ? s_w[n0 + i - BM] : 0.0f;
     }
     __syncthreads();
-    const int mb = m0 + wm * 64, nb = n0 + grp * (BN / 2);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = nb + j * 32 + rl;
-      if (n >= N) continue;
-      const float swn = sw_l[n - n0];
+    // Register r of tile (i, j) holds row mr + (r / 4) * 8 + r % 4, mr = mb +
+    // 32 i + 4 (lane / 32), column nb + 32 j + lane % 32.  Interior tiles
+    // (every tile of most shapes) store without per-element bounds checks.
+    const int mb = m0 + wm * 64 + (lane >> 5) * 4, nb = n0 + grp * (BN / 2);
+    const bool full = m0 + BM <= M && n0 + BN <= N;
+    auto epilogue = [&](auto with_acc, auto checked) __attribute__((always_inline)) {
+      constexpr bool ACC = decltype(with_acc)::value, CHK = decltype(checked)::value;
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
+        const int mr = mb + i * 32;
+        float sa[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = mb + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          if (m < M) {
+        for (int g = 0; g < 4; ++g) {
+          const v4f v = *reinterpret_cast<const v4f*>(sa_l + (mr - m0) + 8 * g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sa[4 * g + e] = v[e];
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int n = nb + j * 32 + rl;
+          if (CHK && n >= N) continue;
+          const float swn = sw_l[n - n0];
+          float* yp = y + (size_t)mr * (size_t)N + (size_t)n;
+          int32_t* ap = ACC ? acc_out + (size_t)mr * (size_t)N + (size_t)n : nullptr;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int dr = (r >> 2) * 8 + (r & 3);
+            if (CHK && mr + dr >= M) continue;
             const int a = W4 ? acc[i][j][r] >> 4 : acc[i][j][r];  // exact: 16 w sums to a multiple of 16
-            const size_t o = (size_t)m * (size_t)N + (size_t)n;
-            if (acc_out) __builtin_nontemporal_store(a, acc_out + o);
-            const float tv = (float)a * sa_l[m - m0];
-            __builtin_nontemporal_store(tv * swn, y + o);
+            if constexpr (ACC) __builtin_nontemporal_store(a, ap + (size_t)dr * (size_t)N);
+            const float tv = (float)a * sa[r];
+            __builtin_nontemporal_store(tv * swn, yp + (size_t)dr * (size_t)N);
           }
         }
       }
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    if (acc_out) {
+      if (full) epilogue(T_{}, F_{});
+      else epilogue(T_{}, T_{});
+    } else {
+      if (full) epilogue(F_{}, F_{});
+      else epilogue(F_{}, T_{});
     }
     if (!has_next) break;
     t = t_next;

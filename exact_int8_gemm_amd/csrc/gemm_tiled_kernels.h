@@ -327,53 +327,83 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_tiled_kernel(const int
   }
 
   const int rl = lane & 31;
+  // Register r of tile (i, j) holds row mb + 32 i + (r / 4) * 8 + r % 4 and
+  // column nb + 32 j; interior tiles store without per-element bounds checks.
+  const int mb = m0 + wm * G::kWTM + (lane >> 5) * 4, nb = n0 + wn * G::kWTN + rl;
+  const bool full = m0 + BM <= M && n0 + BN <= N;
   if (splits > 1) {
     int32_t* yi = reinterpret_cast<int32_t*>(y);
+    auto partial = [&](auto checked) __attribute__((always_inline)) {
+      constexpr bool CHK = decltype(checked)::value;
 #pragma unroll
-    for (int j = 0; j < G::kTN; ++j) {
-      const int n = n0 + wn * G::kWTN + j * 32 + rl;
-      if (n >= N) continue;
+      for (int j = 0; j < G::kTN; ++j) {
+        const int n = nb + j * 32;
+        if (CHK && n >= N) continue;
 #pragma unroll
-      for (int i = 0; i < G::kTM; ++i)
+        for (int i = 0; i < G::kTM; ++i) {
+          const int mr = mb + i * 32;
+          int32_t* p = yi + (size_t)mr * (size_t)N + (size_t)n;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm * G::kWTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const int a = W4 ? (acc[i][j][r] >> 4) : acc[i][j][r];  // exact: each 4-bit partial is a multiple of 16
-          if (m < M)
-            __hip_atomic_fetch_add(yi + (size_t)m * (size_t)N + (size_t)n, a, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+          for (int r = 0; r < 16; ++r) {
+            const int dr = (r >> 2) * 8 + (r & 3);
+            if (CHK && mr + dr >= M) continue;
+            const int a = W4 ? (acc[i][j][r] >> 4) : acc[i][j][r];  // exact: each 4-bit partial is a multiple of 16
+            __hip_atomic_fetch_add(p + (size_t)dr * (size_t)N, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
         }
-    }
+      }
+    };
+    if (full) partial(std::false_type{});
+    else partial(std::true_type{});
     return;
   }
   // The tile's row and column scales, loaded once into LDS instead of per
   // element inside the store loop (as in the direct-to-LDS kernels).
-  __shared__ float sa_l[BM], sw_l[BN];
+  __shared__ __attribute__((aligned(16))) float sa_l[BM];
+  __shared__ float sw_l[BN];
   for (int t = threadIdx.x; t < BM + BN; t += G::kNT) {
     if (t < BM) sa_l[t] = m0 + t < M ? s_a[m0 + t] : 0.0f;
     else sw_l[t - BM] = n0 + t - BM < N ? s_w[n0 + t - BM] : 0.0f;
   }
   __syncthreads();
-#pragma unroll
-  for (int j = 0; j < G::kTN; ++j) {
-    const int n = n0 + wn * G::kWTN + j * 32 + rl;
-    if (n >= N) continue;
-    const float sw = sw_l[n - n0];
+  auto epilogue = [&](auto with_acc, auto checked) __attribute__((always_inline)) {
+    constexpr bool ACC = decltype(with_acc)::value, CHK = decltype(checked)::value;
 #pragma unroll
     for (int i = 0; i < G::kTM; ++i) {
+      const int mr = mb + i * 32;
+      float sa[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * G::kWTM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (m < M) {
+      for (int g = 0; g < 4; ++g) {
+        const v4f v = *reinterpret_cast<const v4f*>(sa_l + (mr - m0) + 8 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sa[4 * g + e] = v[e];
+      }
+#pragma unroll
+      for (int j = 0; j < G::kTN; ++j) {
+        const int n = nb + j * 32;
+        if (CHK && n >= N) continue;
+        const float sw = sw_l[n - n0];
+        float* yp = y + (size_t)mr * (size_t)N + (size_t)n;
+        int32_t* ap = ACC ? acc_out + (size_t)mr * (size_t)N + (size_t)n : nullptr;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int dr = (r >> 2) * 8 + (r & 3);
+          if (CHK && mr + dr >= M) continue;
           int a = acc[i][j][r];
           if (W4) a >>= 4;  // exact: the sum is a multiple of 16
-          const size_t o = (size_t)m * (size_t)N + (size_t)n;
-          if (acc_out) acc_out[o] = a;
-          const float t = (float)a * sa_l[m - m0];
-          y[o] = t * sw;
+          if constexpr (ACC) ap[(size_t)dr * (size_t)N] = a;
+          const float t = (float)a * sa[r];
+          yp[(size_t)dr * (size_t)N] = t * sw;
         }
       }
     }
+  };
+  if (acc_out) {
+    if (full) epilogue(std::true_type{}, std::false_type{});
+    else epilogue(std::true_type{}, std::true_type{});
+  } else {
+    if (full) epilogue(std::false_type{}, std::false_type{});
+    else epilogue(std::false_type{}, std::true_type{});
   }
 }
 

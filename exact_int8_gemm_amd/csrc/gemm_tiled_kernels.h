@@ -962,19 +962,23 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_block_kernel(const int
 
 // The partial-sum output (a debugging aid) is a separate instantiation, so
 // that the hot loop of the plain call carries no per-block stores.
-template <int BM, int BN, int WM, int WN, int RING, int OCC>
+template <int BM, int BN, int WM, int WN, int RING, int OCC, bool WITH_PARTIALS = true>
 void launch_block(const int8_t* q, const float* s_a, const int8_t* w, const uint16_t* d, float* y, int32_t* partials,
                   int M, int N, int K, hipStream_t st) {
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   // The variant that also stores every block partial keeps more values live
   // (the partial tiles and their addresses); it is built for one workgroup
   // per CU so that it has the register file to itself and does not spill.
-  if (partials)
-    gemm_block_kernel<BM, BN, WM, WN, RING, 1, true><<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, 0, st>>>(
-        q, s_a, w, d, y, partials, M, N, K, tiles_m, tiles_n);
-  else
-    gemm_block_kernel<BM, BN, WM, WN, RING, OCC, false><<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, 0, st>>>(
-        q, s_a, w, d, y, nullptr, M, N, K, tiles_m, tiles_n);
+  // WITH_PARTIALS = false: that variant is not built (partials must be null).
+  if constexpr (WITH_PARTIALS) {
+    if (partials) {
+      gemm_block_kernel<BM, BN, WM, WN, RING, 1, true><<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, 0, st>>>(
+          q, s_a, w, d, y, partials, M, N, K, tiles_m, tiles_n);
+      return;
+    }
+  }
+  gemm_block_kernel<BM, BN, WM, WN, RING, OCC, false><<<(unsigned)(tiles_m * tiles_n), 64 * WM * WN, 0, st>>>(
+      q, s_a, w, d, y, nullptr, M, N, K, tiles_m, tiles_n);
 }
 
 // Q4_K-native W4A8 on the repacked planes: packed 4-bit codes w4 [N][K/2]

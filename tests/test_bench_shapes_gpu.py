@@ -91,3 +91,33 @@ def test_q4k_full_size(M):
     y_ref = oracle.gemm_w4a8_q4k(q_ref[rows], s_ref[rows], blocks, N)
     assert np.isfinite(y_ref).all()
     assert_same_floats(y[rows], y_ref, "y")
+
+
+def test_block_scale_large_tiles_ragged():
+    """Block-scale with enough 128 x 128 tiles for the eight-wave tiles (M = 2113, N =
+    16416: ragged last row and column tiles) and K = 288 (a last stage of one block):
+    sampled rows, every column, against the oracle."""
+    M, N, K = 2113, 16416, 288
+    rng = np.random.default_rng(31)
+    q = rng.integers(-128, 128, (M, K), dtype=np.int8)
+    s_a = rng.uniform(1e-3, 1e-1, M).astype(np.float32)
+    w = rng.integers(-128, 128, (N, K), dtype=np.int8)
+    d = rng.uniform(1e-4, 1e-2, (N, K // 32)).astype(np.float16).view(np.uint16)
+    y = host(prism.gemm_w8a8_blockscale(dev(q), dev(s_a), dev(w), dev(d)))
+    rows = _rows(M, 3)
+    y_ref, _ = oracle.gemm_w8a8_blockscale(q[rows], s_a[rows], w, d)
+    assert_same_floats(y[rows], y_ref, "y sampled rows")
+
+
+def test_q4k_large_tiles_ragged():
+    """Q4_K with enough 128 x 128 tiles for the eight-wave tiles (M = 1100, N = 16400:
+    ragged last tiles): sampled rows, every column, against the oracle."""
+    M, N, K = 1100, 16400, 256
+    blocks = _q4k_blocks(33, N, K)
+    w4, hdr = prism.repack_q4_k(dev(blocks), N, K)
+    x = np.random.default_rng(34).standard_normal((M, K), dtype=np.float32)
+    q, s, q_ref, s_ref = _quantize_both(x)
+    y = host(prism.gemm_w4a8_q4k(q, s, w4, hdr))
+    rows = _rows(M, 5)
+    y_ref = oracle.gemm_w4a8_q4k(q_ref[rows], s_ref[rows], blocks, N)
+    assert_same_floats(y[rows], y_ref, "y sampled rows")

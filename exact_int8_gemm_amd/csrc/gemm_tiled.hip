@@ -258,8 +258,13 @@ int launch_gemm_blockscale(const int8_t* q, const float* s_a, const int8_t* w, c
   // us; at M = 512 the larger tiles took 145 against 120-126 us.  The variant
   // that also stores every block sum keeps the smaller tiles (the larger
   // ones would spill it).
+  // Up to 64 rows, 64 x 64 tiles of four waves (four workgroups per CU): the
+  // fold then runs on at most 63 rows past M instead of 111 (M = 17: 46 -> 41
+  // us, M = 64: 51 -> 47 us; from M = 96 on they are slower).
   const int64_t tiles128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
-  if (!partials && tiles128 >= 4 * 2 * (int64_t)tiled::dma::device_cus())
+  if (M <= 64)
+    tiled::dma::launch_block<64, 64, 2, 2, 2, 4>(q, s_a, w, d, y, partials, M, N, K, st);
+  else if (!partials && tiles128 >= 4 * 2 * (int64_t)tiled::dma::device_cus())
     tiled::dma::launch_block<128, 128, 4, 2, 2, 2, false>(q, s_a, w, d, y, nullptr, M, N, K, st);
   else
     tiled::dma::launch_block<128, 64, 2, 2, 2, 3>(q, s_a, w, d, y, partials, M, N, K, st);
@@ -274,16 +279,17 @@ int launch_gemm_q4k(const int8_t* q, const float* s_a, const uint8_t* w4, const 
   if (M <= kBlockSmallMMax)
     return launch_gemm_block_small(q, s_a, reinterpret_cast<const int8_t*>(w4), nullptr, hdr, y, M, N, K, st);
   // 128 x 128 tiles of eight waves (32 x 64 each, two workgroups per CU) when
-  // they fill at least two rounds of the CUs' workgroup slots, else 128 x 64
-  // tiles of four waves (three workgroups per CU), whose more numerous tiles
-  // fill the CUs better.  MI355X, 17408 x 5120, against 128 x 128 tiles of
-  // four waves: M = 256 146 -> 115 us, 512 220 -> 180, 1024 339 -> 313, 2048
-  // 589 -> 561, 4096 1109 -> 1086.
+  // they fill at least two rounds of the CUs' workgroup slots, else 64 x 64
+  // tiles of four waves (four workgroups per CU): few rows then waste less of
+  // the per-block fold on rows past M, and the more numerous tiles fill the
+  // CUs.  MI355X, 17408 x 5120, against 128 x 128 tiles of four waves: M = 17
+  // 80 -> 47 us, 128 83 -> 64, 256 109 -> 98, 512 220 -> 172, 1024 339 ->
+  // 313, 2048 589 -> 561, 4096 1109 -> 1086.
   const int64_t tiles128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
   if (tiles128 >= 2 * 2 * (int64_t)tiled::dma::device_cus())
     tiled::dma::launch_q4k<128, 128, 4, 2, 2, 2>(q, s_a, w4, hdr, y, M, N, K, st);
   else
-    tiled::dma::launch_q4k<128, 64, 2, 2, 2, 3>(q, s_a, w4, hdr, y, M, N, K, st);
+    tiled::dma::launch_q4k<64, 64, 2, 2, 2, 4>(q, s_a, w4, hdr, y, M, N, K, st);
   return launch_status();
 }
 

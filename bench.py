@@ -366,13 +366,8 @@ def kernels(torch, prism, wl, only=None):
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
         t1, t = _time_launches(torch, [L.block(q, sa, w, d, y) for w, d in ws], 10)
         ops = 2 * M * N * K
-        # VALU bound of the block epilogue: one int32 -> fp32 convert and one fp32 fma per
-        # 32-k partial; a wave64 fma occupies a SIMD for 4 cycles and a convert for 2
-        # (measured on MI355X), i.e. 6 cycles per 64 partials on each of 1024 SIMDs at 2.4 GHz
-        valu_s = M * N * (K // 32) * 6 / 64 / (1024 * 2.4e9)
         out["block_scale_m2048"] = dict(us=t * 1e6, tops=ops / t / 1e12, mfma_frac=ops / t / 1e12 / PEAK_INT8_TOPS,
-                                        valu_bound_us=valu_s * 1e6, valu_frac=valu_s / t, us_single_launch=t1 * 1e6,
-                                        copies=R)
+                                        us_single_launch=t1 * 1e6, copies=R)
         # decode: one row through the small-M block kernel (HBM-bound: weights and scales)
         q1, sa1, y1 = q[:1].contiguous(), sa[:1].contiguous(), torch.empty((1, N), dtype=torch.float32, device=dev)
         t1, t = _time_launches(torch, [L.block(q1, sa1, w, d, y1) for w, d in ws], 50)
@@ -532,6 +527,17 @@ def kernels(torch, prism, wl, only=None):
                                us_single_launch=t1 * 1e6, gbs_single_launch=nbytes / t1 / 1e9, copies=R)
             del bufs
         out["peaks"] = peaks
+        # The block fold's floor from the measurement kernel: per SIMD, each 32-k
+        # block of a 32 x 32 tile costs one int8 MFMA, 16 converts and 16 fmaf
+        # (block-scale), plus 16 more fmaf for the Q4_K min term; the two
+        # tiled GEMMs at M = 2048 do (M/32)(N/32)(K/32) / 1024 of them per SIMD.
+        ns_fold = peaks["fold_i8_mfma_cvt_fold"]["ns_per_tile_block_per_simd"]
+        ns_fma = peaks["fold_fold_only"]["ns_per_tile_block_per_simd"]
+        per_simd = (2048 // 32) * (17408 // 32) * (5120 // 32) / 1024
+        for name, ns in (("block_scale_m2048", ns_fold), ("q4k_m2048", ns_fold + ns_fma)):
+            if name in out:
+                floor_us = per_simd * ns / 1e3
+                out[name].update(fold_floor_us=floor_us, fold_floor_frac=floor_us / out[name]["us"])
     if only == "sweep":
         # Not in the default run: the per-channel W8A8 GEMM across M at
         # N = K = 5120 (the plain call's own kernel choice at each M), next to

@@ -37,15 +37,46 @@ using tiled::launch_tiled;
 inline int64_t tiles(int64_t M, int64_t N, int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
 
 // 4-bit weights (unpacked on the way into LDS, so a stage costs more and the
-// int8 fit below does not carry over): floor(256 / t) workgroups per tile, at
-// most 4, each with at least 8 stages of 128 k.
-int split_int4(int64_t t, int K) {
+// int8 fit below does not carry over): 128 x 128 or 64 x 128 tiles of 8
+// waves, two workgroups per CU, K split over s = 1..4 workgroups (each with
+// at least 8 stages of 128 k).  Cost model fitted on MI355X (N x K = 12288 x
+// 4096 at M = 65..256; 4096 x 4096, 2560 x 9728 and 28672 x 4096 at M = 96
+// and 128; 28672 x 14336 at M = 16): per stage of a workgroup alone on its
+// CU about 0.72 us for 128 x 128 and 0.53 us for 64 x 128, with two
+// workgroups per CU about 0.80 and 0.78 us each (the second one hides part
+// of the first one's load latency), times the stages per workgroup and the
+// rounds of 512 workgroups; for s > 1 plus the fill, the atomic partial
+// tiles and the epilogue kernel, about 5 us and 3 us per split and million
+// outputs.  Ties go to 128 x 128 and the smaller split.  E.g. 12288 x 4096:
+// M = 128 takes 64 x 128 unsplit (26.3 -> 16.8 us against 128 x 128 split
+// in two); M = 96, N = K = 4096: 64 x 128, 4 ways (15.2 -> 13.8 us); M =
+// 128, N = 28672: 128 x 128 unsplit (26.7 us against 29.7); M = 16, N x K =
+// 28672 x 14336: 64 x 128, 2 ways (61.0 -> 51.3 us).
+struct SplitChoice {
+  int tile;    // 0: 128 x 128, 1: 64 x 128 (int8 only: 2: 128 x 96)
+  int splits;  // 1..4
+};
+
+SplitChoice split_int4(int64_t M, int64_t N, int K) {
   const int64_t stages = (K + 127) / 128;
-  int64_t splits = 256 / t;
-  if (splits > 4) splits = 4;
-  if (splits > stages / 8) splits = stages / 8;
-  if (splits < 1) splits = 1;
-  return (int)splits;
+  static constexpr int kBm[2] = {128, 64};
+  static constexpr double kAlone[2] = {0.72, 0.53}, kShared[2] = {0.80, 0.78};
+  SplitChoice best{0, 1};
+  double best_cost = 0.0;
+  for (int i = 0; i < 2; ++i) {
+    const int64_t t = tiles(M, N, kBm[i], 128);
+    for (int s = 1; s <= 4 && (s == 1 || stages / s >= 8); ++s) {
+      const int64_t wgs = t * s;
+      const double per_stage = wgs <= 256 ? kAlone[i] : kShared[i] * (double)((wgs + 511) / 512);
+      double cost = per_stage * (double)((stages + s - 1) / s);
+      if (s > 1) cost += 5.0 + 3.0 * (double)s * (double)(M * N) * 1e-6;
+      if ((i == 0 && s == 1) || cost < best_cost) {
+        best = SplitChoice{i, s};
+        best_cost = cost;
+      }
+    }
+  }
+  return best;
 }
 
 // Tile (128 x 128, 64 x 128 or 128 x 96) and K split s in 1..4 of the int8
@@ -63,17 +94,17 @@ int split_int4(int64_t t, int K) {
 // M = 512, N = K = 2560: 64 x 128, no split, 11 us (128 x 128: 16 us);
 // M = 512, N = K = 5120: 128 x 96, no split, 31 us; M = 512, N = 2560,
 // K = 9728: 128 x 128, 3 ways, 36 us.
-struct SplitChoice {
-  int tile;    // 0: 128 x 128, 1: 64 x 128, 2: 128 x 96
-  int splits;  // 1..4
-};
-
 SplitChoice split_for(int64_t M, int64_t N, int K) {
   struct Shape {
     int bm, bn, max_splits;
     double per_stage;
   };
-  static constexpr Shape kShapes[3] = {{128, 128, 4, 0.80}, {64, 128, 4, 0.60}, {128, 96, 2, 0.78}};
+  // One row of 64 x 128 tiles (M <= 64) shares its few activation rows
+  // through L2: about 0.40 us per stage up to 32 rows and 0.50 up to 64 (N
+  // from 2560 to 28672; e.g. M = 64, N x K = 16384 x 9728 then splits in two,
+  // 42.5 -> 36.5 us).
+  const double per_stage_64 = M <= 32 ? 0.40 : M <= 64 ? 0.50 : 0.60;
+  const Shape kShapes[3] = {{128, 128, 4, 0.80}, {64, 128, 4, per_stage_64}, {128, 96, 2, 0.78}};
   const int64_t stages = (K + 127) / 128;
   SplitChoice best{0, 1};
   double best_cost = 0.0;
@@ -152,8 +183,10 @@ void pick_int8(const int8_t* q, const float* s_a, const int8_t* w, const float* 
 //    copied to LDS as they are (256 x 192, 256 x 256 or 256 x 320);
 //  * a register-staged pipeline that unpacks the nibbles on their way into
 //    LDS: 128 x 128 tiles of 8 waves (32 x 64 each; 4-20% faster than 4 waves
-//    of 64 x 64, e.g. M = 256, N = K = 5120: 38.5 -> 30.3 us), two workgroups
-//    per CU, with K split (split_int4) when there are fewer tiles than CUs.
+//    of 64 x 64, e.g. M = 256, N = K = 5120: 38.5 -> 30.3 us) or 64 x 128
+//    tiles of 8 waves (32 x 32 each; 8 waves of 64 x 32 took 20-21 against
+//    17 us at M = 65..128 on 12288 x 4096), two workgroups per CU, tile and
+//    K split from split_int4.
 // Estimate per 256-row round of tiles as for int8 (0.83, 1 and 1.23 for the
 // three widths), against 0.63 per 512 tiles (at least one round) for
 // 128 x 128, from N x K = 12288 x 4096 on MI355X: M = 512: 44.4 us on
@@ -176,8 +209,9 @@ void pick_int4(const int8_t* q, const float* s_a, const int8_t* w, const float* 
     else tiled::dma::launch_pp<128, 320, 1, true>(q, s_a, w, s_w, y, acc, M, N, K, st);
     return;
   }
-  launch_tiled<128, 128, 128, 4, 2, true, 2>(q, s_a, w, s_w, y, acc, M, N, K, st,
-                                              split_int4(tiles(M, N, 128, 128), K));
+  const SplitChoice c = split_int4(M, N, K);
+  if (c.tile == 1) launch_tiled<64, 128, 128, 2, 4, true, 2>(q, s_a, w, s_w, y, acc, M, N, K, st, c.splits);
+  else launch_tiled<128, 128, 128, 4, 2, true, 2>(q, s_a, w, s_w, y, acc, M, N, K, st, c.splits);
 }
 
 }  // namespace
@@ -186,7 +220,7 @@ void pick_int4(const int8_t* q, const float* s_a, const int8_t* w, const float* 
 // 128 x 128 with K split over 1..4 workgroups, 17: 256 x 192, 18: 256 x 320,
 // 19..22: 64 x 128 with K split over 1..4 workgroups, 23, 24: 128 x 96 with
 // K split over 1, 2 workgroups, 26: 192 x 128; the 4-bit path has 7, 9..12,
-// 17 and 18).
+// 17, 18 and 19..22).
 int launch_gemm_tiled_variant(const int8_t* q, const float* s_a, const void* w, bool w_is_int4, const float* s_w,
                               float* y, int32_t* acc, int M, int N, int K, int variant, hipStream_t st) {
   const int8_t* wb = static_cast<const int8_t*>(w);
@@ -197,11 +231,13 @@ int launch_gemm_tiled_variant(const int8_t* q, const float* s_a, const void* w, 
       else tiled::dma::launch_pp<128, 320, 1, true>(q, s_a, wb, s_w, y, acc, M, N, K, st);
       return launch_status();
     }
-    if (variant < 9 || variant > 12) return PRISM_ERR_INVALID_ARG;  // 128 x 128 only
+    const bool t64 = variant >= 19 && variant <= 22;
+    if (!t64 && (variant < 9 || variant > 12)) return PRISM_ERR_INVALID_ARG;  // 128 x 128 or 64 x 128 only
     const int stages = (K + 127) / 128;
-    int splits = variant - 8;
+    int splits = t64 ? variant - 18 : variant - 8;
     if (splits > stages) splits = stages;
-    launch_tiled<128, 128, 128, 4, 2, true, 2>(q, s_a, wb, s_w, y, acc, M, N, K, st, splits);
+    if (t64) launch_tiled<64, 128, 128, 2, 4, true, 2>(q, s_a, wb, s_w, y, acc, M, N, K, st, splits);
+    else launch_tiled<128, 128, 128, 4, 2, true, 2>(q, s_a, wb, s_w, y, acc, M, N, K, st, splits);
     return launch_status();
   }
   if (variant == 7) {

@@ -73,14 +73,33 @@ int check_gemm(const void* q, const void* s_a, const void* w, const void* scale_
 bool grid_fits(int64_t M, int64_t N) { return ((M + 63) / 64) * ((N + 127) / 128) * 4 <= INT_MAX; }
 
 // The small-M kernel re-reads the whole M x K activation block in every
-// workgroup.  With int8 weights, from 32 rows and 240 KiB of activations
-// (M K >= 245760) the 64 x 128 tiles of the tiled path are faster (M = 32,
-// 48, 64 and N, K in {2560, 5120, 9728} on MI355X: e.g. M = 64, N = 5120,
-// K = 9728: 19.9 us against 30.7; M = 64, N = K = 2560 stays small-M: 8.5 us
-// against 10.7).  4-bit weights always take the small-M kernel up to 64 rows.
-bool use_small(int64_t M, int64_t K, bool w4) {
+// workgroup, so from some rows on the 64 x 128 tiles of the tiled path (K
+// split by their cost model) are faster.  Where, measured on MI355X with
+// graph-replayed launches (M = 8, 16, 24, 32, 48, 64; N in {2560, 5120,
+// 9728, 12288, 16384, 18432, 28672}; K in {2560, 4096, 5120, 9728, 14336}):
+//  * N > 16384 (no even column share per CU fits the small-M kernel, whose
+//    16-column blocks then run in several rounds): from 8 rows with int8
+//    weights, 16 with 4-bit ones (e.g. int8 18432 x 5120, M = 16: 25.7 ->
+//    17.2 us; 4-bit 28672 x 4096, M = 48: 55.4 -> 18.0 us);
+//  * int8 weights: from 24 rows where N K >= 40 Mi (16384 x 4096, M = 24:
+//    16.4 -> 13.8 us; 9728 x 4096 stays small-M: 11.8 against 12.9), from
+//    48 rows where N K >= 8 Mi (9728 x 2560, M = 48: 12.0 -> 10.4 us;
+//    2560 x 2560 stays: 7.6 against 9.0), and from 32 rows where M K >=
+//    245760 (2560 x 9728, M = 32: 15.4 -> 13.0 us);
+//  * 4-bit weights: from 48 rows where M K >= 393216 (5120 x 9728, M = 48:
+//    22.3 -> 17.0 us; 12288 x 5120, M = 64 stays: 18.4 against 19.3) and
+//    from 32 rows where N K >= 128 Mi (12288 x 14336, M = 32: 28.4 ->
+//    27.0 us).
+bool use_small(int64_t M, int64_t N, int64_t K, bool w4) {
   if (M > prism::kSmallMMax) return false;
-  return w4 || M < 32 || M * K < 245760;
+  const int64_t nk = N * K;
+  if (w4) {
+    if (N > 16384) return M < 16;
+    return !((M >= 48 && M * K >= 393216) || (M >= 32 && nk >= (int64_t)128 << 20));
+  }
+  if (N > 16384) return M < 8;
+  return !((M >= 24 && nk >= (int64_t)40 << 20) || (M >= 48 && nk >= (int64_t)8 << 20) ||
+           (M >= 32 && M * K >= 245760));
 }
 
 // Variant dispatch shared by the two _variant calls (arguments already checked).
@@ -89,7 +108,7 @@ int run_variant(const int8_t* q, const float* s_a, const void* w, bool w4, const
   static const int kSmall[7][2] = {{0, 0}, {1, 4}, {1, 8}, {1, 16}, {2, 4}, {2, 8}, {2, 16}};
   static const int kSmallWide[4][2] = {{3, 4}, {3, 8}, {4, 4}, {4, 8}};
   if (variant == PRISM_VARIANT_AUTO) {
-    if (use_small(M, K, w4)) return prism::launch_gemm_small(q, s_a, w, w4, s_w, y, acc, (int)M, (int)N, (int)K, s);
+    if (use_small(M, N, K, w4)) return prism::launch_gemm_small(q, s_a, w, w4, s_w, y, acc, (int)M, (int)N, (int)K, s);
     return prism::launch_gemm_tiled(q, s_a, w, w4, s_w, y, acc, (int)M, (int)N, (int)K, s);
   }
   if (variant >= PRISM_VARIANT_SMALL_1x4 && variant <= PRISM_VARIANT_SMALL_2x16) {
@@ -201,7 +220,7 @@ int prism_gemm_w8a8(const int8_t* q, const float* s_a, const int8_t* w, const fl
   if (!grid_fits(M, N)) return PRISM_ERR_INVALID_ARG;
   if ((st = check_device()) != PRISM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (use_small(M, K, false))
+  if (use_small(M, N, K, false))
     return prism::launch_gemm_small(q, s_a, w, false, s_w, y, acc, (int)M, (int)N, (int)K, s);
   return prism::launch_gemm_tiled(q, s_a, w, false, s_w, y, acc, (int)M, (int)N, (int)K, s);
 }
@@ -222,7 +241,7 @@ int prism_quantize_gemm_w8a8(const float* x, int8_t* q, float* scale, const int8
       prism::launch_quantize_gemm_small(x, q, scale, w, s_w, y, acc, (int)M, (int)N, (int)K, s))
     return prism::launch_status();
   if ((st = prism::launch_quantize_rows(x, q, scale, M, K, s)) != PRISM_OK) return st;
-  if (use_small(M, K, false))
+  if (use_small(M, N, K, false))
     return prism::launch_gemm_small(q, scale, w, false, s_w, y, acc, (int)M, (int)N, (int)K, s);
   return prism::launch_gemm_tiled(q, scale, w, false, s_w, y, acc, (int)M, (int)N, (int)K, s);
 }
@@ -236,7 +255,7 @@ int prism_gemm_w4a8(const int8_t* q, const float* s_a, const uint8_t* w4, const 
   if (!grid_fits(M, N)) return PRISM_ERR_INVALID_ARG;
   if ((st = check_device()) != PRISM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (use_small(M, K, true)) return prism::launch_gemm_small(q, s_a, w4, true, s_w, y, acc, (int)M, (int)N, (int)K, s);
+  if (use_small(M, N, K, true)) return prism::launch_gemm_small(q, s_a, w4, true, s_w, y, acc, (int)M, (int)N, (int)K, s);
   return prism::launch_gemm_tiled(q, s_a, w4, true, s_w, y, acc, (int)M, (int)N, (int)K, s);
 }
 

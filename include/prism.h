@@ -228,9 +228,9 @@ int prism_gemm_w4a8(const int8_t* q, const float* s_a, const uint8_t* w4, const 
  *                                 (M <= 64 only);
  *   PRISM_VARIANT_SMALL_BALANCED  the small-M kernel with one even share of
  *                                 the N columns per CU (M <= 64, N <= 16384);
- *   PRISM_VARIANT_TILE_*          the LDS-tiled kernels: 256x128, 192x128,
- *                                 64x128 and 128x96 (int8 weights only),
- *                                 256x192, 256x256, 256x320 and 128x128, and
+ *   PRISM_VARIANT_TILE_*          the LDS-tiled kernels: 256x128, 192x128
+ *                                 and 128x96 (int8 weights only), 256x192,
+ *                                 256x256, 256x320, 128x128 and 64x128, and
  *                                 128x128 or 64x128 with K split over 2, 3 or
  *                                 4 workgroups, 128x96 over 2, whose exact
  *                                 int32 partials are added atomically into y.

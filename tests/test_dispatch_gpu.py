@@ -23,7 +23,7 @@ TILES8 = ["tile_256x256", "tile_256x192", "tile_256x320", "tile_256x128", "tile_
           "tile_128x128_split3", "tile_128x128_split4", "tile_64x128", "tile_64x128_split2", "tile_64x128_split3",
           "tile_64x128_split4", "tile_128x96", "tile_128x96_split2", "tile_192x128"]
 TILES4 = ["tile_256x256", "tile_256x192", "tile_256x320", "tile_128x128", "tile_128x128_split2", "tile_128x128_split3",
-          "tile_128x128_split4"]
+          "tile_128x128_split4", "tile_64x128", "tile_64x128_split2", "tile_64x128_split3", "tile_64x128_split4"]
 
 
 def _inputs(seed, M, N, K, w4=False):
@@ -87,9 +87,9 @@ def test_w4a8_every_entry(M, N, K):
 @pytest.mark.parametrize("M,K", [(31, 9728), (32, 7664), (32, 7680), (48, 5104), (48, 5120), (64, 3824), (64, 3840),
                                  (64, 9728)])
 def test_w8a8_small_m_or_tiled(M, K):
-    """With int8 weights, 32 <= M <= 64 rows take the tiled path (64 x 128 or
-    128 x 128 tiles, K split by the cost model) once M K >= 245760, the
-    small-M kernel below that; the plain call must give the oracle's bits on
+    """With int8 weights and few columns, 32 <= M <= 64 rows take the tiled
+    path (64 x 128 or 128 x 128 tiles, K split by the cost model) once M K >=
+    245760, the small-M kernel below that; the plain call must give the oracle's bits on
     both sides of the boundary, and so must every small-M and tiled entry."""
     N = 300
     q, s_a, w, s_w = _inputs(M * 11 + K, M, N, K)
@@ -97,6 +97,25 @@ def test_w8a8_small_m_or_tiled(M, K):
     names = ["auto"] + SMALL + [n for n in TILES8 if "128" in n]
     _run_all(prism.gemm_w8a8_variant, names, dev(q), dev(s_a), dev(w), dev(s_w), y_ref, acc_ref)
     y = prism.gemm_w8a8(dev(q), dev(s_a), dev(w), dev(s_w))
+    torch.cuda.synchronize()
+    assert_same_floats(host(y), y_ref, "y (plain call)")
+
+
+@pytest.mark.parametrize("w4,M,N,K", [(False, 7, 16400, 256), (False, 8, 16400, 256), (True, 15, 16416, 256),
+                                      (True, 16, 16416, 256), (False, 23, 10240, 4096), (False, 24, 10240, 4096),
+                                      (False, 47, 2048, 4096), (False, 48, 2048, 4096), (True, 47, 1024, 8192),
+                                      (True, 48, 1024, 8192), (True, 32, 8192, 16384)])
+def test_small_m_or_tiled_boundaries(w4, M, N, K):
+    """Up to 64 rows the plain calls choose between the small-M kernel and
+    the 64 x 128 tiles from M, N and K (more than 16384 columns: tiles from
+    8 int8 rows, 16 4-bit rows; otherwise by M, N K and M K); on both sides
+    of each boundary the plain call, one small-M entry and one tile entry
+    must give the oracle's bits."""
+    q, s_a, w, s_w = _inputs(M * 13 + N + K, M, N, K, w4=w4)
+    y_ref, acc_ref = (oracle.gemm_w4a8 if w4 else oracle.gemm_w8a8)(q, s_a, w, s_w)
+    fn = prism.gemm_w4a8_variant if w4 else prism.gemm_w8a8_variant
+    _run_all(fn, ["auto", "small_2x8", "tile_64x128"], dev(q), dev(s_a), dev(w), dev(s_w), y_ref, acc_ref)
+    y = (prism.gemm_w4a8 if w4 else prism.gemm_w8a8)(dev(q), dev(s_a), dev(w), dev(s_w))
     torch.cuda.synchronize()
     assert_same_floats(host(y), y_ref, "y (plain call)")
 

@@ -228,6 +228,28 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
   // the pair's 128-byte row.
   auto read = [&](int buf, int half, int pb) __attribute__((always_inline)) {
     const int8_t* base = lds + buf * kStage;
+    if constexpr (W4 && KSP == 2) {
+      // Packed B with two 32-k steps per phase: lane half h takes k = 64 half
+      // + 32 h + [0, 32) of the stage, one whole 16-byte chunk of the pair
+      // row (16 k in its low 8 bytes for step 0, the next 16 in its high 8
+      // bytes for step 1), and its A fragments the same k: chunk 4 half + 2 h
+      // + ks.  Any k order shared by A and B gives the same exact int32 sums.
+      // One conflict-free 16-byte read per column tile and phase instead of
+      // two 8-byte reads, whose lanes r and r + 16 hit the same LDS banks
+      // (MI355X, 2048 x 12288 x 4096: 125-129 -> 120 us).
+      const int8_t* pbase = lds + pb * kPair;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int c = ((4 * half + 2 * (lane >> 5) + ks) ^ sw) * 16;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) af[i][ks] = *reinterpret_cast<const v4i*>(base + arow + i * 32 * BK + c);
+      }
+      const int cb = ((4 * buf + 2 * half + (lane >> 5)) ^ sw) * 16;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        unpack_w4(*reinterpret_cast<const v4i*>(pbase + brow + j * 32 * BK + cb), bf[j][0], bf[j][1]);
+      return;
+    }
 #pragma unroll
     for (int ks = 0; ks < KSP; ++ks) {
       const int c = ((2 * (KSP * half + ks) + (lane >> 5)) ^ sw) * 16;

@@ -34,7 +34,20 @@ def _draw(i):
     return kind, M, N, K
 
 
-CASES = [_draw(i) for i in range(48)]
+def _draw_wide(i):
+    """More than 16384 columns and at most 160 rows, where the plain calls
+    choose between the small-M kernel and 64-row tiles by M."""
+    r = np.random.default_rng(31337 + i)
+    kind = "w8a8" if i % 2 == 0 else "w4a8"
+    M = int(np.exp(r.uniform(0, np.log(160))))
+    g = 16 if kind == "w8a8" else 32
+    N, K = int(r.integers(16385, 40000)), g * int(r.integers(1, 2048 // g))
+    while M * N * K > 2e9:
+        M = max(1, M // 2)
+    return kind, M, N, K
+
+
+CASES = [_draw(i) for i in range(48)] + [_draw_wide(i) for i in range(16)]
 
 
 @pytest.mark.parametrize("kind,M,N,K", CASES, ids=["%s-M%d-N%d-K%d" % c for c in CASES])

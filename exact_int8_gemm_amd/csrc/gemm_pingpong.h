@@ -18,9 +18,10 @@
 // waves of a SIMD alternate and the MFMA unit always has queued work.
 //
 // Stages are BK bytes of k for all rows of the tile (256 of A, BN of B) in a
-// ring of two LDS buffers.  Both groups issue the copies of stage s + 1 in
-// their first read phase of stage s, into the buffer of stage s - 1, which
-// both groups finished reading before that phase's barrier.  Before the
+// ring of two LDS buffers.  Both groups issue the copies of stage s + 1
+// during stage s (int8: spread over its phases; 4-bit: in its first read
+// phase), into the buffer of stage s - 1, which both groups finished reading
+// before the barrier of stage s's first phase.  Before the
 // barrier that precedes the first read of stage s + 1 every wave waits
 // (s_waitcnt vmcnt) for its own copies of that stage.  LDS layout, swizzle
 // and out-of-range zeros are those of gemm_dma_kernel.
@@ -36,10 +37,12 @@
 // (256 x 320 tiles, two per CU) this took 215 us to 202 us against one
 // workgroup per tile; 4096 x 9728 x 2560: 125 -> 112 us; 2048 x 17408 x 5120:
 // 210 -> 198 us; M = 2048, N = K = 5120 (256 x 256 tiles): 71 -> 64 us.
-// What remains is set by the operand copies (a 128-k stage of a 256 x 320
-// tile takes about 3900 shader cycles against 2560 of MFMA work) and by the
-// y writes of all CUs finishing their tiles together (about 27 us of the
-// 202 at M = 8192).
+// What remains is the overlap of the operand copies with the MFMAs: at M =
+// 8192, N = K = 5120 (uniform int8 data) the kernel takes about 150 us with
+// the copies left out and 123 us with the MFMAs left out, 185 us with both;
+// with two stages in the ring a stage's copies have one stage of MFMA time
+// to land.  The y writes of all CUs finishing their last tiles together add
+// 15-30 us (measured with the stores left out).
 #pragma once
 
 #include <type_traits>
@@ -194,16 +197,28 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
     }
   };
   // Copies of the next stage into ring buffer buf (W4: and half h of the
-  // next pair).
-  auto issue = [&](int buf, int h) __attribute__((always_inline)) {
+  // next pair), in kParts parts: int8 spreads a wave's copies over the
+  // 2 P - 1 phases of a stage before its end-of-stage wait (read and compute
+  // phases alike), copy s in part s kParts / kNCopies, instead of issuing
+  // them all in the stage's first read phase.  The copies of a stage take
+  // about as long as its MFMAs (without MFMAs a 256 x 320 stage runs in about
+  // 2600 cycles, its MFMAs alone in 2560), and a wave that issued all of them
+  // at once waited on their issue in that phase.  MI355X, same bits: M =
+  // 8192, N = K = 5120 194-196 -> 185-187 us; 4096 x 9728 x 2560 109-112 ->
+  // 104 us; 2048 x 5120 x 5120 (256 x 192, two phases per stage) 57 -> 55 us.
+  constexpr int kParts = W4 ? 1 : 2 * P - 1;
+  constexpr int kNCopies = W4 ? kPerWaveA : kPerWave;
+  auto issue_part = [&](int buf, int h, int part) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s = 0; s < (W4 ? kPerWaveA : kPerWave); ++s) {
+    for (int s = 0; s < kNCopies; ++s) {
+      if (s * kParts / kNCopies != part) continue;
       const bool isA = s < kPerWaveA;
       const int copy = isA ? wave * kPerWaveA + s : b_copy(s - kPerWaveA);
       const uint32_t o = (clive && ck + chunk_a(copy) * 16 < K) ? off[s] + (uint32_t)ck : kOutOfRange;
       const int8_t* dst = lds + buf * kStage + (isA ? 0 : BM * BK) + copy * 1024;
       copy_to_lds(isA ? ca : cb, lds_addr(dst), o);
     }
+    if (part != kParts - 1) return;
     if constexpr (W4) issue_half_pair(h);
     ck += BK;
     if (ck >= nkr * BK) {
@@ -212,6 +227,10 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
       ck = 0;
       clive = has_next;
     }
+  };
+  auto issue = [&](int buf, int h) __attribute__((always_inline)) {
+#pragma unroll
+    for (int pt = 0; pt < kParts; ++pt) issue_part(buf, h, pt);
   };
 
   v16i acc[TM][TN];
@@ -303,7 +322,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
 #pragma unroll
         for (int h = 0; h < P; ++h) {
           // read phase of slice h of stage u + r (buffer r)
-          if (h == 0) issue((r + RING - 1) % RING, r);
+          if (2 * h < kParts) issue_part((r + RING - 1) % RING, r, 2 * h);
           read(r, h, (u >> 1) & 1);
           wait_lgkm0();
           if (h == P - 1 && grp == 1) wait_vmcnt<0>();
@@ -312,6 +331,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
           __builtin_amdgcn_sched_barrier(0);
           // compute phase
           mma();
+          if (2 * h + 1 < kParts) issue_part((r + RING - 1) % RING, r, 2 * h + 1);
           if (h == P - 1 && grp == 0) wait_vmcnt<0>();
           __builtin_amdgcn_sched_barrier(0);
           pp_barrier();

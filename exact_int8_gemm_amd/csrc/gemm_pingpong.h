@@ -197,16 +197,18 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
     }
   };
   // Copies of the next stage into ring buffer buf (W4: and half h of the
-  // next pair), in kParts parts: int8 spreads a wave's copies over the
-  // 2 P - 1 phases of a stage before its end-of-stage wait (read and compute
-  // phases alike), copy s in part s kParts / kNCopies, instead of issuing
-  // them all in the stage's first read phase.  The copies of a stage take
-  // about as long as its MFMAs (without MFMAs a 256 x 320 stage runs in about
-  // 2600 cycles, its MFMAs alone in 2560), and a wave that issued all of them
-  // at once waited on their issue in that phase.  MI355X, same bits: M =
-  // 8192, N = K = 5120 194-196 -> 185-187 us; 4096 x 9728 x 2560 109-112 ->
-  // 104 us; 2048 x 5120 x 5120 (256 x 192, two phases per stage) 57 -> 55 us.
-  constexpr int kParts = W4 ? 1 : 2 * P - 1;
+  // next pair), in kParts parts: int8 spreads a wave's copies over the read
+  // and compute phases of the stage's first P - 1 phase pairs (copy s in part
+  // s kParts / kNCopies; none in the last pair, which ends in the wait for
+  // them) instead of issuing them all in the stage's first read phase.  The
+  // copies of a stage take about as long as its MFMAs, and a wave that issued
+  // all of them at once waited on their issue in that phase.  MI355X, same
+  // bits: M = 8192, N = K = 5120 194-196 -> 183-185 us; 4096 x 9728 x 2560
+  // 109-112 -> 104 us; 2048 x 5120 x 5120 (256 x 192, two phase pairs per
+  // stage) 57 -> 54 us.  The 4-bit form (A copies and one half pair per
+  // stage) was not faster spread (2048 x 12288 x 4096: 102-105 against
+  // 102-103 us; 4096 x 12288 x 4096: 187 against 189-191 us).
+  constexpr int kParts = W4 ? 1 : (P > 1 ? 2 * P - 2 : 1);
   constexpr int kNCopies = W4 ? kPerWaveA : kPerWave;
   auto issue_part = [&](int buf, int h, int part) __attribute__((always_inline)) {
 #pragma unroll

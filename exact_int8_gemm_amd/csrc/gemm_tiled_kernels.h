@@ -503,10 +503,13 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(const int8_
     const bool valid = isA ? (m0 + row < M) : (n0 + row < N);
     off[s] = valid ? (uint32_t)(row * K + chunk * 16) : kOutOfRange;
   }
-  auto issue = [&](int8_t* base, int stage) __attribute__((always_inline)) {
+  // Copies of a stage into `base`; part p >= 0 issues only the copies s
+  // with s KS / kPerWave == p (one part per 32-k step of `compute`).
+  auto issue = [&](int8_t* base, int stage, int part = -1) __attribute__((always_inline)) {
     const int k0 = stage * BK;
 #pragma unroll
     for (int s = 0; s < C::kPerWave; ++s) {
+      if (part >= 0 && s * (BK / 32) / C::kPerWave != part) continue;
       const bool isA = s < C::kPerWaveA;
       const int copy = isA ? wave * C::kPerWaveA + s : wave * C::kPerWaveB + (s - C::kPerWaveA);
       const uint32_t o = (k0 + kc[s] < kend) ? off[s] + (uint32_t)k0 : kOutOfRange;
@@ -530,7 +533,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(const int8_
   const int brow = (BM + wn * C::kWTN + rl) * BK;
   constexpr int KS = BK / 32;
 
-  auto compute = [&](const int8_t* buf) __attribute__((always_inline)) {
+  auto compute = [&](const int8_t* buf, int8_t* nxt, int nstage) __attribute__((always_inline)) {
     v4i af[2][C::kTM], bf[2][C::kTN];
     auto read = [&](int ks, int slot) __attribute__((always_inline)) {
       const int c = ((2 * ks + (lane >> 5)) ^ sw) * 16;
@@ -542,6 +545,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(const int8_
     read(0, 0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      issue(nxt, nstage, ks);
       if (ks + 1 < KS) read(ks + 1, (ks + 1) & 1);
 #pragma unroll
       for (int i = 0; i < C::kTM; ++i)
@@ -551,12 +555,15 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(const int8_
     }
   };
   // One pipeline step: stage `stage` sits in `cur`; the copies of stage
-  // stage + RING - 1 go into `nxt` (the buffer of stage - 1).
+  // stage + RING - 1 go into `nxt` (the buffer of stage - 1), a part before
+  // each 32-k step's MFMAs rather than all before the first: a wave that
+  // issued them all at once waited on their issue (MI355X, same bits:
+  // 512 x 9728 x 2560 23.0 -> 21.2 us, 512 x 2560 x 9728 34.1 -> 32.1 us,
+  // 1024 x 5120 x 5120 38.6-40.9 -> 36.1-36.7 us).
   auto step = [&](const int8_t* cur, int8_t* nxt, int stage) __attribute__((always_inline)) {
     wait_vmcnt<(RING - 2) * C::kPerWave>();
     __syncthreads();
-    issue(nxt, stage + RING - 1);
-    compute(cur);
+    compute(cur, nxt, stage + RING - 1);
   };
 
   // Stage count padded to a multiple of the ring: padded stages read zeros.
@@ -828,10 +835,13 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_block_kernel(const int
     dks[s] = c / (BN / 64);
     doff[s] = (n0 + col < N) ? (uint32_t)(col * NB * 2) : kOutOfRange;
   }
-  auto issue = [&](int8_t* base, int stage) __attribute__((always_inline)) {
+  // Copies of a stage into `base`; part p >= 0 issues only the copies s
+  // (operands, then scales) with s KS / kPerWave == p.
+  auto issue = [&](int8_t* base, int stage, int part = -1) __attribute__((always_inline)) {
     const int k0 = stage * BK;
 #pragma unroll
     for (int s = 0; s < C::kPerWave; ++s) {
+      if (part >= 0 && s * KS / kPerWave != part) continue;
       const bool isA = s < C::kPerWaveA;
       const int copy = isA ? wave * C::kPerWaveA + s : wave * C::kPerWaveB + (s - C::kPerWaveA);
       // No per-lane check against K: bytes past K (the next row, or zeros past
@@ -843,6 +853,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_block_kernel(const int
     }
 #pragma unroll
     for (int s = 0; s < kPerWaveD; ++s) {
+      if (part >= 0 && (C::kPerWave + s) * KS / kPerWave != part) continue;
       const int b = stage * KS + dks[s];
       const uint32_t o = (b < NB) ? doff[s] + (uint32_t)(b * 2) : kOutOfRange;
       const int8_t* dst = base + kDOff + (wave * kPerWaveD + s) * 256;
@@ -866,10 +877,16 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_block_kernel(const int
 #pragma unroll
   for (int j = 0; j < C::kTN; ++j) ncol[j] = wn * C::kWTN + j * 32 + rl;
 
-  auto compute = [&](const int8_t* buf, int stage) __attribute__((always_inline)) {
+  // The eight-wave 128 x 128 instance issues the next stage's copies a part
+  // before each block instead of all before the first (MI355X, M = 2048,
+  // 17408 x 5120: 430-459 -> 415-424 us, same bits); the four-wave 128 x 64
+  // and 64 x 64 instances were slower that way (M = 512: 124 -> 132 us).
+  constexpr bool kSpread = C::kNW == 8;
+  auto compute = [&](const int8_t* buf, int stage, int8_t* nxt) __attribute__((always_inline)) {
     const v16i zero = v16i{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      if constexpr (kSpread) issue(nxt, stage + RING - 1, ks);
       // Blocks past K (padding of the last stage and of the ring) read zero
       // operands and zero scales: fmaf(0, 0, f) returns f unchanged (f starts
       // at +0 and can never become -0), so they need no branch.
@@ -919,8 +936,8 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_block_kernel(const int
   auto step = [&](const int8_t* cur, int8_t* nxt, int stage) __attribute__((always_inline)) {
     wait_vmcnt<(RING - 2) * kPerWave>();
     __syncthreads();
-    issue(nxt, stage + RING - 1);
-    compute(cur, stage);
+    if constexpr (!kSpread) issue(nxt, stage + RING - 1);
+    compute(cur, stage, nxt);
   };
 
   const int nk = (K + BK - 1) / BK;
@@ -1069,7 +1086,10 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_q4k_kernel(const int8_
     const int col = (wave * kPerWaveH + s) * 16 + lane / 4;
     offh[s] = (n0 + col < N) ? (uint32_t)(col * NS * 16 + (lane & 3) * 4) : kOutOfRange;
   }
-  auto issue = [&](int8_t* base, int stage) __attribute__((always_inline)) {
+  // Copies of a stage into `base`; part p >= 0 issues only the copies s
+  // (operands, packed codes, then headers) with s KS / kQ == p.
+  auto issue = [&](int8_t* base, int stage, int part = -1) __attribute__((always_inline)) {
+    constexpr int kQ = C::kPerWaveA + kPerWaveB + kPerWaveH;
     const int k0 = stage * BK;
     // The LDS address of the stage as a scalar once (not a pointer per copy,
     // which the compiler kept in VGPRs and read back with readfirstlane).
@@ -1078,16 +1098,19 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_q4k_kernel(const int8_
     for (int s = 0; s < C::kPerWaveA; ++s) {
       // No check against K on the operand copies: a stage past K (ring
       // padding) meets zero headers below, so both fmas leave f unchanged.
+      if (part >= 0 && s * KS / kQ != part) continue;
       const uint32_t o = offa[s] + (uint32_t)k0;
       copy_to_lds(ra, lb + (uint32_t)((wave * C::kPerWaveA + s) * 1024), o);
     }
 #pragma unroll
     for (int s = 0; s < kPerWaveB; ++s) {
+      if (part >= 0 && (C::kPerWaveA + s) * KS / kQ != part) continue;
       const uint32_t o = offb[s] + (uint32_t)(k0 / 2);
       copy_to_lds(rb, lb + (uint32_t)(kBOff + (wave * kPerWaveB + s) * 1024), o);
     }
 #pragma unroll
     for (int s = 0; s < kPerWaveH; ++s) {
+      if (part >= 0 && (C::kPerWaveA + kPerWaveB + s) * KS / kQ != part) continue;
       const uint32_t o = (k0 < K && offh[s] != kOutOfRange) ? offh[s] + (uint32_t)(stage / 2) * 16u : kOutOfRange;
       copy4_to_lds(rh, lb + (uint32_t)(kHOff + (wave * kPerWaveH + s) * 256), o);
     }
@@ -1142,10 +1165,17 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_q4k_kernel(const int8_
       nsc[ks][row] = -(float)t;
     }
   };
-  auto compute = [&](const int8_t* buf) __attribute__((always_inline)) {
+  // As in the block-scale kernel, the eight-wave 128 x 128 instance issues
+  // the next stage's copies a part before each sub-block (MI355X, M = 2048,
+  // 17408 x 5120: 568-586 -> 551-563 us; M = 4096 1100 -> 1072-1082 us; same
+  // bits); the four-wave 64 x 64 instance was slower that way (M = 64: 48.6
+  // -> 52.8 us).
+  constexpr bool kSpread = C::kNW == 8;
+  auto compute = [&](const int8_t* buf, int8_t* nxt, int nstage) __attribute__((always_inline)) {
     const v16i zero = v16i{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      if constexpr (kSpread) issue(nxt, nstage, ks);
       // Sub-blocks past K read zero operands and zero scales: both fmas
       // return f unchanged (f starts at +0 and never becomes -0).
       const int c = ((2 * ks + (lane >> 5)) ^ sw) * 16;
@@ -1194,10 +1224,10 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_q4k_kernel(const int8_
   auto step = [&](const int8_t* cur, int8_t* nxt, int stage) __attribute__((always_inline)) {
     wait_vmcnt<0>();
     __syncthreads();
-    issue(nxt, stage + RING - 1);
+    if constexpr (!kSpread) issue(nxt, stage + RING - 1);
     decode(cur, stage);
     __syncthreads();
-    compute(cur);
+    compute(cur, nxt, stage + RING - 1);
   };
 
   static_assert(RING == 2 || RING == 3, "ring depth");

@@ -75,31 +75,33 @@ bool grid_fits(int64_t M, int64_t N) { return ((M + 63) / 64) * ((N + 127) / 128
 // The small-M kernel re-reads the whole M x K activation block in every
 // workgroup, so from some rows on the 64 x 128 tiles of the tiled path (K
 // split by their cost model) are faster.  Where, measured on MI355X with
-// graph-replayed launches (M = 8, 16, 24, 32, 48, 64; N in {2560, 5120,
-// 9728, 12288, 16384, 18432, 28672}; K in {2560, 4096, 5120, 9728, 14336}):
+// graph-replayed launches and the weights rotated through at least 640 MB
+// (so that they come from HBM, as in a model's forward pass), M = 8, 16,
+// 24, 32, 48, 64; N in {2560, 5120, 9728, 12288, 16384, 18432, 28672}; K in
+// {2560, 4096, 5120, 9728, 14336}:
 //  * N > 16384 (no even column share per CU fits the small-M kernel, whose
-//    16-column blocks then run in several rounds): from 8 rows with int8
-//    weights, 16 with 4-bit ones (e.g. int8 18432 x 5120, M = 16: 25.7 ->
-//    17.2 us; 4-bit 28672 x 4096, M = 48: 55.4 -> 18.0 us);
-//  * int8 weights: from 24 rows where N K >= 40 Mi (16384 x 4096, M = 24:
-//    16.4 -> 13.8 us; 9728 x 4096 stays small-M: 11.8 against 12.9), from
-//    48 rows where N K >= 8 Mi (9728 x 2560, M = 48: 12.0 -> 10.4 us;
-//    2560 x 2560 stays: 7.6 against 9.0), and from 32 rows where M K >=
-//    245760 (2560 x 9728, M = 32: 15.4 -> 13.0 us);
-//  * 4-bit weights: from 48 rows where M K >= 393216 (5120 x 9728, M = 48:
-//    22.3 -> 17.0 us; 12288 x 5120, M = 64 stays: 18.4 against 19.3) and
-//    from 32 rows where N K >= 128 Mi (12288 x 14336, M = 32: 28.4 ->
-//    27.0 us).
+//    16-column blocks then run in several rounds): from 8 int8 rows (18432
+//    x 5120, M = 16: 30.3 -> 28.8 us; 28672 x 2560, M = 64: 56.9 -> 20.4
+//    us); 4-bit from 24 rows, or 16 where K >= 8192 (28672 x 4096, M = 48:
+//    34.3 -> 22.9 us; 18432 x 4096, M = 16 stays: 14.8 against 18.2 us);
+//  * int8 weights up to 16384 columns: from 24 rows where M K >= 229376
+//    (5120 x 9728, M = 24: 20.6 -> 19.1 us; 9728 x 14336, M = 24: 38.3 ->
+//    34.3 us; 5120 x 2560, M = 64 stays: 12.1 against 13.9 us);
+//  * 4-bit weights up to 16384 columns: from 48 rows where M K >= 393216
+//    and from 32 rows where N K >= 128 Mi (5120 x 9728, M = 48: 24.0 ->
+//    18.5 us; 16384 x 14336, M = 32: 41.2 -> 35.1 us).
+// Over those 210 shapes the calls take 5541 against 6125 us (int8) and 4221
+// against 4808 us (4-bit) with the rule of small-M up to 64 rows except
+// int8 from 32 rows and M K >= 245760; the int8 part was then narrowed where
+// small-M stayed faster (12288 x 4096 and 16384 x 2560 at M = 24, 32).
 bool use_small(int64_t M, int64_t N, int64_t K, bool w4) {
   if (M > prism::kSmallMMax) return false;
-  const int64_t nk = N * K;
   if (w4) {
-    if (N > 16384) return M < 16;
-    return !((M >= 48 && M * K >= 393216) || (M >= 32 && nk >= (int64_t)128 << 20));
+    if (N > 16384) return !(M >= 24 || (M >= 16 && K >= 8192));
+    return !((M >= 48 && M * K >= 393216) || (M >= 32 && N * K >= (int64_t)128 << 20));
   }
   if (N > 16384) return M < 8;
-  return !((M >= 24 && nk >= (int64_t)40 << 20) || (M >= 48 && nk >= (int64_t)8 << 20) ||
-           (M >= 32 && M * K >= 245760));
+  return !(M >= 24 && M * K >= 229376);
 }
 
 // Variant dispatch shared by the two _variant calls (arguments already checked).

@@ -101,16 +101,18 @@ def test_w8a8_small_m_or_tiled(M, K):
     assert_same_floats(host(y), y_ref, "y (plain call)")
 
 
-@pytest.mark.parametrize("w4,M,N,K", [(False, 7, 16400, 256), (False, 8, 16400, 256), (True, 15, 16416, 256),
-                                      (True, 16, 16416, 256), (False, 23, 10240, 4096), (False, 24, 10240, 4096),
-                                      (False, 47, 2048, 4096), (False, 48, 2048, 4096), (True, 47, 1024, 8192),
-                                      (True, 48, 1024, 8192), (True, 32, 8192, 16384)])
+@pytest.mark.parametrize("w4,M,N,K", [(False, 7, 16400, 256), (False, 8, 16400, 256), (True, 23, 16416, 256),
+                                      (True, 24, 16416, 256), (True, 15, 16416, 8192), (True, 16, 16416, 8192),
+                                      (False, 23, 2048, 9728), (False, 24, 2048, 9728), (False, 55, 2048, 4096),
+                                      (False, 56, 2048, 4096), (True, 47, 1024, 8192), (True, 48, 1024, 8192),
+                                      (True, 32, 8192, 16384)])
 def test_small_m_or_tiled_boundaries(w4, M, N, K):
     """Up to 64 rows the plain calls choose between the small-M kernel and
     the 64 x 128 tiles from M, N and K (more than 16384 columns: tiles from
-    8 int8 rows, 16 4-bit rows; otherwise by M, N K and M K); on both sides
-    of each boundary the plain call, one small-M entry and one tile entry
-    must give the oracle's bits."""
+    8 int8 rows, 24 4-bit rows or 16 where K >= 8192; otherwise int8 from 24
+    rows where M K >= 229376, 4-bit by M K and N K); on both sides of each
+    boundary the plain call, one small-M entry and one tile entry must give
+    the oracle's bits."""
     q, s_a, w, s_w = _inputs(M * 13 + N + K, M, N, K, w4=w4)
     y_ref, acc_ref = (oracle.gemm_w4a8 if w4 else oracle.gemm_w8a8)(q, s_a, w, s_w)
     fn = prism.gemm_w4a8_variant if w4 else prism.gemm_w8a8_variant

@@ -557,9 +557,11 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(const int8_
   // One pipeline step: stage `stage` sits in `cur`; the copies of stage
   // stage + RING - 1 go into `nxt` (the buffer of stage - 1), a part before
   // each 32-k step's MFMAs rather than all before the first: a wave that
-  // issued them all at once waited on their issue (MI355X, same bits:
-  // 512 x 9728 x 2560 23.0 -> 21.2 us, 512 x 2560 x 9728 34.1 -> 32.1 us,
-  // 1024 x 5120 x 5120 38.6-40.9 -> 36.1-36.7 us).
+  // issued them all at once waited on their issue (MI355X, same bits, with
+  // the weights in the memory-side cache: 512 x 9728 x 2560 23.0 -> 21.2 us,
+  // 1024 x 5120 x 5120 38.6-40.9 -> 36.1-36.7 us; with the weights from HBM
+  // 0-6%, e.g. 1024 x 5120 x 9728 66.4 -> 62.9 us, 36 shapes of M = 128 to
+  // 1024 summing to 1148 against 1167 us).
   auto step = [&](const int8_t* cur, int8_t* nxt, int stage) __attribute__((always_inline)) {
     wait_vmcnt<(RING - 2) * C::kPerWave>();
     __syncthreads();

@@ -334,8 +334,16 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
           __builtin_amdgcn_sched_barrier(0);
           pp_barrier();
           __builtin_amdgcn_sched_barrier(0);
-          // compute phase
+          // compute phase.  int8 tiles with two 32-k steps per phase (256 x
+          // 192 and 256 x 256) raise the wave's priority while it issues its
+          // MFMAs, so the other group's reads and copies on the same SIMD do
+          // not delay them (MI355X, same bits: 2048 x 5120 x 5120 69-75 ->
+          // 63-72 us, 3072 x 5120 x 5120 84-85 -> 82 us; other shapes
+          // within 1%).  The 320-wide tiles and the 4-bit ones were slower
+          // that way.
+          if constexpr (KSP == 2 && !W4) __builtin_amdgcn_s_setprio(1);
           mma();
+          if constexpr (KSP == 2 && !W4) __builtin_amdgcn_s_setprio(0);
           if (2 * h + 1 < kParts) issue_part((r + RING - 1) % RING, r, 2 * h + 1);
           if (h == P - 1 && grp == 0) wait_vmcnt<0>();
           __builtin_amdgcn_sched_barrier(0);

@@ -252,12 +252,18 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
     if constexpr (W4 && KSP == 2) {
       // Packed B with two 32-k steps per phase: lane half h takes k = 64 half
       // + 32 h + [0, 32) of the stage, one whole 16-byte chunk of the pair
-      // row (16 k in its low 8 bytes for step 0, the next 16 in its high 8
-      // bytes for step 1), and its A fragments the same k: chunk 4 half + 2 h
-      // + ks.  Any k order shared by A and B gives the same exact int32 sums.
-      // One conflict-free 16-byte read per column tile and phase instead of
-      // two 8-byte reads, whose lanes r and r + 16 hit the same LDS banks
-      // (MI355X, 2048 x 12288 x 4096: 125-129 -> 120 us).
+      // row, and its A fragments the same k: chunks 4 half + 2 h and 4 half
+      // + 2 h + 1.  One conflict-free 16-byte read per column tile and phase
+      // instead of two 8-byte reads, whose lanes r and r + 16 hit the same
+      // LDS banks (MI355X, 2048 x 12288 x 4096: 125-129 -> 120 us).
+      // Step 0 then takes the 16 even k of those 32 and step 1 the 16 odd k
+      // (any k order shared by A and B gives the same exact int32 sums): B's
+      // fragments are the low nibbles moved up and the high nibbles in
+      // place, two and one operations per dword, with no byte interleave;
+      // A's 32 bytes are split into even and odd bytes once per 32-row tile
+      // (8 byte permutes), where interleaving the nibbles took 20 operations
+      // per column tile (MI355X: 2048 x 12288 x 4096 110 -> 104-108 us,
+      // 4096 x 12288 x 4096 204-213 -> 197-198 us).
       const int8_t* pbase = lds + pb * kPair;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -267,8 +273,28 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(const int8_t* __restric
       }
       const int cb = ((4 * buf + 2 * half + (lane >> 5)) ^ sw) * 16;
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        unpack_w4(*reinterpret_cast<const v4i*>(pbase + brow + j * 32 * BK + cb), bf[j][0], bf[j][1]);
+      for (int j = 0; j < TN; ++j) {
+        const v4i u = *reinterpret_cast<const v4i*>(pbase + brow + j * 32 * BK + cb);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          bf[j][0][d] = (int)(((uint32_t)u[d] << 4) & 0xF0F0F0F0u);  // even k: 16 w of the low nibbles
+          bf[j][1][d] = (int)((uint32_t)u[d] & 0xF0F0F0F0u);         // odd k: 16 w of the high nibbles
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const v4i a0 = af[i][0], a1 = af[i][1];  // k 0..15 and 16..31 of the lane's 32
+        v4i ev, od;
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          ev[d] = (int)__builtin_amdgcn_perm((uint32_t)a0[2 * d + 1], (uint32_t)a0[2 * d], 0x06040200u);
+          od[d] = (int)__builtin_amdgcn_perm((uint32_t)a0[2 * d + 1], (uint32_t)a0[2 * d], 0x07050301u);
+          ev[d + 2] = (int)__builtin_amdgcn_perm((uint32_t)a1[2 * d + 1], (uint32_t)a1[2 * d], 0x06040200u);
+          od[d + 2] = (int)__builtin_amdgcn_perm((uint32_t)a1[2 * d + 1], (uint32_t)a1[2 * d], 0x07050301u);
+        }
+        af[i][0] = ev;
+        af[i][1] = od;
+      }
       return;
     }
 #pragma unroll

@@ -187,19 +187,27 @@ void pick_int8(const int8_t* q, const float* s_a, const int8_t* w, const float* 
 //    tiles of 8 waves (32 x 32 each; 8 waves of 64 x 32 took 20-21 against
 //    17 us at M = 65..128 on 12288 x 4096), two workgroups per CU, tile and
 //    K split from split_int4.
-// Estimate per 256-row round of tiles as for int8 (0.83, 1 and 1.23 for the
-// three widths), against 0.63 per 512 tiles (at least one round) for
-// 128 x 128, from N x K = 12288 x 4096 on MI355X: M = 512: 44.4 us on
-// 128 x 128 against 53.7 on the best 256-row tile; M = 1024: 72.8 -> 58.8 us
-// (256 x 192); 2048: 135 -> 118 (256 x 192); 3072: 201 -> 170-173 (256 x 192
-// or 320); 4096: 260 -> 214 (256 x 256).
+// Estimates in us per 1024 of K, fitted on MI355X with weights that do not
+// stay in cache (N x K = 12288 x 4096, 9728 x 2560, 2560 x 9728, 5120 x 5120
+// and 17408 x 5120, M = 96..2048): 11.7 per 256-tile round of 256 x 192
+// (14.1 and 17.3 for 256 x 256 and 256 x 320, the int8 ratios, which this
+// sweep does not separate).  128 x 128 always wins while its t tiles fit the
+// 512 workgroups that run together (two per CU); past that it takes about
+// 0.02 t + 3, the remainder adding a second, partly filled wave.  Against the
+// earlier rule (0.63 per 512 tiles of 128 x 128, at least 0.63) this moves
+// 17 shapes from 128 x 128 to 256-row tiles, bits unchanged: M x N x K =
+// 512 x 17408 x 5120: 78.5 -> 68.4 us, 768 x 12288 x 4096: 60.8 -> 54.1,
+// 1024 x 9728 x 2560: 43.1 -> 38.4, 2048 x 5120 x 5120: 77.4 -> 66.8,
+// 4096 x 2560 x 9728: 133.6 -> 114.8, 6144 x 4096 x 14336: 393 -> 336
+// (2331 -> 2091 us summed over the 17 and the four it leaves at exactly 512
+// tiles).
 void pick_int4(const int8_t* q, const float* s_a, const int8_t* w, const float* s_w, float* y, int32_t* acc, int M,
                int N, int K, hipStream_t st) {
   auto rounds = [](int64_t t) { return (double)((t + 255) / 256); };
-  const double pp[3] = {0.83 * rounds(tiles(M, N, 256, 192)), rounds(tiles(M, N, 256, 256)),
-                        1.23 * rounds(tiles(M, N, 256, 320))};
+  const double pp[3] = {11.7 * rounds(tiles(M, N, 256, 192)), 14.1 * rounds(tiles(M, N, 256, 256)),
+                        17.3 * rounds(tiles(M, N, 256, 320))};
   const int64_t t128 = tiles(M, N, 128, 128);
-  const double c128 = 0.63 * (t128 > 512 ? (double)t128 / 512.0 : 1.0);
+  const double c128 = t128 <= 512 ? 0.0 : 0.02 * (double)t128 + 3.0;
   int best = 0;
   for (int i = 1; i < 3; ++i)
     if (pp[i] < pp[best]) best = i;

@@ -122,6 +122,23 @@ def test_small_m_or_tiled_boundaries(w4, M, N, K):
     assert_same_floats(host(y), y_ref, "y (plain call)")
 
 
+@pytest.mark.parametrize("M,N", [(2048, 4096), (2048, 4224), (1024, 8192), (1024, 8320)])
+def test_w4_tile_family_boundary(M, N):
+    """4-bit weights from 65 rows: the plain call keeps 128 x 128 tiles while
+    they fit the 512 workgroups that run together (2048 x 4096, 1024 x 8192:
+    exactly 512) and weighs the 256-row persistent tiles once there are more
+    (4224 and 8320 columns: 528 and 520 tiles, which go to 256 x 192); on both
+    sides the plain call and both families must give the oracle's bits."""
+    K = 256
+    q, s_a, w4, s_w = _inputs(M + N * 7, M, N, K, w4=True)
+    y_ref, acc_ref = oracle.gemm_w4a8(q, s_a, w4, s_w)
+    _run_all(prism.gemm_w4a8_variant, ["auto", "tile_128x128", "tile_256x192"], dev(q), dev(s_a), dev(w4),
+             dev(s_w), y_ref, acc_ref)
+    y = prism.gemm_w4a8(dev(q), dev(s_a), dev(w4), dev(s_w))
+    torch.cuda.synchronize()
+    assert_same_floats(host(y), y_ref, "y (plain call)")
+
+
 @pytest.mark.parametrize("M,N,K", [(70, 2052, 2080), (129, 1028, 1056), (3, 2560, 4096), (200, 1030, 1056),
                                    (33, 4098, 544)])
 def test_k_split_epilogue_rows(M, N, K):
